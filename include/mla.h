@@ -1,0 +1,156 @@
+/*
+ * mla.h -- C ABI of the MI355X (gfx950) Multi-head Latent Attention hot path.
+ *
+ * What the library computes (page titles and page parts):
+ *   - "MLA low-rank attention" tech note [what the KV cache stores]: per token
+ *     only the latent c^KV (d_c values) and one RoPE key k^R shared by all heads
+ *     (d_h^R values) are cached; [(2) Key] k^R = RoPE(W^KR h) comes from h, not
+ *     from c^KV; [(4) attention and output] o_{t,i} = sum_{j<=t}
+ *     softmax_j(q_{t,i} . k_{j,i} / sqrt(d_h^C + d_h^R)) v^C_{j,i}.
+ *   - "From LLaMA to DeepSeek [01] - MLA (part 1)" [section 6, matrix
+ *     absorption]: decode transforms the query once and dots it with the cached
+ *     latent rows, and applies W^UV once at the end; [section 7] prefill expands
+ *     K and V instead.
+ *   - atyun.com MLA explainer [KV cache]: each decode step appends the new
+ *     token's entry to the cache and reuses the rest; [RoPE] consecutive pairs
+ *     of dimensions are rotated by position-dependent angles.
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is DEVICE memory owned by the caller.  The library
+ *     never allocates or frees memory, never synchronises, and only enqueues
+ *     work on the stream it is given (a hipStream_t; NULL = the null stream).
+ *   - Tensors are dense row-major.  Element type is bf16 or fp32 as given by
+ *     mla_dims.dtype, except int32 index arrays.  Weights are stored out x in
+ *     per head: W^UK and W^UV are [n_heads, d_nope, d_latent], head i's block
+ *     mapping a latent row to that head's d_nope-long key/value.
+ *   - One cached row is [c^KV (d_latent) ; RoPE(k^R, position) (d_rope)],
+ *     d_latent + d_rope elements; rows live in pages of page_size rows.  Token
+ *     at position p of sequence b is in slot p % page_size of physical page
+ *     page_table[b * max_pages + p / page_size].
+ *   - RoPE: pair k = (x_2k, x_2k+1) is rotated by angle p * base^(-2k/d_rope)
+ *     with [[cos, -sin], [sin, cos]], computed in fp64.
+ *   - Errors: arguments are validated on the host before anything is enqueued;
+ *     on a non-OK status nothing was launched and no memory was touched.
+ *     Values that live in device memory (lengths, positions, page ids) are the
+ *     caller's precondition: page ids outside [0, num_pages) are skipped by the
+ *     kernels (nothing is read from or written to such a page), other
+ *     violations give unspecified results but stay inside the given buffers.
+ *     A failing kernel launch returns MLA_ERR_HIP.  mla_last_error() returns a
+ *     thread-local description of the last non-OK status.
+ *   - Alignment: the pool, every floating-point tensor and the workspace must
+ *     be 16-byte aligned; int32 arrays (page_table, start_pos, seq_lens) 4-byte
+ *     aligned.
+ *   - Thread safety: the library keeps no state besides a per-device property
+ *     cache; calls are re-entrant.  Calls that share a workspace race unless
+ *     they are ordered on one stream.
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, non-positive size, bad dims   */
+  MLA_ERR_UNSUPPORTED = 2, /* dims outside every implemented kernel family           */
+  MLA_ERR_WORKSPACE = 3,   /* workspace smaller than the *_workspace_size() result   */
+  MLA_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed             */
+} mla_status;
+
+typedef enum { MLA_BF16 = 0, MLA_F32 = 1 } mla_dtype;
+
+/* Sizes of one MLA layer (symbols of the tech note's symbol table).
+ * Two kernel families exist:
+ *   - the MFMA family for the DeepSeek-V2 sizes: n_heads 128, d_nope 128,
+ *     d_rope 64, d_latent 512, page_size 64, dtype MLA_BF16;
+ *   - a generic fp32-arithmetic family for small layers: d_latent <= 1024,
+ *     d_nope <= 256, 2 <= d_rope <= 256 (even), n_heads <= 1024,
+ *     page_size <= 4096, either dtype.                                          */
+typedef struct {
+  int32_t n_heads;   /* n_h                                                     */
+  int32_t d_nope;    /* d_h^C: per-head content dimension                       */
+  int32_t d_rope;    /* d_h^R: RoPE dimension, even, shared key                 */
+  int32_t d_latent;  /* d_c: KV latent rank                                     */
+  int32_t page_size; /* cached rows per page                                    */
+  int32_t dtype;     /* mla_dtype of every floating-point tensor                */
+  float sm_scale;    /* softmax scale; 0 selects 1/sqrt(d_nope + d_rope)        */
+  float reserved;    /* must be 0                                               */
+  double rope_base;  /* RoPE base, > 0 (10000 for the V2 layer)                 */
+} mla_dims;
+
+/* A paged latent cache. */
+typedef struct {
+  void* pool;                 /* [num_pages, page_size, d_latent + d_rope]         */
+  int32_t num_pages;          /* pages in the pool (>= 1)                          */
+  int32_t max_pages;          /* columns of page_table (>= 1)                      */
+  const int32_t* page_table;  /* [batch, max_pages] physical page ids; device mem  */
+} mla_paged_cache;
+
+/* Append n_new tokens to each of `batch` sequences.
+ * Token k of sequence b has position p = start_pos[b] + k and is written to its
+ * slot as [c_kv[b, k, :] verbatim ; RoPE(k_rope[b, k, :], p) rounded to dtype
+ * (round to nearest even from the fp64 rotation)].  Lengths are not tracked:
+ * the caller passes start_pos (device int32 [batch]) and later seq_lens.
+ * c_kv:   [batch, n_new, d_latent]     k_rope: [batch, n_new, d_rope] (pre-RoPE)
+ * The cache's page_table is read as [batch, max_pages].                        */
+mla_status mla_cache_append(const mla_dims* dims, const mla_paged_cache* cache, int32_t batch,
+                            const int32_t* start_pos, int32_t n_new, const void* c_kv,
+                            const void* k_rope, void* stream);
+
+/* Bytes of device workspace mla_decode needs for `batch` sequences when it runs
+ * with n_workgroups split-KV workgroups (0 = one per compute unit of the
+ * current device).                                                             */
+size_t mla_decode_workspace_size(const mla_dims* dims, int32_t batch, int32_t n_workgroups);
+
+/* Weight-absorbed decode: one query per sequence over its paged latent cache.
+ * seq_lens: device int32 [batch], the number of cached tokens each query
+ *   attends (positions 0 .. seq_lens[b]-1); the query sits at position
+ *   seq_lens[b]-1.  A sequence with seq_lens[b] == 0 produces zeros.
+ * q_nope: [batch, n_heads, d_nope]   q_rope: [batch, n_heads, d_rope] (pre-RoPE)
+ * w_uk, w_uv: [n_heads, d_nope, d_latent]
+ * out: [batch, n_heads, d_nope] = per head W^UV_i (sum_j p_ij c_j), before W^O.
+ * Steps: q_lat_i = W^UK_i^T q^C_i and RoPE of q^R; split-KV attention over the
+ * 576-wide rows with an online softmax; log-sum-exp combine of the splits;
+ * output projection through W^UV.
+ * n_workgroups: number of split-KV workgroups (0 = one per compute unit); it
+ *   changes how the work is split, not the result beyond rounding.
+ * workspace: device memory of at least mla_decode_workspace_size(dims, batch,
+ *   n_workgroups) bytes; its contents on entry do not matter.                 */
+mla_status mla_decode(const mla_dims* dims, const mla_paged_cache* cache, int32_t batch,
+                      const int32_t* seq_lens, const void* q_nope, const void* q_rope,
+                      const void* w_uk, const void* w_uv, void* out, void* workspace,
+                      size_t workspace_bytes, int32_t n_workgroups, void* stream);
+
+/* Bytes of device workspace mla_prefill needs. */
+size_t mla_prefill_workspace_size(const mla_dims* dims, int32_t batch, int32_t seq_len);
+
+/* Un-absorbed causal prefill of `batch` prompts of seq_len tokens at positions
+ * 0 .. seq_len-1.  Writes the latent cache for every prompt token (as
+ * mla_cache_append with start_pos 0), expands K^C = W^UK c and V^C = W^UV c per
+ * head, and runs causal attention with q = [q^C ; RoPE(q^R, t)] and
+ * k = [K^C ; cached RoPE(k^R, j)], scale as in mla_dims.
+ * q_nope: [batch, seq_len, n_heads, d_nope]  q_rope: [batch, seq_len, n_heads, d_rope]
+ * c_kv:   [batch, seq_len, d_latent]         k_rope: [batch, seq_len, d_rope]
+ * out:    [batch, seq_len, n_heads, d_nope]                                   */
+mla_status mla_prefill(const mla_dims* dims, const mla_paged_cache* cache, int32_t batch,
+                       int32_t seq_len, const void* q_nope, const void* q_rope,
+                       const void* c_kv, const void* k_rope, const void* w_uk,
+                       const void* w_uv, void* out, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/* Static name of a status code. */
+const char* mla_status_string(mla_status status);
+
+/* Thread-local description of the last non-OK status ("" if none). */
+const char* mla_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

@@ -1,0 +1,260 @@
+// C ABI of libmla: host-side validation and dispatch to the HIP launchers.
+// The entry points, their arguments and their error behaviour are documented
+// in include/mla.h.  Nothing here allocates device memory or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "mla.h"
+#include "mla_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+mla_status fail(mla_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// Compute units of the current device (cached per device id).
+int device_cus(int* out) {
+  static std::mutex mu;
+  static int cache[256] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 256) return -1;
+  std::lock_guard<std::mutex> lk(mu);
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      return -1;
+    cache[dev] = n;
+  }
+  *out = cache[dev];
+  return 0;
+}
+
+enum class Family { V2, Generic };
+
+mla_status check_dims(const mla_dims* d, mla::Layer* L, Family* fam) {
+  if (!d) return fail(MLA_ERR_INVALID_ARG, "dims is NULL");
+  if (d->n_heads < 1 || d->d_nope < 1 || d->d_latent < 1 || d->page_size < 1)
+    return fail(MLA_ERR_INVALID_ARG, "n_heads, d_nope, d_latent and page_size must be >= 1");
+  if (d->d_rope < 2 || (d->d_rope & 1)) return fail(MLA_ERR_INVALID_ARG, "d_rope must be even and >= 2");
+  if (d->dtype != MLA_BF16 && d->dtype != MLA_F32) return fail(MLA_ERR_INVALID_ARG, "unknown dtype");
+  if (d->reserved != 0.f) return fail(MLA_ERR_INVALID_ARG, "reserved field must be 0");
+  if (!(d->rope_base > 0.0) || !std::isfinite(d->rope_base))
+    return fail(MLA_ERR_INVALID_ARG, "rope_base must be finite and > 0");
+  if (!(d->sm_scale >= 0.f) || !std::isfinite(d->sm_scale))
+    return fail(MLA_ERR_INVALID_ARG, "sm_scale must be finite and >= 0");
+  L->n_heads = d->n_heads;
+  L->d_nope = d->d_nope;
+  L->d_rope = d->d_rope;
+  L->d_latent = d->d_latent;
+  L->page_size = d->page_size;
+  L->bf16 = d->dtype == MLA_BF16;
+  L->scale = d->sm_scale > 0.f ? d->sm_scale : (float)(1.0 / std::sqrt((double)(d->d_nope + d->d_rope)));
+  L->rope_base = d->rope_base;
+  if (L->is_v2()) {
+    *fam = Family::V2;
+    return MLA_OK;
+  }
+  if (d->d_latent <= 1024 && d->d_nope <= 256 && d->d_rope <= 256 && d->n_heads <= 1024 &&
+      d->page_size <= 4096) {
+    *fam = Family::Generic;
+    return MLA_OK;
+  }
+  return fail(MLA_ERR_UNSUPPORTED,
+              "dims match neither the V2 MFMA family (128 heads, d_nope 128, d_rope 64, d_latent "
+              "512, page 64, bf16) nor the generic family (d_latent <= 1024, d_nope <= 256, "
+              "d_rope <= 256, n_heads <= 1024, page_size <= 4096)");
+}
+
+mla_status check_cache(const mla_paged_cache* c) {
+  if (!c) return fail(MLA_ERR_INVALID_ARG, "cache is NULL");
+  if (!c->pool || !c->page_table) return fail(MLA_ERR_INVALID_ARG, "cache pool or page_table is NULL");
+  if (!aligned16(c->pool)) return fail(MLA_ERR_INVALID_ARG, "cache pool must be 16-byte aligned");
+  if (!aligned4(c->page_table)) return fail(MLA_ERR_INVALID_ARG, "page_table must be 4-byte aligned");
+  if (c->num_pages < 1 || c->max_pages < 1)
+    return fail(MLA_ERR_INVALID_ARG, "num_pages and max_pages must be >= 1");
+  return MLA_OK;
+}
+
+mla_status check_ptr(const void* p, const char* name) {
+  if (!p) return fail(MLA_ERR_INVALID_ARG, std::string(name) + " is NULL");
+  if (!aligned16(p)) return fail(MLA_ERR_INVALID_ARG, std::string(name) + " must be 16-byte aligned");
+  return MLA_OK;
+}
+
+mla_status check_idx(const int32_t* p, const char* name) {
+  if (!p) return fail(MLA_ERR_INVALID_ARG, std::string(name) + " is NULL");
+  if (!aligned4(p)) return fail(MLA_ERR_INVALID_ARG, std::string(name) + " must be 4-byte aligned");
+  return MLA_OK;
+}
+
+mla_status launched(hipError_t e, const char* what) {
+  if (e != hipSuccess)
+    return fail(MLA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  return MLA_OK;
+}
+
+int resolve_wg(int n_workgroups, int* out) {
+  if (n_workgroups < 0 || n_workgroups > 65536) return -1;
+  if (n_workgroups > 0) {
+    *out = n_workgroups;
+    return 0;
+  }
+  return device_cus(out);
+}
+
+}  // namespace
+
+#define MLA_TRY(expr)                 \
+  do {                                \
+    const mla_status st_ = (expr);    \
+    if (st_ != MLA_OK) return st_;    \
+  } while (0)
+
+extern "C" {
+
+const char* mla_status_string(mla_status s) {
+  switch (s) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_INVALID_ARG: return "MLA_ERR_INVALID_ARG";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP";
+  }
+  return "MLA_ERR_UNKNOWN";
+}
+
+const char* mla_last_error(void) { return g_err.c_str(); }
+
+mla_status mla_cache_append(const mla_dims* dims, const mla_paged_cache* cache, int32_t batch,
+                            const int32_t* start_pos, int32_t n_new, const void* c_kv,
+                            const void* k_rope, void* stream) {
+  mla::Layer L;
+  Family fam;
+  MLA_TRY(check_dims(dims, &L, &fam));
+  MLA_TRY(check_cache(cache));
+  if (batch < 1 || n_new < 1) return fail(MLA_ERR_INVALID_ARG, "batch and n_new must be >= 1");
+  if ((long long)batch * n_new > 0x7fffffffLL) return fail(MLA_ERR_INVALID_ARG, "batch * n_new too large");
+  MLA_TRY(check_idx(start_pos, "start_pos"));
+  MLA_TRY(check_ptr(c_kv, "c_kv"));
+  MLA_TRY(check_ptr(k_rope, "k_rope"));
+  g_err.clear();
+  return launched(mla::launch_append(L, cache->pool, cache->num_pages, cache->page_table,
+                                     cache->max_pages, batch, start_pos, n_new, c_kv, k_rope,
+                                     (hipStream_t)stream),
+                  "append launch");
+}
+
+size_t mla_decode_workspace_size(const mla_dims* dims, int32_t batch, int32_t n_workgroups) {
+  mla::Layer L;
+  Family fam;
+  if (check_dims(dims, &L, &fam) != MLA_OK || batch < 1) return 0;
+  if (fam == Family::Generic) return mla::generic_decode_workspace(L, batch);
+  int wg = 0;
+  if (resolve_wg(n_workgroups, &wg) != 0) return 0;
+  return mla::v2_decode_workspace(batch, wg);
+}
+
+mla_status mla_decode(const mla_dims* dims, const mla_paged_cache* cache, int32_t batch,
+                      const int32_t* seq_lens, const void* q_nope, const void* q_rope,
+                      const void* w_uk, const void* w_uv, void* out, void* workspace,
+                      size_t workspace_bytes, int32_t n_workgroups, void* stream) {
+  mla::Layer L;
+  Family fam;
+  MLA_TRY(check_dims(dims, &L, &fam));
+  MLA_TRY(check_cache(cache));
+  if (batch < 1) return fail(MLA_ERR_INVALID_ARG, "batch must be >= 1");
+  if ((long long)batch * L.n_heads > 0x7fffffffLL) return fail(MLA_ERR_INVALID_ARG, "batch too large");
+  MLA_TRY(check_idx(seq_lens, "seq_lens"));
+  MLA_TRY(check_ptr(q_nope, "q_nope"));
+  MLA_TRY(check_ptr(q_rope, "q_rope"));
+  MLA_TRY(check_ptr(w_uk, "w_uk"));
+  MLA_TRY(check_ptr(w_uv, "w_uv"));
+  MLA_TRY(check_ptr(out, "out"));
+  if (n_workgroups < 0 || n_workgroups > 65536)
+    return fail(MLA_ERR_INVALID_ARG, "n_workgroups must be in [0, 65536]");
+  hipStream_t s = (hipStream_t)stream;
+  if (fam == Family::Generic) {
+    const size_t need = mla::generic_decode_workspace(L, batch);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+      return fail(MLA_ERR_WORKSPACE, "workspace smaller than mla_decode_workspace_size()");
+    g_err.clear();
+    return launched(mla::launch_generic_decode(L, cache->pool, cache->num_pages, cache->page_table,
+                                               cache->max_pages, batch, seq_lens, q_nope, q_rope,
+                                               w_uk, w_uv, out, workspace, s),
+                    "generic decode launch");
+  }
+  int wg = 0;
+  if (resolve_wg(n_workgroups, &wg) != 0) return fail(MLA_ERR_HIP, "cannot query the device");
+  const size_t need = mla::v2_decode_workspace(batch, wg);
+  if (!workspace || workspace_bytes < need)
+    return fail(MLA_ERR_WORKSPACE, "workspace smaller than mla_decode_workspace_size()");
+  MLA_TRY(check_ptr(workspace, "workspace"));
+  g_err.clear();
+  return launched(mla::launch_v2_decode(L, cache->pool, cache->num_pages, cache->page_table,
+                                        cache->max_pages, batch, seq_lens, q_nope, q_rope, w_uk,
+                                        w_uv, out, workspace, wg, s),
+                  "decode launch");
+}
+
+size_t mla_prefill_workspace_size(const mla_dims* dims, int32_t batch, int32_t seq_len) {
+  mla::Layer L;
+  Family fam;
+  if (check_dims(dims, &L, &fam) != MLA_OK || batch < 1 || seq_len < 1) return 0;
+  if (fam == Family::V2) return mla::v2_prefill_workspace(batch, seq_len);
+  return mla::generic_prefill_workspace(L, batch, seq_len);
+}
+
+mla_status mla_prefill(const mla_dims* dims, const mla_paged_cache* cache, int32_t batch,
+                       int32_t seq_len, const void* q_nope, const void* q_rope, const void* c_kv,
+                       const void* k_rope, const void* w_uk, const void* w_uv, void* out,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  mla::Layer L;
+  Family fam;
+  MLA_TRY(check_dims(dims, &L, &fam));
+  MLA_TRY(check_cache(cache));
+  if (batch < 1 || seq_len < 1) return fail(MLA_ERR_INVALID_ARG, "batch and seq_len must be >= 1");
+  if ((long long)batch * seq_len * L.n_heads > 0x7fffffffLL)
+    return fail(MLA_ERR_INVALID_ARG, "batch * seq_len * n_heads too large");
+  MLA_TRY(check_ptr(q_nope, "q_nope"));
+  MLA_TRY(check_ptr(q_rope, "q_rope"));
+  MLA_TRY(check_ptr(c_kv, "c_kv"));
+  MLA_TRY(check_ptr(k_rope, "k_rope"));
+  MLA_TRY(check_ptr(w_uk, "w_uk"));
+  MLA_TRY(check_ptr(w_uv, "w_uv"));
+  MLA_TRY(check_ptr(out, "out"));
+  const size_t need = fam == Family::V2 ? mla::v2_prefill_workspace(batch, seq_len)
+                                        : mla::generic_prefill_workspace(L, batch, seq_len);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(MLA_ERR_WORKSPACE, "workspace smaller than mla_prefill_workspace_size()");
+  if (need > 0) MLA_TRY(check_ptr(workspace, "workspace"));
+  hipStream_t s = (hipStream_t)stream;
+  g_err.clear();
+  // the prompt's latent rows go into the cache first; attention reads the
+  // rotated keys back from it
+  MLA_TRY(launched(mla::launch_append(L, cache->pool, cache->num_pages, cache->page_table,
+                                      cache->max_pages, batch, nullptr, seq_len, c_kv, k_rope, s),
+                   "prefill append launch"));
+  if (fam == Family::V2)
+    return launched(mla::launch_v2_prefill(L, cache->pool, cache->num_pages, cache->page_table,
+                                           cache->max_pages, batch, seq_len, q_nope, q_rope, c_kv,
+                                           w_uk, w_uv, out, workspace, s),
+                    "prefill launch");
+  return launched(mla::launch_generic_prefill(L, cache->pool, cache->num_pages, cache->page_table,
+                                              cache->max_pages, batch, seq_len, q_nope, q_rope,
+                                              c_kv, w_uk, w_uv, out, workspace, s),
+                  "generic prefill launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,119 @@
+// Internal declarations shared by the HIP translation units of libmla.
+// Device helpers (vector types, fp64 -> storage rounding, RoPE angle) and the
+// host-side launchers that api.cpp dispatches to.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "mla.h"
+
+namespace mla {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Round an fp64 value to the nearest bf16 (ties to even), directly from fp64
+// (no intermediate fp32 rounding).  Returns the bit pattern.
+__device__ __forceinline__ uint16_t bf16_bits_rne_f64(double x) {
+  const unsigned long long u = (unsigned long long)__double_as_longlong(x);
+  const unsigned sign = (unsigned)(u >> 63) << 15;
+  const int ex = (int)((u >> 52) & 0x7ff);
+  if (ex == 0x7ff) {  // inf / nan
+    const bool nan = (u & 0xfffffffffffffULL) != 0;
+    return (uint16_t)(sign | 0x7f80u | (nan ? 0x40u : 0u));
+  }
+  const int e = ex - 1023;  // |x| in [2^e, 2^(e+1)) for normal fp64
+  if (ex != 0 && e >= -126) {
+    unsigned long long mant = (u & 0xfffffffffffffULL) | (1ULL << 52);  // 53 bits
+    unsigned long long keep = mant >> 45;                               // 8 bits
+    const unsigned long long rem = mant & ((1ULL << 45) - 1);
+    const unsigned long long half = 1ULL << 44;
+    if (rem > half || (rem == half && (keep & 1ULL))) ++keep;
+    int eb = e;
+    if (keep == 256ULL) { keep = 128ULL; ++eb; }
+    if (eb > 127) return (uint16_t)(sign | 0x7f80u);
+    return (uint16_t)(sign | ((unsigned)(eb + 127) << 7) | (unsigned)(keep & 127ULL));
+  }
+  // below the normal bf16 range: grid spacing 2^-133
+  const double k = __builtin_rint(__builtin_fabs(x) * 0x1p133);  // exact scaling, RNE
+  return (uint16_t)(sign | (unsigned)k);  // k <= 128; k == 128 is the smallest normal
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(((unsigned)b) << 16);
+}
+
+__device__ __forceinline__ uint16_t bf16_bits_rne_f32(float f) {
+  __bf16 h = (__bf16)f;  // round to nearest even
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+// Rotate the pair (a, b) by angle pos * base^(-2k/d) in fp64, without
+// contracting the products into fused multiply-adds.
+__device__ __forceinline__ void rope_pair_f64(double a, double b, double pos, int k, int d,
+                                              double base, double* ra, double* rb) {
+  const double theta = pow(base, -2.0 * (double)k / (double)d);
+  const double ang = __dmul_rn(pos, theta);
+  double s, c;
+  sincos(ang, &s, &c);
+  *ra = __dsub_rn(__dmul_rn(a, c), __dmul_rn(b, s));
+  *rb = __dadd_rn(__dmul_rn(a, s), __dmul_rn(b, c));
+}
+
+// ---------------------------------------------------------------------------
+// Host-side launchers (defined in the .hip files; called from api.cpp after
+// validation).  Each returns hipSuccess or the launch error.
+// ---------------------------------------------------------------------------
+struct Layer {
+  int n_heads, d_nope, d_rope, d_latent, page_size;
+  bool bf16;
+  float scale;       // softmax scale
+  double rope_base;
+  int row() const { return d_latent + d_rope; }
+  bool is_v2() const {
+    return bf16 && n_heads == 128 && d_nope == 128 && d_rope == 64 && d_latent == 512 &&
+           page_size == 64;
+  }
+};
+
+// start_pos == nullptr means position 0 for every sequence.
+hipError_t launch_append(const Layer& L, void* pool, int num_pages, const int32_t* table,
+                         int max_pages, int batch, const int32_t* start_pos, int n_new,
+                         const void* c_kv, const void* k_rope, hipStream_t s);
+
+// generic fp32-arithmetic family
+size_t generic_decode_workspace(const Layer& L, int batch);
+hipError_t launch_generic_decode(const Layer& L, const void* pool, int num_pages,
+                                 const int32_t* table, int max_pages, int batch,
+                                 const int32_t* seq_lens, const void* q_nope, const void* q_rope,
+                                 const void* w_uk, const void* w_uv, void* out, void* ws,
+                                 hipStream_t s);
+size_t generic_prefill_workspace(const Layer& L, int batch, int seq_len);
+hipError_t launch_generic_prefill(const Layer& L, const void* pool, int num_pages,
+                                  const int32_t* table, int max_pages, int batch, int seq_len,
+                                  const void* q_nope, const void* q_rope, const void* c_kv,
+                                  const void* w_uk, const void* w_uv, void* out, void* ws,
+                                  hipStream_t s);
+
+// MFMA family for the V2 sizes
+size_t v2_decode_workspace(int batch, int n_wg);
+hipError_t launch_v2_decode(const Layer& L, const void* pool, int num_pages, const int32_t* table,
+                            int max_pages, int batch, const int32_t* seq_lens, const void* q_nope,
+                            const void* q_rope, const void* w_uk, const void* w_uv, void* out,
+                            void* ws, int n_wg, hipStream_t s);
+size_t v2_prefill_workspace(int batch, int seq_len);
+hipError_t launch_v2_prefill(const Layer& L, const void* pool, int num_pages, const int32_t* table,
+                             int max_pages, int batch, int seq_len, const void* q_nope,
+                             const void* q_rope, const void* c_kv, const void* w_uk,
+                             const void* w_uv, void* out, void* ws, hipStream_t s);
+
+// round a byte count up to a 256-byte boundary
+static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace mla

@@ -1,0 +1,166 @@
+"""GPU parity of the decode path (append + weight-absorbed split-KV decode)
+against the fp64 oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import mla_synth as syn
+from oracle import append_expected, decode_ref
+
+pytestmark = pytest.mark.gpu
+
+from gpu_common import (DEV, assert_close, device_case, f64, pool_bits, run_decode)  # noqa: E402
+
+
+def _oracle(case, b, heads=None):
+    c, kr = case.seq_rows(b)
+    return decode_ref(f64(case.q_c[b]), f64(case.q_r[b]), f64(c), f64(kr), f64(case.w_uk),
+                      f64(case.w_uv), base=case.dims.rope_base, heads=heads)
+
+
+def _expected_pool(case, dims_pool_shape):
+    d = case.dims
+    if d.dtype == "bf16":
+        img = np.full(dims_pool_shape, 0xFFBF, dtype=np.uint16)
+    else:
+        img = np.full(dims_pool_shape, np.nan, dtype=np.float32)
+    for b in range(case.batch):
+        c, kr = case.seq_rows(b)
+        img = append_expected(img, case.table[b], 0, f64(c), f64(kr), base=d.rope_base, dtype=d.dtype)
+    return img
+
+
+def _same_bits(a, b):
+    if a.dtype == np.float32:
+        return np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    return np.array_equal(a, b)
+
+
+def test_tiny_fp32_layer_append_and_decode():
+    """Tiny fp32 layer: 64 cached tokens + 1 appended, query at position 64."""
+    print("case tiny_decode", flush=True)
+    case = syn.config_case("tiny_decode")
+    dims, pool, table, seq_lens = device_case(case)
+    assert _same_bits(pool_bits(pool), _expected_pool(case, tuple(pool.shape)))
+    out = run_decode(case, dims, pool, table, seq_lens)
+    assert_close(f64(out[0]), _oracle(case, 0), "tiny decode")
+
+
+@pytest.mark.parametrize("lens,shuffle", [([1, 63, 64, 65, 300], True), ([700], False), ([129, 2], True)])
+def test_v2_small_ragged(lens, shuffle):
+    print(f"case v2 small ragged {lens}", flush=True)
+    case = syn.decode_case(syn.V2, lens, append=True, seed=3, shuffle=shuffle)
+    dims, pool, table, seq_lens = device_case(case)
+    assert np.array_equal(pool_bits(pool), _expected_pool(case, tuple(pool.shape)))
+    out = run_decode(case, dims, pool, table, seq_lens)
+    for b in range(case.batch):
+        assert_close(f64(out[b]), _oracle(case, b), f"seq {b} (len {case.attended[b]})")
+
+
+def test_v2_b1_4k_contiguous():
+    print("case v2_b1_4k", flush=True)
+    case = syn.config_case("v2_b1_4k")
+    dims, pool, table, seq_lens = device_case(case)
+    out = run_decode(case, dims, pool, table, seq_lens)
+    assert_close(f64(out[0]), _oracle(case, 0), "b1 4k")
+
+
+def test_v2_peaky_softmax():
+    """q x 3: logits of standard deviation ~3 make the softmax peaky."""
+    print("case peaky", flush=True)
+    case = syn.decode_case(syn.V2, [2000, 130], append=False, seed=5, shuffle=True, q_gain=3.0)
+    dims, pool, table, seq_lens = device_case(case)
+    out = run_decode(case, dims, pool, table, seq_lens)
+    for b in range(case.batch):
+        assert_close(f64(out[b]), _oracle(case, b), f"peaky seq {b}")
+
+
+def test_v2_running_max_rescale():
+    """The first 100 cached rows are scaled by 0.05, so the running maximum of
+    the first tiles sits near 0 and a later tile raises it by well over 2^8;
+    the accumulated sums must be rescaled for the result to stay right."""
+    print("case rescale", flush=True)
+    case = syn.decode_case(syn.V2, [3000, 900], append=False, seed=12, shuffle=True, q_gain=2.5)
+    for b in range(case.batch):
+        o = int(case.offsets[b])
+        case.c_kv[o:o + 100] = (case.c_kv[o:o + 100].float() * 0.05).to(case.c_kv.dtype)
+        case.k_r[o:o + 100] = (case.k_r[o:o + 100].float() * 0.05).to(case.k_r.dtype)
+    dims, pool, table, seq_lens = device_case(case)
+    for wg in (0, 5):
+        out = run_decode(case, dims, pool, table, seq_lens, n_workgroups=wg)
+        for b in range(case.batch):
+            assert_close(f64(out[b]), _oracle(case, b), f"rescale n_wg {wg} seq {b}")
+
+
+def test_v2_split_count_and_repeatability():
+    """The split plan changes rounding only; the same plan gives the same bits."""
+    print("case splits", flush=True)
+    case = syn.decode_case(syn.V2, [1500, 900, 64], append=True, seed=7, shuffle=True)
+    dims, pool, table, seq_lens = device_case(case)
+    ref = [_oracle(case, b) for b in range(case.batch)]
+    outs = {}
+    for wg in (1, 3, 7, 64, 256):
+        outs[wg] = run_decode(case, dims, pool, table, seq_lens, n_workgroups=wg)
+        for b in range(case.batch):
+            assert_close(f64(outs[wg][b]), ref[b], f"n_wg {wg} seq {b}")
+    again = run_decode(case, dims, pool, table, seq_lens, n_workgroups=7)
+    assert torch.equal(again, outs[7])
+
+
+def test_v2_page_shuffle_bit_identity():
+    """The same logical cache under two page layouts gives identical bits."""
+    print("case shuffle identity", flush=True)
+    a = syn.decode_case(syn.V2, [1000, 333], append=False, seed=9, shuffle=False)
+    b = syn.decode_case(syn.V2, [1000, 333], append=False, seed=9, shuffle=True)
+    assert not np.array_equal(a.table, b.table)
+    oa = run_decode(a, *device_case(a))
+    ob = run_decode(b, *device_case(b))
+    assert torch.equal(oa, ob)
+
+
+def test_v2_zero_length_sequence_gives_zeros():
+    print("case zero length", flush=True)
+    case = syn.decode_case(syn.V2, [100, 5], append=False, seed=2, shuffle=True)
+    dims, pool, table, seq_lens = device_case(case)
+    seq_lens = torch.tensor([100, 0], dtype=torch.int32, device=DEV)
+    out = run_decode(case, dims, pool, table, seq_lens)
+    assert (out[1] == 0).all()
+    assert_close(f64(out[0]), _oracle(case, 0), "seq 0")
+
+
+def test_v2_b64_ragged_full_size_sampled():
+    """Batch 64, cached lengths uniform in [1024, 8192], shuffled 64-token pages,
+    one appended token per sequence; the oracle checks a sample of sequences
+    and heads, the cache image is checked on every touched page of the sample."""
+    print("case v2_b64_ragged", flush=True)
+    case = syn.config_case("v2_b64_ragged")
+    dims, pool, table, seq_lens = device_case(case)
+    out = run_decode(case, dims, pool, table, seq_lens)
+    assert torch.isfinite(out.float()).all()
+    rng = np.random.default_rng(11)
+    seqs = rng.choice(case.batch, size=6, replace=False)
+    heads = rng.choice(case.dims.n_heads, size=8, replace=False)
+    bits = pool_bits(pool)
+    for b in seqs:
+        got = f64(out[b])[heads]
+        assert_close(got, _oracle(case, b, heads=heads), f"seq {b} len {case.attended[b]}")
+        # cache image of this sequence
+        c, kr = case.seq_rows(b)
+        n = int(case.attended[b])
+        pages = case.table[b][: (n + 63) // 64]
+        sub = np.full((len(pages), 64, case.dims.row), 0xFFBF, dtype=np.uint16)
+        want = append_expected(sub, np.arange(len(pages)), 0, f64(c), f64(kr),
+                               base=case.dims.rope_base, dtype="bf16")
+        np.testing.assert_array_equal(bits[pages], want)
+
+
+def test_v2_b4_128k_long_context_sampled():
+    """Batch 4 x 131072 cached tokens: split-KV over all compute units plus
+    combine; sampled heads of one sequence against the oracle."""
+    print("case v2_b4_128k", flush=True)
+    case = syn.config_case("v2_b4_128k")
+    dims, pool, table, seq_lens = device_case(case)
+    out = run_decode(case, dims, pool, table, seq_lens)
+    assert torch.isfinite(out.float()).all()
+    heads = np.array([0, 77, 127])
+    assert_close(f64(out[2])[heads], _oracle(case, 2, heads=heads), "128k seq 2")

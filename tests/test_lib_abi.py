@@ -1,0 +1,84 @@
+"""Host-only checks of the C ABI: the library loads, exports every entry point
+include/mla.h declares, and rejects bad arguments before touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mla_latent_kv_34_amd as mla
+from mla_latent_kv_34_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "mla.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(mla.LIB_PATH):
+        from mla_latent_kv_34_amd import build
+        build.build()
+    return mla.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _declared()
+    assert set(declared) == set(mla.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code, name in enumerate(["MLA_OK", "MLA_ERR_INVALID_ARG", "MLA_ERR_UNSUPPORTED",
+                                 "MLA_ERR_WORKSPACE", "MLA_ERR_HIP"]):
+        assert lib.mla_status_string(code).decode() == name
+
+
+def _dims(**kw):
+    base = dict(n_heads=128, d_nope=128, d_rope=64, d_latent=512, page_size=64, dtype=0,
+                sm_scale=0.0, reserved=0.0, rope_base=10000.0)
+    base.update(kw)
+    return _lib._Dims(**base)
+
+
+def test_invalid_arguments_rejected_on_host(lib):
+    d = _dims()
+    cache = _lib._Cache(None, 1, 1, None)
+    st = lib.mla_cache_append(ctypes.byref(d), ctypes.byref(cache), 1, None, 1, None, None, None)
+    assert st == mla.MLA_ERR_INVALID_ARG
+    assert b"NULL" in lib.mla_last_error()
+    bad = _dims(d_rope=63)
+    st = lib.mla_cache_append(ctypes.byref(bad), ctypes.byref(cache), 1, None, 1, None, None, None)
+    assert st == mla.MLA_ERR_INVALID_ARG and b"d_rope" in lib.mla_last_error()
+    big = _dims(d_latent=4096, n_heads=16)
+    st = lib.mla_decode(ctypes.byref(big), ctypes.byref(cache), 1, None, None, None, None, None, None,
+                        None, 0, 0, None)
+    assert st == mla.MLA_ERR_UNSUPPORTED
+    assert lib.mla_decode_workspace_size(None, 1, 0) == 0
+    assert lib.mla_prefill_workspace_size(ctypes.byref(_dims()), 0, 10) == 0
+
+
+def test_misaligned_pointer_rejected(lib):
+    d = _dims(n_heads=4, d_nope=16, d_rope=8, d_latent=32, dtype=1)
+    cache = _lib._Cache(0x1008, 2, 2, 0x2000)   # never dereferenced: validation fails first
+    st = lib.mla_cache_append(ctypes.byref(d), ctypes.byref(cache), 1, 0x3000, 1, 0x4000, 0x5000, None)
+    assert st == mla.MLA_ERR_INVALID_ARG and b"aligned" in lib.mla_last_error()
+
+
+def test_workspace_size_generic_family_needs_no_device(lib):
+    d = _dims(n_heads=4, d_nope=16, d_rope=8, d_latent=32, dtype=1)
+    assert lib.mla_decode_workspace_size(ctypes.byref(d), 3, 0) == 0
+    # generic prefill: fp32 K^C and V^C for every prompt token and head
+    assert lib.mla_prefill_workspace_size(ctypes.byref(d), 2, 10) == 2 * 10 * 2 * 4 * 16 * 4
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(mla.LibraryMissing):
+        _lib.load()
