@@ -1,0 +1,276 @@
+"""Benchmark of the MLA decode hot path on one MI355X.
+
+Workload: DeepSeek-V2 sized layer (128 heads, d_h^C 128, d_h^R 64, d_c 512,
+bf16), batch 64, cached lengths uniform on [1024, 8192], 64-token pages in a
+shuffled page table.  One step = append one new token per sequence
+(mla_cache_append, RoPE'd key) + weight-absorbed decode over the attended
+lengths + 1 (mla_decode: q absorption, split-KV attention, combine, W^UV).
+Inputs are synthetic and seeded (mla_synth); the timed steps rotate over
+several cache/weight replicas so that the 256 MB last-level cache cannot hold
+the working set.
+
+Prints one JSON line.  `value` is whole-step cached tokens per second with
+every input resident in HBM; `roofline` describes the split-KV attention
+kernel, timed with HIP events recorded on the launch stream around that
+kernel; `cpu_baseline` times the fp64 oracle on a bounded sample of the same
+workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MLA decode cached-tokens/s + latent-cache GB/s, % of HBM/MFMA roofline"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+BYTES_PER_TOKEN = 1152          # one cached row: 576 bf16
+FLOP_PER_TOKEN = 278528         # 2*128*576 (scores) + 2*128*512 (latent sum)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_splitkv_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "mla_latent_kv_34_amd", "csrc", "decode_v2.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--replicas", type=int, default=4)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="wall-clock budget of the oracle sample (cpu_baseline)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches only")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run a plain device copy of this many bytes (HBM counter calibration)")
+    return ap.parse_args()
+
+
+def copy_calibration(nbytes: int, reps: int = 3):
+    """A plain device-to-device copy of known size, for scaling the HBM
+    FETCH_SIZE / WRITE_SIZE counters of the profiled kernels."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": src.numel() * 4, "reps": reps}), flush=True)
+
+
+def main():
+    args = parse()
+    if args.copy_bytes:
+        copy_calibration(args.copy_bytes)
+        return
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "this build has no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mla_latent_kv_34_amd as mla
+    import mla_synth as syn
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    mla.load()  # fails loudly when the HIP library is not built
+    dev = torch.device("cuda:0")
+    d = syn.V2
+    dims = mla.Dims(d.n_heads, d.d_nope, d.d_rope, d.d_latent, d.page_size, d.torch_dtype,
+                    rope_base=d.rope_base)
+    lens = syn.ragged_lengths(64, 1024, 8192, seed=0)
+    B = len(lens)
+    attended = lens + 1
+    tokens = int(attended.sum())
+
+    print(f"[bench] building {args.replicas} replicas of batch {B}, {tokens} attended tokens",
+          file=sys.stderr, flush=True)
+    reps = []
+    case0 = None
+    for r in range(args.replicas):
+        case = syn.decode_case(d, lens, append=True, seed=r, shuffle=True)
+        if r == 0:
+            case0 = case
+        pool = torch.zeros((case.num_pages, d.page_size, d.row), dtype=d.torch_dtype, device=dev)
+        table = torch.from_numpy(case.table).to(dev)
+        zero = torch.zeros(1, dtype=torch.int32, device=dev)
+        for b in range(B):  # fill the cached tokens (positions 0 .. lens[b]-1)
+            c, kr = case.seq_rows(b)
+            n = int(lens[b])
+            mla.cache_append(dims, pool, table[b:b + 1].contiguous(), zero,
+                             c[:n].unsqueeze(0).to(dev), kr[:n].unsqueeze(0).to(dev))
+        new_c = torch.stack([case.seq_rows(b)[0][-1] for b in range(B)]).unsqueeze(1).to(dev)
+        new_k = torch.stack([case.seq_rows(b)[1][-1] for b in range(B)]).unsqueeze(1).to(dev)
+        start = torch.tensor(lens, dtype=torch.int32, device=dev)
+        seq_lens = torch.tensor(attended, dtype=torch.int32, device=dev)
+        q_c, q_r = case.q_c.to(dev), case.q_r.to(dev)
+        w_uk, w_uv = case.w_uk.to(dev), case.w_uv.to(dev)
+        ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        for e in ev:
+            e.record()
+        app = mla.cache_append(dims, pool, table, start, new_c, new_k, prepare=True)
+        dec, out = mla.decode(dims, pool, table, seq_lens, q_c, q_r, w_uk, w_uv, prepare=True)
+        dec_t, _ = mla.decode(dims, pool, table, seq_lens, q_c, q_r, w_uk, w_uv, out=out,
+                              timing_events=ev, prepare=True)
+        reps.append(dict(app=app, dec=dec, dec_t=dec_t, ev=ev, out=out,
+                         keep=(pool, table, start, seq_lens, new_c, new_k, q_c, q_r, w_uk, w_uv)))
+        if r > 0:
+            del case
+    torch.cuda.synchronize()
+    resident = sum(r["keep"][0].numel() * 2 for r in reps) / 1e9
+
+    def step(i, timed=False):
+        r = reps[i % len(reps)]
+        r["app"]()
+        (r["dec_t"] if timed else r["dec"])()
+
+    # ---- eager: whole-step time and per-launch attention-kernel time
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(args.steps):
+        step(i)
+    t1.record()
+    torch.cuda.synchronize()
+    eager_ms = t0.elapsed_time(t1) / args.steps
+    # attention kernel durations (events recorded by the library around it)
+    kern_ms = []
+    for i in range(args.steps):
+        step(i, timed=True)
+        r = reps[i % len(reps)]
+        torch.cuda.synchronize()
+        kern_ms.append(r["ev"][0].elapsed_time(r["ev"][1]))
+    kern_ms = float(np.mean(kern_ms))
+
+    # ---- graph replay of the same steps
+    graph_ms = None
+    if not args.no_graph:
+        graphs = []
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for i in range(len(reps)):  # warm the capture stream
+                step(i)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        for i in range(len(reps)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(i)
+            graphs.append(g)
+        for i in range(args.warmup):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+        t0.record()
+        for i in range(args.steps):
+            graphs[i % len(graphs)].replay()
+        t1.record()
+        torch.cuda.synchronize()
+        graph_ms = t0.elapsed_time(t1) / args.steps
+
+    ms = graph_ms if graph_ms is not None else eager_ms
+    value = tokens / (ms * 1e-3)
+    cache_bytes = tokens * BYTES_PER_TOKEN
+    achieved = cache_bytes / (kern_ms * 1e-3) / 1e9
+    kern_tflops = tokens * FLOP_PER_TOKEN / (kern_ms * 1e-3) / 1e12
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        try:
+            tf = json.load(open(TRAFFIC_FILE))
+            src_sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+            if tf.get("kernel_source_sha256") == src_sha and tf.get("workload") == "v2_b64_ragged":
+                traffic = tf.get("bytes_per_launch")
+        except Exception:
+            traffic = None
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(case0, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "cached tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "v2_b64_ragged: DeepSeek-V2 MLA layer (128 heads, d_h^C 128, d_h^R 64, d_c 512), "
+                        "batch 64, cached 1024-8192 tokens (uniform), shuffled 64-token pages, "
+                        "append 1 token + absorbed decode",
+            "batch": B,
+            "attended_tokens": tokens,
+            "replicas": len(reps),
+            "resident_cache_GB": round(resident, 3),
+            "timing": "hip graph replay" if graph_ms is not None else "eager launches",
+        },
+        "latent_cache_GBps": round(cache_bytes / (ms * 1e-3) / 1e9, 1),
+        "step_hbm_frac": round(cache_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "eager_ms_per_step": round(eager_ms, 5),
+        "roofline": {
+            "kernel": "decode_splitkv",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "kernel_ms": round(kern_ms, 5),
+            "algorithmic_bytes": cache_bytes,
+            "mfma": {"achieved": round(kern_tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(kern_tflops / MFMA_BF16_PEAK_TFLOPS, 4)},
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(case, budget_s: float):
+    """The fp64 oracle on whole sequences of replica 0 until the budget is spent."""
+    import numpy as np
+    from oracle import decode_ref
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    f64 = lambda t: t.double().numpy()  # noqa: E731
+    wk, wv = f64(case.w_uk), f64(case.w_uv)
+    done_tok = 0
+    seqs = 0
+    t_start = time.perf_counter()
+    for b in range(case.batch):
+        c, kr = case.seq_rows(b)
+        decode_ref(f64(case.q_c[b]), f64(case.q_r[b]), f64(c), f64(kr), wk, wv, base=case.dims.rope_base)
+        done_tok += int(case.attended[b])
+        seqs += 1
+        if time.perf_counter() - t_start >= budget_s:
+            break
+    el = time.perf_counter() - t_start
+    return {"value": round(done_tok / el, 1), "unit": "cached tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{seqs} of 64 sequences (all 128 heads, {done_tok} attended tokens) of the "
+                      f"same workload, fp64 numpy, {el:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -120,11 +120,14 @@ size_t mla_decode_workspace_size(const mla_dims* dims, int32_t batch, int32_t n_
  * n_workgroups: number of split-KV workgroups (0 = one per compute unit); it
  *   changes how the work is split, not the result beyond rounding.
  * workspace: device memory of at least mla_decode_workspace_size(dims, batch,
- *   n_workgroups) bytes; its contents on entry do not matter.                 */
+ *   n_workgroups) bytes; its contents on entry do not matter.
+ * timing_events: NULL, or two hipEvent_t that are recorded on `stream`
+ *   immediately before and after the attention kernel (profiling only).       */
 mla_status mla_decode(const mla_dims* dims, const mla_paged_cache* cache, int32_t batch,
                       const int32_t* seq_lens, const void* q_nope, const void* q_rope,
                       const void* w_uk, const void* w_uv, void* out, void* workspace,
-                      size_t workspace_bytes, int32_t n_workgroups, void* stream);
+                      size_t workspace_bytes, int32_t n_workgroups, void* const* timing_events,
+                      void* stream);
 
 /* Bytes of device workspace mla_prefill needs. */
 size_t mla_prefill_workspace_size(const mla_dims* dims, int32_t batch, int32_t seq_len);
@@ -136,12 +139,14 @@ size_t mla_prefill_workspace_size(const mla_dims* dims, int32_t batch, int32_t s
  * k = [K^C ; cached RoPE(k^R, j)], scale as in mla_dims.
  * q_nope: [batch, seq_len, n_heads, d_nope]  q_rope: [batch, seq_len, n_heads, d_rope]
  * c_kv:   [batch, seq_len, d_latent]         k_rope: [batch, seq_len, d_rope]
- * out:    [batch, seq_len, n_heads, d_nope]                                   */
+ * out:    [batch, seq_len, n_heads, d_nope]
+ * timing_events: NULL, or two hipEvent_t recorded immediately before and after
+ *   the causal attention kernel (profiling only).                             */
 mla_status mla_prefill(const mla_dims* dims, const mla_paged_cache* cache, int32_t batch,
                        int32_t seq_len, const void* q_nope, const void* q_rope,
                        const void* c_kv, const void* k_rope, const void* w_uk,
                        const void* w_uv, void* out, void* workspace, size_t workspace_bytes,
-                       void* stream);
+                       void* const* timing_events, void* stream);
 
 /* Static name of a status code. */
 const char* mla_status_string(mla_status status);

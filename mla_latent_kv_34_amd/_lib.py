@@ -97,12 +97,12 @@ def load() -> ctypes.CDLL:
     lib.mla_decode_workspace_size.argtypes = [ctypes.POINTER(_Dims), ctypes.c_int32, ctypes.c_int32]
     lib.mla_decode_workspace_size.restype = ctypes.c_size_t
     lib.mla_decode.argtypes = [ctypes.POINTER(_Dims), ctypes.POINTER(_Cache), ctypes.c_int32, P, P, P, P, P,
-                               P, P, ctypes.c_size_t, ctypes.c_int32, P]
+                               P, P, ctypes.c_size_t, ctypes.c_int32, P, P]
     lib.mla_decode.restype = ctypes.c_int
     lib.mla_prefill_workspace_size.argtypes = [ctypes.POINTER(_Dims), ctypes.c_int32, ctypes.c_int32]
     lib.mla_prefill_workspace_size.restype = ctypes.c_size_t
     lib.mla_prefill.argtypes = [ctypes.POINTER(_Dims), ctypes.POINTER(_Cache), ctypes.c_int32, ctypes.c_int32,
-                                P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+                                P, P, P, P, P, P, P, P, ctypes.c_size_t, P, P]
     lib.mla_prefill.restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
@@ -151,9 +151,38 @@ def _cache(dims: Dims, pool: torch.Tensor, page_table: torch.Tensor) -> _Cache:
     return _Cache(pool.data_ptr(), pool.shape[0], page_table.shape[1], page_table.data_ptr())
 
 
+class _Prepared:
+    """A validated, packed C call; calling it re-issues the call on a stream."""
+
+    def __init__(self, fn, args, keep):
+        self._fn = fn
+        self._args = args
+        self._keep = keep   # keeps the ctypes structs and tensors alive
+
+    def __call__(self, stream=None):
+        _check(self._fn(*self._args, _stream(stream)))
+
+
+class _Events:
+    """The void*[2] array of hipEvent_t handles the C ABI takes (or NULL)."""
+
+    def __init__(self, ev):
+        self.arr = None
+        self.ptr = None
+        if ev is not None:
+            self.arr = (ctypes.c_void_p * 2)(ev[0].cuda_event, ev[1].cuda_event)
+            self.ptr = ctypes.cast(self.arr, ctypes.c_void_p)
+            self.ev = ev
+
+
+def _events(ev):
+    return _Events(ev)
+
+
 def cache_append(dims: Dims, pool: torch.Tensor, page_table: torch.Tensor, start_pos: torch.Tensor,
-                 c_kv: torch.Tensor, k_rope: torch.Tensor, stream=None) -> None:
-    """Write n_new tokens per sequence at positions start_pos[b] + k (mla_cache_append)."""
+                 c_kv: torch.Tensor, k_rope: torch.Tensor, stream=None, prepare: bool = False):
+    """Write n_new tokens per sequence at positions start_pos[b] + k (mla_cache_append).
+    prepare=True returns a call(stream=None) that re-issues the same append."""
     lib = load()
     cache = _cache(dims, pool, page_table)
     dev = pool.device
@@ -164,8 +193,12 @@ def cache_append(dims: Dims, pool: torch.Tensor, page_table: torch.Tensor, start
     if page_table.shape[0] < B:
         raise ValueError("page_table has fewer rows than the batch")
     d = dims._c()
-    _check(lib.mla_cache_append(ctypes.byref(d), ctypes.byref(cache), B, _ptr(start_pos), n_new,
-                                _ptr(c_kv), _ptr(k_rope), _stream(stream)))
+    call = _Prepared(lib.mla_cache_append,
+                     [ctypes.byref(d), ctypes.byref(cache), B, _ptr(start_pos), n_new, _ptr(c_kv),
+                      _ptr(k_rope)], keep=(d, cache, start_pos, c_kv, k_rope, page_table, pool))
+    if prepare:
+        return call
+    call(stream)
 
 
 def decode_workspace_size(dims: Dims, batch: int, n_workgroups: int = 0) -> int:
@@ -176,8 +209,13 @@ def decode_workspace_size(dims: Dims, batch: int, n_workgroups: int = 0) -> int:
 def decode(dims: Dims, pool: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor,
            q_nope: torch.Tensor, q_rope: torch.Tensor, w_uk: torch.Tensor, w_uv: torch.Tensor,
            out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-           n_workgroups: int = 0, stream=None) -> torch.Tensor:
-    """Weight-absorbed decode of one query per sequence (mla_decode); returns out."""
+           n_workgroups: int = 0, stream=None, timing_events=None, prepare: bool = False):
+    """Weight-absorbed decode of one query per sequence (mla_decode); returns out.
+
+    timing_events: optional pair of torch.cuda.Event recorded around the
+    attention kernel.  prepare=True validates and packs the arguments once and
+    returns (call, out) where call(stream=None) re-issues the same decode.
+    """
     lib = load()
     cache = _cache(dims, pool, page_table)
     dev = pool.device
@@ -198,9 +236,15 @@ def decode(dims: Dims, pool: torch.Tensor, page_table: torch.Tensor, seq_lens: t
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     d = dims._c()
-    _check(lib.mla_decode(ctypes.byref(d), ctypes.byref(cache), B, _ptr(seq_lens), _ptr(q_nope),
-                          _ptr(q_rope), _ptr(w_uk), _ptr(w_uv), _ptr(out), _ptr(workspace), wbytes,
-                          n_workgroups, _stream(stream)))
+    args = [ctypes.byref(d), ctypes.byref(cache), B, _ptr(seq_lens), _ptr(q_nope), _ptr(q_rope),
+            _ptr(w_uk), _ptr(w_uv), _ptr(out), _ptr(workspace), wbytes, n_workgroups]
+    evs = _events(timing_events)
+    args.append(evs.ptr)
+    call = _Prepared(lib.mla_decode, args, keep=(d, cache, seq_lens, q_nope, q_rope, w_uk, w_uv,
+                                                  out, workspace, evs))
+    if prepare:
+        return call, out
+    call(stream)
     return out
 
 
@@ -212,8 +256,10 @@ def prefill_workspace_size(dims: Dims, batch: int, seq_len: int) -> int:
 def prefill(dims: Dims, pool: torch.Tensor, page_table: torch.Tensor, q_nope: torch.Tensor,
             q_rope: torch.Tensor, c_kv: torch.Tensor, k_rope: torch.Tensor, w_uk: torch.Tensor,
             w_uv: torch.Tensor, out: torch.Tensor | None = None,
-            workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """Un-absorbed causal prefill (mla_prefill); also writes the latent cache."""
+            workspace: torch.Tensor | None = None, stream=None, timing_events=None,
+            prepare: bool = False):
+    """Un-absorbed causal prefill (mla_prefill); also writes the latent cache.
+    timing_events and prepare as for decode()."""
     lib = load()
     cache = _cache(dims, pool, page_table)
     dev = pool.device
@@ -235,9 +281,15 @@ def prefill(dims: Dims, pool: torch.Tensor, page_table: torch.Tensor, q_nope: to
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     d = dims._c()
-    _check(lib.mla_prefill(ctypes.byref(d), ctypes.byref(cache), B, T, _ptr(q_nope), _ptr(q_rope),
-                           _ptr(c_kv), _ptr(k_rope), _ptr(w_uk), _ptr(w_uv), _ptr(out),
-                           _ptr(workspace), wbytes, _stream(stream)))
+    args = [ctypes.byref(d), ctypes.byref(cache), B, T, _ptr(q_nope), _ptr(q_rope), _ptr(c_kv),
+            _ptr(k_rope), _ptr(w_uk), _ptr(w_uv), _ptr(out), _ptr(workspace), wbytes]
+    evs = _events(timing_events)
+    args.append(evs.ptr)
+    call = _Prepared(lib.mla_prefill, args, keep=(d, cache, q_nope, q_rope, c_kv, k_rope, w_uk,
+                                                   w_uv, out, workspace, evs))
+    if prepare:
+        return call, out
+    call(stream)
     return out
 
 

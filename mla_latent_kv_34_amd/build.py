@@ -46,8 +46,22 @@ def _compile(src: str) -> str:
     return obj
 
 
+def _generate() -> None:
+    """Regenerate the inline-assembly header of the split-KV kernel."""
+    gen = os.path.join(CSRC, "gen_splitkv_asm.py")
+    r = subprocess.run([sys.executable, gen], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"{gen} failed:\n{r.stderr}")
+    out = os.path.join(CSRC, "splitkv_asm.h")
+    old = open(out).read() if os.path.exists(out) else None
+    if old != r.stdout:
+        with open(out, "w") as f:
+            f.write(r.stdout)
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
+    _generate()
     with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"

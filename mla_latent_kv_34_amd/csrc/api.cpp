@@ -169,7 +169,8 @@ size_t mla_decode_workspace_size(const mla_dims* dims, int32_t batch, int32_t n_
 mla_status mla_decode(const mla_dims* dims, const mla_paged_cache* cache, int32_t batch,
                       const int32_t* seq_lens, const void* q_nope, const void* q_rope,
                       const void* w_uk, const void* w_uv, void* out, void* workspace,
-                      size_t workspace_bytes, int32_t n_workgroups, void* stream) {
+                      size_t workspace_bytes, int32_t n_workgroups, void* const* timing_events,
+                      void* stream) {
   mla::Layer L;
   Family fam;
   MLA_TRY(check_dims(dims, &L, &fam));
@@ -192,7 +193,7 @@ mla_status mla_decode(const mla_dims* dims, const mla_paged_cache* cache, int32_
     g_err.clear();
     return launched(mla::launch_generic_decode(L, cache->pool, cache->num_pages, cache->page_table,
                                                cache->max_pages, batch, seq_lens, q_nope, q_rope,
-                                               w_uk, w_uv, out, workspace, s),
+                                               w_uk, w_uv, out, workspace, timing_events, s),
                     "generic decode launch");
   }
   int wg = 0;
@@ -204,7 +205,7 @@ mla_status mla_decode(const mla_dims* dims, const mla_paged_cache* cache, int32_
   g_err.clear();
   return launched(mla::launch_v2_decode(L, cache->pool, cache->num_pages, cache->page_table,
                                         cache->max_pages, batch, seq_lens, q_nope, q_rope, w_uk,
-                                        w_uv, out, workspace, wg, s),
+                                        w_uv, out, workspace, wg, timing_events, s),
                   "decode launch");
 }
 
@@ -219,7 +220,8 @@ size_t mla_prefill_workspace_size(const mla_dims* dims, int32_t batch, int32_t s
 mla_status mla_prefill(const mla_dims* dims, const mla_paged_cache* cache, int32_t batch,
                        int32_t seq_len, const void* q_nope, const void* q_rope, const void* c_kv,
                        const void* k_rope, const void* w_uk, const void* w_uv, void* out,
-                       void* workspace, size_t workspace_bytes, void* stream) {
+                       void* workspace, size_t workspace_bytes, void* const* timing_events,
+                       void* stream) {
   mla::Layer L;
   Family fam;
   MLA_TRY(check_dims(dims, &L, &fam));
@@ -249,11 +251,11 @@ mla_status mla_prefill(const mla_dims* dims, const mla_paged_cache* cache, int32
   if (fam == Family::V2)
     return launched(mla::launch_v2_prefill(L, cache->pool, cache->num_pages, cache->page_table,
                                            cache->max_pages, batch, seq_len, q_nope, q_rope, c_kv,
-                                           w_uk, w_uv, out, workspace, s),
+                                           w_uk, w_uv, out, workspace, timing_events, s),
                     "prefill launch");
   return launched(mla::launch_generic_prefill(L, cache->pool, cache->num_pages, cache->page_table,
                                               cache->max_pages, batch, seq_len, q_nope, q_rope,
-                                              c_kv, w_uk, w_uv, out, workspace, s),
+                                              c_kv, w_uk, w_uv, out, workspace, timing_events, s),
                   "generic prefill launch");
 }
 

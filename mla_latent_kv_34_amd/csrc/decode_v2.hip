@@ -39,11 +39,19 @@ constexpr int KSTEPS = ROW / 16;  // 36 MFMA k-steps over a row
 
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 
-// Chunk swizzle inside a 128-byte LDS line: the 16-byte chunk c of row t is
-// stored at chunk c ^ swz(t).  Eight consecutive rows map a chunk to eight
-// different bank groups (token-major 16-byte reads), and rows t..t+3 map a
-// 32-byte column pair to disjoint banks (transpose reads).
-__device__ __forceinline__ int swz(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
+#include "splitkv_asm.h"
+
+// Chunk swizzle of the cached-row tiles in LDS: the 16-byte chunk c of row t
+// is stored at chunk c ^ swz(t) of its 128-byte line.  Rows are 1152 bytes, so
+// even and odd rows start in opposite halves of the 256-byte bank window; a
+// 16-lane group of 16-byte row reads (16 consecutive rows, one chunk) hits 16
+// distinct bank groups because swz takes 8 different values on the even rows
+// and on the odd rows of every 16-row block, and a 32-lane group of transpose
+// reads (4 consecutive rows, 4 chunks each) is conflict-free because rows t
+// and t + 2 of every aligned quad differ in bit 2 of swz.
+__device__ __forceinline__ int swz(int t) { return (((t >> 1) & 1) << 2) | ((t >> 2) & 3); }
+// Swizzle of the 128-byte-row weight tile of q_absorb.
+__device__ __forceinline__ int swz_w(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -51,11 +59,12 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 // Workspace layout
 // ---------------------------------------------------------------------------
 struct WsLayout {
-  size_t plan, q_abs, part_ml, part_o, o_lat, total;
+  size_t plan, plan_wg, q_abs, part_ml, part_o, o_lat, total;
   WsLayout(int B, int W) {
     const size_t slots = (size_t)W + B;
     plan = 0;
-    q_abs = align256(plan + sizeof(int32_t) * (size_t)(3 * B + 2));
+    plan_wg = align256(plan + sizeof(int32_t) * (size_t)(3 * B + 2));
+    q_abs = align256(plan_wg + sizeof(int32_t) * 4 * (size_t)W);
     part_ml = align256(q_abs + (size_t)B * H * ROW * 2);
     part_o = align256(part_ml + slots * H * 2 * sizeof(float));
     o_lat = align256(part_o + slots * H * DL * sizeof(float));
@@ -68,10 +77,24 @@ struct WsLayout {
 // plan[0..B] = exclusive prefix of ceil(len/64) (plan[B] = N),
 // plan[B+1+2b], plan[B+2+2b] = first, last workgroup of sequence b (first >
 // last when the sequence is empty), plan[3B+1] = W_eff = min(W, N): the number
-// of workgroups that get tiles (each gets at least one).
+// of workgroups that get tiles (each gets at least one).  wg[ib] = (t0, t1, b0,
+// w) for launched workgroup ib: its logical index w and page range [t0, t1)
+// and the sequence holding page t0 (t0 == t1 for an idle workgroup).
+// Logical workgroups are laid out XCD by XCD: launched workgroup ib runs on
+// XCD ib % 8, and XCD x owns the contiguous logical block starting at
+// x * (W_eff / 8) + min(x, W_eff % 8), so neighbouring splits of a sequence
+// share one XCD's L2.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ int launched_of_logical(int w, int We) {
+  const int q8 = We >> 3, r8 = We & 7;
+  int x = 0;
+  while (x < 7 && w >= (x + 1) * q8 + min(x + 1, r8)) ++x;
+  return 8 * (w - (x * q8 + min(x, r8))) + x;
+}
+
 __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ seq_lens, int B,
-                                                    int W, int32_t* __restrict__ plan) {
+                                                    int W, int32_t* __restrict__ plan,
+                                                    int4* __restrict__ wg) {
   __shared__ int32_t part[1024];
   __shared__ int32_t carry;
   if (threadIdx.x == 0) carry = 0;
@@ -101,19 +124,26 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
   }
   __syncthreads();
   const long long N = carry;
-  W = We;
+  for (int ib = We + threadIdx.x; ib < W; ib += 1024) wg[ib] = make_int4(0, 0, 0, 0);
   for (int b = threadIdx.x; b < B; b += 1024) {
     const int len = seq_lens[b];
     const int tiles = len > 0 ? (len + PS - 1) / PS : 0;
     int first = 1, last = 0;
     if (tiles > 0) {
       const long long x0 = plan[b], x1 = x0 + tiles - 1;
-      first = (int)(((x0 + 1) * W - 1) / N);
-      last = (int)(((x1 + 1) * W - 1) / N);
+      first = (int)(((x0 + 1) * We - 1) / N);
+      last = (int)(((x1 + 1) * We - 1) / N);
+      // the workgroups whose range starts inside this sequence
+      for (int w = first; w <= last; ++w) {
+        const long long s0 = (long long)w * N / We;
+        if (s0 >= x0 && s0 <= x1)
+          wg[launched_of_logical(w, We)] = make_int4((int)s0, (int)((long long)(w + 1) * N / We), b, w);
+      }
     }
     plan[B + 1 + 2 * b] = first;
     plan[B + 2 + 2 * b] = last;
   }
+  if (N == 0 && threadIdx.x == 0) wg[0] = make_int4(0, 0, 0, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -133,7 +163,7 @@ q_absorb_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __restrict_
   for (int i = tid; i < DC * 8; i += 256) {
     const int r = i >> 3, ch = i & 7;
     const uint4 v = *(const uint4*)(w_uk + ((size_t)(h * DC + r) * DL + c0 + ch * 8));
-    *(uint4*)(wl + r * 128 + ((ch ^ swz(r)) << 4)) = v;
+    *(uint4*)(wl + r * 128 + ((ch ^ swz_w(r)) << 4)) = v;
   }
   if (chunk == 0) {  // rotated query RoPE part
     for (int i = tid; i < B * (DR / 2); i += 256) {
@@ -171,7 +201,7 @@ q_absorb_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __restrict_
         const int r = 16 * s + rsub + 4 * hlf;
         const int col = mc * 32 + colsub;
         const int ch = col >> 3;
-        const char* p = wl + r * 128 + ((ch ^ swz(r)) << 4) + ((col & 4) << 1);
+        const char* p = wl + r * 128 + ((ch ^ swz_w(r)) << 4) + ((col & 4) << 1);
         s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) s16x4*)(p));
         a01[hlf] = __builtin_bit_cast(bf16x4, v);
@@ -205,114 +235,110 @@ q_absorb_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __restrict_
 // ---------------------------------------------------------------------------
 // decode_splitkv (see the file header)
 // ---------------------------------------------------------------------------
-constexpr int DMA_PER_WAVE = TILEB / 1024 / 4;  // 18 one-KiB blocks per wave per tile
+constexpr int SUB = 32;                   // tokens per pipelined sub-tile
+constexpr int SUBB = SUB * ROWB;          // 36864 bytes
+constexpr int NBUF = 4;                   // LDS ring of sub-tiles
+constexpr int DMA_SUB = SUBB / 1024 / 4;  // 9 one-KiB loads per wave per sub-tile
 
 // Workgroup barrier without the memory fence __syncthreads() implies (that
-// fence would wait for the prefetch of the next tile too).  Completion of the
-// direct-to-LDS loads is waited for explicitly with vmcnt; LDS reads always
-// complete before their results feed an MFMA, i.e. before the barrier.
+// fence would wait for the loads of the sub-tiles in flight too).  Completion
+// of the direct-to-LDS loads is waited for explicitly with vmcnt; LDS reads
+// always complete before their results feed an MFMA, i.e. before the barrier.
 __device__ __forceinline__ void raw_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
 
-__device__ __forceinline__ void wait_vmcnt_le18() {
-  // s_waitcnt vmcnt(18): vmcnt[3:0] = 2, vmcnt[5:4] = 1, expcnt/lgkmcnt unconstrained
-  __builtin_amdgcn_s_waitcnt((18 & 15) | ((18 >> 4) << 14) | (7 << 4) | (15 << 8));
+// s_waitcnt vmcnt(N) with expcnt and lgkmcnt unconstrained (N <= 63).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 __device__ __forceinline__ void wait_lgkmcnt_0() {
   // s_waitcnt lgkmcnt(0): vmcnt and expcnt unconstrained
   __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
 }
-__device__ __forceinline__ void wait_vmcnt_0() {
-  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
-}
 
-// Direct-to-LDS page copy.  Wave v copies rows 16v..16v+15 of the page (18
-// one-KiB LDS blocks).  Nine blocks span exactly eight rows, and the swizzle
-// repeats every eight rows, so the per-lane source offsets of blocks m and
-// m + 9 differ by the constant 9216 bytes: nine per-lane offsets serve all 18.
+// Direct-to-LDS copy of one 32-token sub-tile: wave v copies rows 8v..8v+7
+// (nine one-KiB LDS blocks, 9216 bytes = 8 rows).  Lane i of block m writes
+// LDS bytes 1024m + 16i and reads the 16-byte chunk that the row swizzle puts
+// there; the nine per-lane source offsets are the same for every sub-tile
+// because the swizzle repeats every sixteen rows.
 struct DmaPlan {
-  uint32_t off[9];
+  uint32_t off[DMA_SUB];
 };
-__device__ __forceinline__ DmaPlan make_dma_plan(int lane) {
+__device__ __forceinline__ DmaPlan make_dma_plan(int wave, int lane) {
   DmaPlan p;
 #pragma unroll
-  for (int m = 0; m < 9; ++m) {
-    const int o = m * 1024 + lane * 16;   // byte offset inside the wave's 16 rows
+  for (int m = 0; m < DMA_SUB; ++m) {
+    const int o = m * 1024 + lane * 16;  // byte offset inside the wave's 8 rows
     const int t = o / ROWB;
     const int r = o - t * ROWB;
     const int pc = (r >> 4) & 7;
-    p.off[m] = (uint32_t)(o + (((pc ^ swz(t)) - pc) << 4));
+    p.off[m] = (uint32_t)(o + (((pc ^ swz(8 * wave + t)) - pc) << 4));
   }
   return p;
 }
-__device__ __forceinline__ void issue_tile(const char* __restrict__ page_base, char* buf, int wave,
-                                           const DmaPlan& dp) {
-  const char* src0 = page_base + wave * 16 * ROWB;
-  char* dst0 = buf + wave * 16 * ROWB;
+__device__ __forceinline__ void issue_sub(const char* __restrict__ src, char* buf, int wave,
+                                          const DmaPlan& dp) {
+  const char* src0 = src + wave * 8 * ROWB;
+  char* dst0 = buf + wave * 8 * ROWB;
 #pragma unroll
-  for (int hlf = 0; hlf < 2; ++hlf)
-#pragma unroll
-    for (int m = 0; m < 9; ++m)
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(src0 + hlf * 9216 + dp.off[m]),
-          (__attribute__((address_space(3))) void*)(dst0 + hlf * 9216 + m * 1024), 16, 0, 0);
+  for (int m = 0; m < DMA_SUB; ++m)
+    __builtin_amdgcn_global_load_lds((const void*)(src0 + dp.off[m]),
+                                     (__attribute__((address_space(3))) void*)(dst0 + m * 1024), 16,
+                                     0, 0);
 }
 
 __global__ void __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(1, 1)))
 decode_splitkv_kernel(const char* __restrict__ pool, int num_pages, const int32_t* __restrict__ table,
                       int max_pages, const int32_t* __restrict__ seq_lens, int B,
-                      const uint16_t* __restrict__ q_abs, const int32_t* __restrict__ plan, int W,
-                      float* __restrict__ part_ml, float* __restrict__ part_o, float sc_log2) {
-  __shared__ __attribute__((aligned(1024))) char lds[2 * TILEB];
-  const int w = blockIdx.x;
-  const long long N = plan[B];
-  const int We = plan[3 * B + 1];
-  if (w >= We) return;
-  const int t0 = (int)((long long)w * N / We), t1 = (int)((long long)(w + 1) * N / We);
+                      const uint16_t* __restrict__ q_abs, const int32_t* __restrict__ plan,
+                      const int4* __restrict__ wg, float* __restrict__ part_ml,
+                      float* __restrict__ part_o, float sc_log2) {
+  __shared__ __attribute__((aligned(1024))) char lds[NBUF * SUBB];
+  const int4 mine = wg[blockIdx.x];  // (t0, t1, first sequence, logical index)
+  const int t0 = mine.x, t1 = mine.y, w = mine.w;
   if (t0 >= t1) return;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 5, n = lane & 31;
   const int head = wave * 32 + n;
-  // QK A-operand geometry: row n of a 32-token block, chunk 2s+g
+  // QK A-operand geometry: row n of the sub-tile, 16-byte chunk 2s+g
   const int fx = swz(n);
   int xo[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) xo[k] = n * ROWB + ((((2 * k + g) ^ fx)) << 4);
-  // PV transpose-read geometry
+  // PV transpose-read geometry: source row trow (+8 for the second read) of
+  // each 16-token half, column blocks of parity par
   const int G = lane >> 4, s16 = lane & 15;
   const int trow = 4 * (G >> 1) + (s16 >> 2);
-  const int ft = swz(trow);
   const int c2 = 2 * (G & 1) + ((s16 & 3) >> 1);
   const int half8 = (s16 & 1) * 8;
-  int vo[2];
+  int vo[4];
 #pragma unroll
-  for (int par = 0; par < 2; ++par) vo[par] = trow * ROWB + (((4 * par + c2) ^ ft) << 4) + half8;
+  for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+    for (int par = 0; par < 2; ++par)
+      vo[2 * hi + par] = (trow + 8 * hi) * ROWB + (((4 * par + c2) ^ swz(trow + 8 * hi)) << 4) + half8;
 
-  const DmaPlan dp = make_dma_plan(lane);
-  // first sequence whose tiles reach past t0
-  int b = 0;
-  {
-    int lo = 0, hi = B - 1;  // largest b with plan[b] <= t0
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (plan[mid] <= t0) lo = mid; else hi = mid - 1;
-    }
-    b = lo;
-    while (plan[b + 1] <= t0) ++b;
-  }
+  const DmaPlan dp = make_dma_plan(wave, lane);
+  const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)lds);
+  int b = mine.z;
   int t = t0;
   while (t < t1) {
-    while (plan[b + 1] <= t) ++b;
-    const int seg_end = min(t1, plan[b + 1]);
-    const int j_begin = t - plan[b], j_end = seg_end - plan[b];
-    const int len = seq_lens[b];
+    int pbeg = plan[b], pend = plan[b + 1];
+    while (pend <= t) {  // sequences without pages
+      ++b;
+      pbeg = pend;
+      pend = plan[b + 1];
+    }
+    const int seg_end = min(t1, pend);
     const int32_t* trow_tab = table + (size_t)b * max_pages;
-
+    const int len = seq_lens[b];
     // query fragments (B operand of S^T = K Q^T): 8 consecutive dims per lane
     bf16x8 qreg[KSTEPS];
     {
@@ -320,113 +346,124 @@ decode_splitkv_kernel(const char* __restrict__ pool, int num_pages, const int32_
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) qreg[s] = *(const bf16x8*)(qp + 16 * s);
     }
+    // sub-tiles of this segment: pages [t - pbeg, seg_end - pbeg), two per
+    // page, none past the sequence end
+    const int u0 = 2 * (t - pbeg);
+    const int u1 = min(2 * (seg_end - pbeg), (len + SUB - 1) / SUB);
     f32x16 acc[DL / 32];
 #pragma unroll
     for (int cb = 0; cb < DL / 32; ++cb) acc[cb] = (f32x16){};
     float m_run = -INFINITY, l_part = 0.f;
 
-    auto page_of = [&](int j) -> int {
-      const int p = j < max_pages ? trow_tab[j] : -1;
-      return p;
+    // The segment runs in windows of up to 64 pages: the window's page ids are
+    // loaded once, one per lane, and read back with readlane.
+    for (int wu = u0; wu < u1; wu += 128) {
+    const int nsub = min(128, u1 - wu);
+    const int pbase = wu >> 1;
+    const int pvec = pbase + lane < max_pages ? trow_tab[pbase + lane] : -1;
+    // physical page of sub-tile u of this window (-1 if the entry is unusable)
+    auto page_of = [&](int u) -> int {
+      const int j = u >> 1;
+      const int p = __builtin_amdgcn_readlane(pvec, j - pbase);
+      return (j < max_pages && p >= 0 && p < num_pages) ? p : -1;
     };
-    {
-      const int p = page_of(j_begin);
-      const int ps = (p >= 0 && p < num_pages) ? p : 0;
-      wait_vmcnt_0();
-      raw_barrier();
-      issue_tile(pool + (size_t)ps * TILEB, lds, wave, dp);
-    }
-    for (int j = j_begin; j < j_end; ++j) {
-      const int cur = (j - j_begin) & 1;
-      char* buf = lds + cur * TILEB;
-      raw_barrier();  // every wave is done with the other buffer
-      if (j + 1 < j_end) {
-        const int p = page_of(j + 1);
-        const int ps = (p >= 0 && p < num_pages) ? p : 0;
-        issue_tile(pool + (size_t)ps * TILEB, lds + (cur ^ 1) * TILEB, wave, dp);
-        wait_vmcnt_le18();
-      } else {
-        wait_vmcnt_0();
-      }
-      const int pj = page_of(j);
-      const bool page_ok = pj >= 0 && pj < num_pages;
-      const int valid = page_ok ? min(PS, len - PS * j) : 0;
-      if (valid < PS) {
+    int okmask = 0;  // bit i: the sub-tile in LDS buffer i has a usable page
+    auto issue = [&](int u, int p, int slot) {
+      okmask = (okmask & ~(1 << slot)) | ((p >= 0 ? 1 : 0) << slot);
+      issue_sub(pool + (size_t)(p >= 0 ? p : 0) * TILEB + (u & 1) * SUBB, lds + slot * SUBB, wave, dp);
+    };
+    // all prologue page ids first, so no copy is issued before the ids arrive
+    int pro[NBUF - 1];
+#pragma unroll
+    for (int i = 0; i < NBUF - 1; ++i) pro[i] = page_of(wu + i);
+    raw_barrier();  // every wave is done with every buffer
+#pragma unroll
+    for (int i = 0; i < NBUF - 1; ++i)
+      if (i < nsub) issue(wu + i, pro[i], i);
+
+    for (int k = 0; k < nsub; ++k) {
+      const int u = wu + k;
+      char* buf = lds + (k & (NBUF - 1)) * SUBB;
+      // sub-tiles issued after this one: min(2, nsub - 1 - k)
+      const int later = min(2, nsub - 1 - k);
+      if (later >= 2) wait_vmcnt<2 * DMA_SUB>();
+      else if (later == 1) wait_vmcnt<DMA_SUB>();
+      else wait_vmcnt<0>();
+      const bool page_ok = (okmask >> (k & (NBUF - 1))) & 1;
+      const int valid = page_ok ? min(SUB, len - SUB * u) : 0;
+      if (valid < SUB) {
         // Rows past the sequence end (or of an unusable page) may hold any
         // bits; a zero probability times a NaN row would still poison the
         // P.V product, so each wave clears the rows its own loads wrote.
-        for (int r = max(valid, 16 * wave); r < 16 * wave + 16; ++r)
+        for (int r = max(valid, 8 * wave); r < 8 * wave + 8; ++r)
           for (int o = lane * 16; o < ROWB; o += 1024) *(uint4*)(buf + r * ROWB + o) = make_uint4(0, 0, 0, 0);
         wait_lgkmcnt_0();
       }
-      raw_barrier();  // tile j is in LDS
+      raw_barrier();  // sub-tile k is in LDS and every wave is done with sub-tile k-1
+      if (k + NBUF - 1 < nsub) issue(u + NBUF - 1, page_of(u + NBUF - 1), (k + NBUF - 1) & (NBUF - 1));
 
-      // Two 32-token blocks, each: S^T = K Q^T, online softmax, O^T += V^T P^T
+      // ---- S^T = K Q^T for the 32 tokens
+      const uint32_t boff = lds_base + (uint32_t)(k & (NBUF - 1)) * SUBB;
+      uint32_t qa[4];
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        f32x16 sacc = {};
+      for (int kk = 0; kk < 4; ++kk) qa[kk] = boff + (uint32_t)xo[kk];
+      f32x16 s_even, s_odd;
+      qk_subtile(qreg, qa, s_even, s_odd);
+      f32x16 sacc = s_even + s_odd;
+      // ---- online softmax in log2 units; lane = one head, 16 tokens per lane
+      if (valid < SUB) {
 #pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) {
-          const bf16x8 kf = *(const bf16x8*)(buf + tb * 32 * ROWB + (s >> 2) * 128 + xo[s & 3]);
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[s], sacc, 0, 0, 0);
-        }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int tok = 32 * tb + 8 * (i >> 2) + 4 * g + (i & 3);
-          float x = sacc[i] * sc_log2;
-          if (tok >= valid) x = -INFINITY;
-          sacc[i] = x;
-          mx = fmaxf(mx, x);
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        if (__any(mx > m_run + 8.0f)) {
-          const float m_new = fmaxf(m_run, mx);
-          const float alpha = (m_run == -INFINITY) ? 0.f : exp2_fast(m_run - m_new);
-#pragma unroll
-          for (int cb = 0; cb < DL / 32; ++cb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              float x = acc[cb][i];
-              float tmp;
-              asm volatile(
-                  "v_accvgpr_read_b32 %1, %0\n\t"
-                  "v_mul_f32 %1, %1, %2\n\t"
-                  "v_accvgpr_write_b32 %0, %1"
-                  : "+a"(x), "=&v"(tmp)
-                  : "v"(alpha));
-              acc[cb][i] = x;
-            }
-          asm volatile("s_nop 7");
-          l_part *= alpha;
-          m_run = m_new;
-        }
-        bf16x8 pb[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int jj = 0; jj < 8; ++jj) {
-            const float x = sacc[8 * kb + jj];
-            const float p = (x == -INFINITY) ? 0.f : exp2_fast(x - m_run);
-            l_part += p;
-            pb[kb][jj] = (__bf16)p;
-          }
-#pragma unroll
-        for (int cb = 0; cb < DL / 32; ++cb) {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-            const char* p0 = buf + (32 * tb + 16 * kb) * ROWB + (cb >> 1) * 128 + vo[cb & 1];
-            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4*)(p0));
-            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4*)(p0 + 8 * ROWB));
-            const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v),
-                                                               pb[kb], acc[cb], 0, 0, 0);
-          }
-        }
+        for (int i = 0; i < 16; ++i)
+          if (8 * (i >> 2) + 4 * g + (i & 3) >= valid) sacc[i] = -INFINITY;
       }
+      float mx = sacc[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * sc_log2;
+      // The reference m_run moves only when some head's maximum rose by more
+      // than 8 (probabilities stay below 2^8); the rescale of the running sums
+      // is written as AGPR read / multiply / write so the accumulators stay in
+      // AGPRs.
+      if (__any(mx > m_run + 8.0f)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = (m_run == -INFINITY) ? 0.f : exp2_fast(m_run - m_new);
+#pragma unroll
+        for (int cb = 0; cb < DL / 32; ++cb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            float x = acc[cb][i];
+            float tmp;
+            asm volatile(
+                "v_accvgpr_read_b32 %1, %0\n\t"
+                "v_mul_f32 %1, %1, %2\n\t"
+                "v_accvgpr_write_b32 %0, %1"
+                : "+a"(x), "=&v"(tmp)
+                : "v"(alpha));
+            acc[cb][i] = x;
+          }
+        asm volatile("s_nop 7");
+        l_part *= alpha;
+        m_run = m_new;
+      }
+      // (m_run is still -inf only while every token so far was masked; then
+      // every score here is -inf too and every probability 0)
+      const float nm = (m_run == -INFINITY) ? 0.f : -m_run;
+      bf16x8 pb[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const float p = exp2_fast(__builtin_fmaf(sacc[8 * kb + jj], sc_log2, nm));
+          l_part += p;
+          pb[kb][jj] = (__bf16)p;
+        }
+      // ---- O^T += V^T P^T over 16 blocks of 32 latent columns
+      uint32_t va[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) va[i] = boff + (uint32_t)vo[i];
+      pv_subtile(acc, pb, va);
     }
+    }  // window
     // ---- write this segment's partial result to slot w + b
     const float l_tot = l_part + __shfl_xor(l_part, 32);
     const size_t slot = (size_t)w + b;
@@ -551,7 +588,7 @@ size_t v2_decode_workspace(int batch, int n_wg) { return v2::WsLayout(batch, n_w
 hipError_t launch_v2_decode(const Layer& L, const void* pool, int num_pages, const int32_t* table,
                             int max_pages, int batch, const int32_t* seq_lens, const void* q_nope,
                             const void* q_rope, const void* w_uk, const void* w_uv, void* out,
-                            void* ws, int n_wg, hipStream_t s) {
+                            void* ws, int n_wg, void* const* ev, hipStream_t s) {
   using namespace v2;
   const WsLayout lay(batch, n_wg);
   char* base = (char*)ws;
@@ -561,13 +598,18 @@ hipError_t launch_v2_decode(const Layer& L, const void* pool, int num_pages, con
   float* part_o = (float*)(base + lay.part_o);
   float* o_lat = (float*)(base + lay.o_lat);
   const float sc_log2 = L.scale * 1.4426950408889634f;
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, seq_lens, batch, n_wg, plan);
+  int4* plan_wg = (int4*)(base + lay.plan_wg);
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, seq_lens, batch, n_wg, plan, plan_wg);
   hipLaunchKernelGGL(q_absorb_kernel, dim3(H * 8), dim3(256), 0, s, (const uint16_t*)q_nope,
                      (const uint16_t*)q_rope, (const uint16_t*)w_uk, seq_lens, batch, L.rope_base,
                      q_abs);
+  hipError_t e = mark(ev, 0, s);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_splitkv_kernel, dim3(n_wg), dim3(256), 0, s, (const char*)pool,
                      num_pages, table, max_pages, seq_lens, batch, (const uint16_t*)q_abs, plan,
-                     n_wg, part_ml, part_o, sc_log2);
+                     (const int4*)plan_wg, part_ml, part_o, sc_log2);
+  e = mark(ev, 1, s);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(combine_kernel, dim3(batch * H), dim3(64), 0, s, plan, batch, part_ml, part_o,
                      o_lat);
   hipLaunchKernelGGL(out_absorb_kernel, dim3(H * 4), dim3(64), 0, s, o_lat,

@@ -227,9 +227,11 @@ hipError_t launch_generic_decode(const Layer& L, const void* pool, int num_pages
                                  const int32_t* table, int max_pages, int batch,
                                  const int32_t* seq_lens, const void* q_nope, const void* q_rope,
                                  const void* w_uk, const void* w_uv, void* out, void*,
-                                 hipStream_t s) {
+                                 void* const* ev, hipStream_t s) {
   const long long blocks = (long long)batch * L.n_heads;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipError_t e = mark(ev, 0, s);
+  if (e != hipSuccess) return e;
   if (L.bf16)
     hipLaunchKernelGGL(generic_decode_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0, s,
                        pool, num_pages, table, max_pages, seq_lens, q_nope, q_rope, w_uk, w_uv,
@@ -240,7 +242,9 @@ hipError_t launch_generic_decode(const Layer& L, const void* pool, int num_pages
                        pool, num_pages, table, max_pages, seq_lens, q_nope, q_rope, w_uk, w_uv,
                        out, L.n_heads, L.d_nope, L.d_rope, L.d_latent, L.page_size, L.scale,
                        L.rope_base);
-  return hipGetLastError();
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return mark(ev, 1, s);
 }
 
 size_t generic_prefill_workspace(const Layer& L, int batch, int seq_len) {
@@ -251,7 +255,7 @@ hipError_t launch_generic_prefill(const Layer& L, const void* pool, int num_page
                                   const int32_t* table, int max_pages, int batch, int seq_len,
                                   const void* q_nope, const void* q_rope, const void* c_kv,
                                   const void* w_uk, const void* w_uv, void* out, void* ws,
-                                  hipStream_t s) {
+                                  void* const* ev, hipStream_t s) {
   const long long bt = (long long)batch * seq_len;
   const long long blocks = bt * L.n_heads;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
@@ -259,6 +263,7 @@ hipError_t launch_generic_prefill(const Layer& L, const void* pool, int num_page
   if (L.bf16) {
     hipLaunchKernelGGL(generic_expand_kernel<true>, dim3((unsigned)bt), dim3(kThreads), 0, s, c_kv,
                        w_uk, w_uv, kv, L.n_heads, L.d_nope, L.d_latent);
+    if (mark(ev, 0, s) != hipSuccess) return hipErrorInvalidValue;
     hipLaunchKernelGGL(generic_prefill_attn_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0,
                        s, pool, num_pages, table, max_pages, q_nope, q_rope, kv, out, seq_len,
                        L.n_heads, L.d_nope, L.d_rope, L.d_latent, L.page_size, L.scale,
@@ -266,12 +271,15 @@ hipError_t launch_generic_prefill(const Layer& L, const void* pool, int num_page
   } else {
     hipLaunchKernelGGL(generic_expand_kernel<false>, dim3((unsigned)bt), dim3(kThreads), 0, s, c_kv,
                        w_uk, w_uv, kv, L.n_heads, L.d_nope, L.d_latent);
+    if (mark(ev, 0, s) != hipSuccess) return hipErrorInvalidValue;
     hipLaunchKernelGGL(generic_prefill_attn_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), 0,
                        s, pool, num_pages, table, max_pages, q_nope, q_rope, kv, out, seq_len,
                        L.n_heads, L.d_nope, L.d_rope, L.d_latent, L.page_size, L.scale,
                        L.rope_base);
   }
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return mark(ev, 1, s);
 }
 
 }  // namespace mla

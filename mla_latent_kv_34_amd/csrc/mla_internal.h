@@ -93,25 +93,31 @@ hipError_t launch_generic_decode(const Layer& L, const void* pool, int num_pages
                                  const int32_t* table, int max_pages, int batch,
                                  const int32_t* seq_lens, const void* q_nope, const void* q_rope,
                                  const void* w_uk, const void* w_uv, void* out, void* ws,
-                                 hipStream_t s);
+                                 void* const* ev, hipStream_t s);
 size_t generic_prefill_workspace(const Layer& L, int batch, int seq_len);
 hipError_t launch_generic_prefill(const Layer& L, const void* pool, int num_pages,
                                   const int32_t* table, int max_pages, int batch, int seq_len,
                                   const void* q_nope, const void* q_rope, const void* c_kv,
                                   const void* w_uk, const void* w_uv, void* out, void* ws,
-                                  hipStream_t s);
+                                  void* const* ev, hipStream_t s);
 
 // MFMA family for the V2 sizes
 size_t v2_decode_workspace(int batch, int n_wg);
 hipError_t launch_v2_decode(const Layer& L, const void* pool, int num_pages, const int32_t* table,
                             int max_pages, int batch, const int32_t* seq_lens, const void* q_nope,
                             const void* q_rope, const void* w_uk, const void* w_uv, void* out,
-                            void* ws, int n_wg, hipStream_t s);
+                            void* ws, int n_wg, void* const* ev, hipStream_t s);
 size_t v2_prefill_workspace(int batch, int seq_len);
 hipError_t launch_v2_prefill(const Layer& L, const void* pool, int num_pages, const int32_t* table,
                              int max_pages, int batch, int seq_len, const void* q_nope,
                              const void* q_rope, const void* c_kv, const void* w_uk,
-                             const void* w_uv, void* out, void* ws, hipStream_t s);
+                             const void* w_uv, void* out, void* ws, void* const* ev,
+                             hipStream_t s);
+
+// Record timing event ev[i] (a hipEvent_t) on s when ev is non-null.
+static inline hipError_t mark(void* const* ev, int i, hipStream_t s) {
+  return ev ? hipEventRecord((hipEvent_t)ev[i], s) : hipSuccess;
+}
 
 // round a byte count up to a 256-byte boundary
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }

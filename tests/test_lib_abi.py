@@ -57,7 +57,7 @@ def test_invalid_arguments_rejected_on_host(lib):
     assert st == mla.MLA_ERR_INVALID_ARG and b"d_rope" in lib.mla_last_error()
     big = _dims(d_latent=4096, n_heads=16)
     st = lib.mla_decode(ctypes.byref(big), ctypes.byref(cache), 1, None, None, None, None, None, None,
-                        None, 0, 0, None)
+                        None, 0, 0, None, None)
     assert st == mla.MLA_ERR_UNSUPPORTED
     assert lib.mla_decode_workspace_size(None, 1, 0) == 0
     assert lib.mla_prefill_workspace_size(ctypes.byref(_dims()), 0, 10) == 0
