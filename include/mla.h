@@ -140,8 +140,10 @@ size_t mla_prefill_workspace_size(const mla_dims* dims, int32_t batch, int32_t s
  * q_nope: [batch, seq_len, n_heads, d_nope]  q_rope: [batch, seq_len, n_heads, d_rope]
  * c_kv:   [batch, seq_len, d_latent]         k_rope: [batch, seq_len, d_rope]
  * out:    [batch, seq_len, n_heads, d_nope]
- * timing_events: NULL, or two hipEvent_t recorded immediately before and after
- *   the causal attention kernel (profiling only).                             */
+ * The page table needs at least ceil(seq_len / page_size) columns
+ * (MLA_ERR_INVALID_ARG otherwise).
+ * timing_events: NULL, or two hipEvent_t recorded immediately before the K/V
+ *   expansion and after the causal attention kernel (profiling only).       */
 mla_status mla_prefill(const mla_dims* dims, const mla_paged_cache* cache, int32_t batch,
                        int32_t seq_len, const void* q_nope, const void* q_rope,
                        const void* c_kv, const void* k_rope, const void* w_uk,

@@ -46,17 +46,21 @@ def _compile(src: str) -> str:
     return obj
 
 
+GENERATED = [("gen_splitkv_asm.py", "splitkv_asm.h"), ("gen_prefill_asm.py", "prefill_asm.h")]
+
+
 def _generate() -> None:
-    """Regenerate the inline-assembly header of the split-KV kernel."""
-    gen = os.path.join(CSRC, "gen_splitkv_asm.py")
-    r = subprocess.run([sys.executable, gen], capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"{gen} failed:\n{r.stderr}")
-    out = os.path.join(CSRC, "splitkv_asm.h")
-    old = open(out).read() if os.path.exists(out) else None
-    if old != r.stdout:
-        with open(out, "w") as f:
-            f.write(r.stdout)
+    """Regenerate the inline-assembly headers of the MFMA kernels."""
+    for script, header in GENERATED:
+        gen = os.path.join(CSRC, script)
+        r = subprocess.run([sys.executable, gen], capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"{gen} failed:\n{r.stderr}")
+        out = os.path.join(CSRC, header)
+        old = open(out).read() if os.path.exists(out) else None
+        if old != r.stdout:
+            with open(out, "w") as f:
+                f.write(r.stdout)
 
 
 def build(verbose: bool = False) -> str:

@@ -227,6 +227,8 @@ mla_status mla_prefill(const mla_dims* dims, const mla_paged_cache* cache, int32
   MLA_TRY(check_dims(dims, &L, &fam));
   MLA_TRY(check_cache(cache));
   if (batch < 1 || seq_len < 1) return fail(MLA_ERR_INVALID_ARG, "batch and seq_len must be >= 1");
+  if ((long long)cache->max_pages * L.page_size < seq_len)
+    return fail(MLA_ERR_INVALID_ARG, "page_table rows are too short for seq_len tokens");
   if ((long long)batch * seq_len * L.n_heads > 0x7fffffffLL)
     return fail(MLA_ERR_INVALID_ARG, "batch * seq_len * n_heads too large");
   MLA_TRY(check_ptr(q_nope, "q_nope"));

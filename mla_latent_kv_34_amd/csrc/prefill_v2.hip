@@ -1,12 +1,414 @@
-// Un-absorbed causal prefill for the DeepSeek-V2 layer sizes.
-// (Routed through the generic kernels until the MFMA prefill lands.)
+// Un-absorbed causal prefill for the DeepSeek-V2 layer sizes on gfx950.
+//
+// For a prompt the heads' keys and values are expanded from the latent rows
+// and attention runs in the ordinary per-head form (tech note [(3) prefill];
+// haowenji [section 6]: prefill is compute-bound, so it does not absorb):
+//   K^C_i = C W^UK_i^T,  V^C_i = C W^UV_i^T                 (expand, MFMA GEMM)
+//   s_ti  = ([q^C_ti ; RoPE(q^R_ti, t)] . [K^C_ij ; RoPE(k^R_j, j)]) / sqrt(192)
+//   o_ti  = sum_{j <= t} softmax_j(s_ti) V^C_ij             (prefill_attn)
+// The rotated k^R rows are read back from the latent cache, which the bulk
+// append has written for positions 0..T-1 before these kernels run.
+//
+// Workspace (per prompt b and head h, T rounded up to Tp = 64 * ceil(T/64)):
+//   rope  [T][32] (cos, sin) in fp64 of the query rotation angles
+//   K^C   [b][h][Tp][128] bf16, the 128 dims of every 16-dim group stored in
+//         the order 0-3, 8-11, 4-7, 12-15 (the k-slot order of the MFMA result
+//         layout, so the expansion writes 16-byte pieces; the query is read in
+//         the same order, which leaves every dot product unchanged)
+//   V^T   [b][h][128][Tp] bf16, keys in the same order within 16-key groups,
+//         so one 16-byte LDS read gives a lane the 8 keys its probabilities
+//         cover; rows past T hold zeros.
 #include "mla_internal.h"
 
 namespace mla {
+namespace v2p {
+
+constexpr int H = 128;      // heads
+constexpr int DC = 128;     // d_h^C
+constexpr int DR = 64;      // d_h^R
+constexpr int DL = 512;     // d_c
+constexpr int ROWB = 1152;  // cached row bytes
+constexpr int PS = 64;      // page size = key tile
+constexpr int TILEB = PS * ROWB;
+
+#include "prefill_asm.h"
+
+// 16-byte-chunk swizzle of the LDS tiles whose rows are a multiple of 128
+// bytes: chunk c of row r is stored at chunk c ^ swz8(r) of its 128-byte
+// line.  A 16-lane group reading one chunk of 16 consecutive rows then hits
+// 16 distinct bank groups (rows of the same parity differ in swz8).
+__device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
+
+__device__ __forceinline__ void raw_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+__device__ __forceinline__ void wait_vmcnt0() {
+  // s_waitcnt vmcnt(0), expcnt and lgkmcnt unconstrained
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Launched workgroup ib runs on XCD ib % 8; give every XCD a contiguous range
+// of logical indices so neighbouring work shares that XCD's L2.
+__device__ __forceinline__ int logical_of_launched(int ib, int n) {
+  const int x = ib & 7, k = ib >> 3, q8 = n >> 3, r8 = n & 7;
+  return x * q8 + min(x, r8) + k;
+}
+
+__device__ __forceinline__ void dma16(const void* src, char* lds_block) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_block, 16,
+                                   0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// rope_table: tab[t][k] = (cos, sin) of t * base^(-2k/64) in fp64.
+// ---------------------------------------------------------------------------
+__global__ void rope_table_kernel(int T, double base, double2* __restrict__ tab) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= T * (DR / 2)) return;
+  const int t = i / (DR / 2), k = i % (DR / 2);
+  const double theta = pow(base, -2.0 * (double)k / (double)DR);
+  const double ang = __dmul_rn((double)t, theta);
+  double s, c;
+  sincos(ang, &s, &c);
+  tab[i] = make_double2(c, s);
+}
+
+// ---------------------------------------------------------------------------
+// expand: one workgroup per (head h, 128-token tile of prompt b).  Waves 0-1
+// compute K^C for tokens 0-63 / 64-127 of the tile as K^T = W^UK_h C^T (rows =
+// key dims, so a lane ends with 8 key dims of one token in k-slot order);
+// waves 2-3 compute V = C W^UV_h^T (rows = tokens, so a lane ends with 8
+// tokens of one value dim).  The latent dimension runs in 8 stages of 64
+// columns, double-buffered in LDS with direct-to-LDS loads: C rows of the
+// tile [128][64] then W^UK_h and W^UV_h rows [256][64], 128 bytes per row.
+// ---------------------------------------------------------------------------
+constexpr int EX_TOK = 128;
+constexpr int EX_CB = EX_TOK * 128;       // 16384 bytes of C per stage
+constexpr int EX_STAGEB = EX_CB + 256 * 128;  // + 32768 bytes of W
+constexpr int EX_DMA = EX_STAGEB / 1024 / 4;  // 12 one-KiB loads per wave per stage
+
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+expand_kernel(const uint16_t* __restrict__ c_kv, const uint16_t* __restrict__ w_uk,
+              const uint16_t* __restrict__ w_uv, int B, int T, int tp, int nt,
+              uint16_t* __restrict__ kc, uint16_t* __restrict__ vt) {
+  __shared__ __attribute__((aligned(1024))) char lds[2 * EX_STAGEB];
+  const int ttiles = B * nt;
+  const int h = blockIdx.x / ttiles, tile = blockIdx.x % ttiles;
+  const int b = tile / nt, t0 = (tile % nt) * EX_TOK;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int g = lane >> 5, n = lane & 31;
+
+  // direct-to-LDS plan: load m of wave w fills LDS unit u = (4m + w) * 64 +
+  // lane (16 bytes each); units 0..1023 are C rows, 1024..3071 W rows
+  const char* src[EX_DMA];
+#pragma unroll
+  for (int m = 0; m < EX_DMA; ++m) {
+    const int u = (4 * m + wave) * 64 + lane;
+    if (m < 4) {
+      const int r = u >> 3, c = (u & 7) ^ swz8(u >> 3);
+      const int t = min(t0 + r, T - 1);
+      src[m] = (const char*)(c_kv + ((size_t)b * T + t) * DL) + 16 * c;
+    } else {
+      const int v = u - 1024, r = v >> 3, c = (v & 7) ^ swz8(v >> 3);
+      const uint16_t* w = r < DC ? w_uk + ((size_t)h * DC + r) * DL
+                                 : w_uv + ((size_t)h * DC + r - DC) * DL;
+      src[m] = (const char*)w + 16 * c;
+    }
+  }
+  auto issue = [&](int stage) {
+    char* buf = lds + (stage & 1) * EX_STAGEB;
+#pragma unroll
+    for (int m = 0; m < EX_DMA; ++m) dma16(src[m] + stage * 128, buf + (4 * m + wave) * 1024);
+  };
+
+  const bool vhalf = wave >= 2;
+  const int tb = 64 * (wave & 1);  // first token of this wave inside the tile
+  const int x = swz8(n);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)lds);
+  uint32_t cof[4], wof[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    cof[ks] = (uint32_t)((tb + n) * 128 + 16 * ((2 * ks + g) ^ x));
+    wof[ks] = (uint32_t)(EX_CB + (128 * (vhalf ? 1 : 0) + n) * 128 + 16 * ((2 * ks + g) ^ x));
+  }
+  f32x16 acc[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) acc[k] = (f32x16){};
+
+  issue(0);
+  for (int st = 0; st < DL / 64; ++st) {
+    wait_vmcnt0();
+    raw_barrier();  // stage st is in LDS; every wave is done with stage st - 1
+    if (st + 1 < DL / 64) issue(st + 1);
+    const uint32_t base = lds0 + (uint32_t)(st & 1) * EX_STAGEB;
+    uint32_t ca[4], wa[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      ca[ks] = base + cof[ks];
+      wa[ks] = base + wof[ks];
+    }
+    if (vhalf) expand_stage_v(acc, ca, wa);
+    else expand_stage_k(acc, ca, wa);
+  }
+
+  const size_t bh = (size_t)b * H + h;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        bf16x8 v;
+        if (!vhalf) {
+          // token t0 + tb + 32i + n; key dims 32j + 16hh + (k-slot order) 8g..8g+7
+          const int t = t0 + tb + 32 * i + n;
+          if (t >= tp) continue;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = t < T ? (__bf16)acc[4 * i + j][8 * hh + e] : (__bf16)0.f;
+          *(bf16x8*)(kc + (bh * tp + t) * DC + 32 * j + 16 * hh + 8 * g) = v;
+        } else {
+          // value dim 32j + n; stored key positions p0 .. p0+7 of the tile
+          const int p0 = t0 + tb + 32 * i + 16 * hh + 8 * g;
+          if (p0 >= tp) continue;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int t = t0 + tb + 32 * i + 16 * hh + 8 * (e >> 2) + 4 * g + (e & 3);
+            v[e] = t < T ? (__bf16)acc[4 * i + j][8 * hh + e] : (__bf16)0.f;
+          }
+          *(bf16x8*)(vt + (bh * DC + 32 * j + n) * tp + p0) = v;
+        }
+      }
+}
+
+// ---------------------------------------------------------------------------
+// prefill_attn: one workgroup per (prompt b, head h, 128-query block); wave v
+// owns queries 32v..32v+31 of the block.  Key tiles of 64 (one cache page)
+// are double-buffered in LDS as four regions of 128-byte rows, each filled by
+// direct-to-LDS loads from one source: K^C dims 0-63 and 64-127 [64 keys],
+// the rotated k^R from the cache page [64 keys], and V^T [128 dims][64 keys].
+// Per tile a wave computes S^T = K Q^T (so each lane owns one query's
+// scores), masks the causal triangle on diagonal tiles, runs the online
+// softmax in log2 units, and accumulates O^T += V^T P^T with the
+// probabilities straight from registers.
+// ---------------------------------------------------------------------------
+constexpr int QB = 128;
+constexpr int KREG = PS * 128;             // 8192 bytes per key region
+constexpr int KTILEB = 3 * KREG;           // K^C lo, K^C hi, rotated k^R
+constexpr int VTILEB = DC * PS * 2;        // 16384
+constexpr int STAGEB = KTILEB + VTILEB;    // 40960
+constexpr int AT_DMA = STAGEB / 1024 / 4;  // 10 one-KiB loads per wave per tile
+
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+prefill_attn_kernel(const char* __restrict__ pool, int num_pages, const int32_t* __restrict__ table,
+                    int max_pages, const uint16_t* __restrict__ q_nope,
+                    const uint16_t* __restrict__ q_rope, const double2* __restrict__ rope_tab,
+                    const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vt, int B, int T,
+                    int tp, int nqb, float sc_log2, uint16_t* __restrict__ out) {
+  __shared__ __attribute__((aligned(1024))) char lds[2 * STAGEB];
+  const int L = logical_of_launched(blockIdx.x, B * H * nqb);
+  const int bh = L / nqb, qb = nqb - 1 - L % nqb;  // longest query blocks first
+  const int b = bh / H, h = bh % H;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int g = lane >> 5, n = lane & 31;
+  const int q0 = qb * QB + 32 * wave;       // first query of this wave
+  const int tq = q0 + n;                    // this lane's query
+  const int lim = min(tq, T - 1);           // keys <= lim are visible to it
+  const int lim_lo = min(q0, T - 1), lim_hi = min(q0 + 31, T - 1);
+
+  // ---- query fragments: B operand of S^T = K Q^T, 8 dims per lane per
+  // k-step.  Each lane builds its 96 bf16 (K^C dims in k-slot order
+  // 16s + 4g + {0..3, 8..11}, then the rotated q^R dims 16(s-8) + 8g .. +7)
+  // in LDS (which the key tiles do not use yet) and reads them back as whole
+  // 16-byte fragments.
+  bf16x8 q[12];
+  {
+    char* qs = lds + (wave * 64 + lane) * 192;  // 12 fragments of 16 bytes
+    const uint16_t* qc = q_nope + (((size_t)b * T + lim) * H + h) * DC;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const uint2 lo = *(const uint2*)(qc + 16 * s + 4 * g);
+      const uint2 hi = *(const uint2*)(qc + 16 * s + 4 * g + 8);
+      *(uint4*)(qs + 16 * s) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    }
+    const uint16_t* qr = q_rope + (((size_t)b * T + lim) * H + h) * DR;
+#pragma unroll
+    for (int s = 8; s < 12; ++s) {
+      const int e0 = 16 * (s - 8) + 8 * g;
+      const uint4 raw = *(const uint4*)(qr + e0);
+      const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+      uint32_t rot[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const double2 cs = rope_tab[(size_t)lim * (DR / 2) + e0 / 2 + k];
+        const double a = (double)bf16_bits_to_f32((uint16_t)(w4[k] & 0xffff));
+        const double bb = (double)bf16_bits_to_f32((uint16_t)(w4[k] >> 16));
+        const double ra = __dsub_rn(__dmul_rn(a, cs.x), __dmul_rn(bb, cs.y));
+        const double rb = __dadd_rn(__dmul_rn(a, cs.y), __dmul_rn(bb, cs.x));
+        rot[k] = (uint32_t)bf16_bits_rne_f64(ra) | ((uint32_t)bf16_bits_rne_f64(rb) << 16);
+      }
+      *(uint4*)(qs + 16 * s) = make_uint4(rot[0], rot[1], rot[2], rot[3]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < 12; ++s) q[s] = *(const bf16x8*)(qs + 16 * s);
+    __syncthreads();  // the key tiles may overwrite the staging area now
+  }
+
+  // ---- direct-to-LDS plan: load m of wave w fills LDS unit u = (4m + w) * 64
+  // + lane (16 bytes each).  Loads 0-1 fill K^C dims 0-63, 2-3 K^C dims
+  // 64-127, 4-5 the rotated k^R rows, 6-9 the V^T rows; every region stores
+  // chunk c of row r at chunk c ^ swz8(r).  Load m covers rows 32 * (m & 1)
+  // (key regions) or 32 * (m - 6) (V^T) on from those of load 0 / 6, so a
+  // lane keeps three 32-bit source offsets and the rest are uniform steps.
+  const size_t bhs = (size_t)b * H + h;
+  const char* kc_bh = (const char*)(kc + bhs * tp * DC);
+  const char* vt_bh = (const char*)(vt + bhs * DC * tp);
+  const int r0 = 8 * wave + (lane >> 3);           // row of load 0 / 6 in its region
+  const int c0 = (lane & 7) ^ swz8(r0);            // source chunk (swz8(r0 + 32) == swz8(r0))
+  const uint32_t off_kc = (uint32_t)(r0 * 256 + 16 * c0);
+  const uint32_t off_pg = (uint32_t)(r0 * ROWB + 1024 + 16 * c0);
+  const uint32_t off_vt = (uint32_t)(r0 * tp * 2 + 16 * c0);
+  const int32_t* trow = table + (size_t)b * max_pages;
+  auto issue = [&](int kt, int page) {
+    char* buf = lds + (kt & 1) * STAGEB + wave * 1024;
+    const char* kbase = kc_bh + (size_t)kt * PS * 256;
+    const char* pbase = pool + (size_t)page * TILEB;
+    const char* vbase = vt_bh + (size_t)kt * 128;
+#pragma unroll
+    for (int m = 0; m < AT_DMA; ++m) {
+      const char* s;
+      if (m < 4) s = kbase + (m >> 1) * 128 + (m & 1) * 32 * 256 + off_kc;
+      else if (m < 6) s = pbase + (m & 1) * 32 * ROWB + off_pg;
+      else s = vbase + (size_t)(m - 6) * 32 * tp * 2 + off_vt;
+      dma16(s, buf + m * 4096);
+    }
+  };
+  auto page_of = [&](int kt) {
+    const int p = trow[kt];
+    return (p >= 0 && p < num_pages) ? p : 0;  // stay in bounds on a bad table
+  };
+
+  const int x = swz8(n);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)lds);
+  uint32_t kof[4], vof[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    kof[k] = (uint32_t)(n * 128 + 16 * ((2 * k + g) ^ x));
+    vof[k] = (uint32_t)(KTILEB + n * 128 + 16 * ((2 * k + g) ^ x));
+  }
+
+  f32x16 o[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) o[d] = (f32x16){};
+  float m_run = -INFINITY, l_part = 0.f;
+
+  const int ntile = min(tp / PS, (qb * QB + QB - 1) / PS + 1);
+  issue(0, page_of(0));
+  for (int kt = 0; kt < ntile; ++kt) {
+    const int pnext = kt + 1 < ntile ? page_of(kt + 1) : 0;
+    wait_vmcnt0();
+    raw_barrier();  // tile kt is in LDS; every wave is done with tile kt - 1
+    if (kt + 1 < ntile) issue(kt + 1, pnext);
+    if (kt * PS > lim_hi) continue;  // every key of the tile is after every query of this wave
+    const uint32_t base = lds0 + (uint32_t)(kt & 1) * STAGEB;
+    uint32_t a[4], va[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      a[k] = base + kof[k];
+      va[k] = base + vof[k];
+    }
+    f32x16 s0, s1;
+    prefill_qk(q, a, s0, s1);
+    if (kt * PS + PS - 1 > lim_lo) {  // causal mask on the diagonal
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = kt * PS + 8 * (i >> 2) + 4 * g + (i & 3);
+        if (key > lim) s0[i] = -INFINITY;
+        if (key + 32 > lim) s1[i] = -INFINITY;
+      }
+    }
+    float mx = fmaxf(s0[0], s1[0]);
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * sc_log2;
+    // lazy rescale: the reference maximum moves only when some query's tile
+    // maximum exceeds it by more than 8 (probabilities stay below 2^8)
+    if (__any(mx > m_run + 8.0f)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = (m_run == -INFINITY) ? 0.f : exp2_fast(m_run - m_new);
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float xv = o[d][i];
+          float tmp;
+          asm volatile(
+              "v_accvgpr_read_b32 %1, %0\n\t"
+              "v_mul_f32 %1, %1, %2\n\t"
+              "v_accvgpr_write_b32 %0, %1"
+              : "+a"(xv), "=&v"(tmp)
+              : "v"(alpha));
+          o[d][i] = xv;
+        }
+      asm volatile("s_nop 7");
+      l_part *= alpha;
+      m_run = m_new;
+    }
+    const float nm = (m_run == -INFINITY) ? 0.f : -m_run;
+    bf16x8 p[4];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float p0 = exp2_fast(__builtin_fmaf(s0[e], sc_log2, nm));
+      const float p1 = exp2_fast(__builtin_fmaf(s0[8 + e], sc_log2, nm));
+      const float p2 = exp2_fast(__builtin_fmaf(s1[e], sc_log2, nm));
+      const float p3 = exp2_fast(__builtin_fmaf(s1[8 + e], sc_log2, nm));
+      l_part += (p0 + p1) + (p2 + p3);
+      p[0][e] = (__bf16)p0;
+      p[1][e] = (__bf16)p1;
+      p[2][e] = (__bf16)p2;
+      p[3][e] = (__bf16)p3;
+    }
+    prefill_pv(o, p, va);
+  }
+
+  // ---- normalise and store o[b, t, h, :]
+  const float l_tot = l_part + __shfl_xor(l_part, 32);
+  if (tq < T) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    uint16_t* dst = out + (((size_t)b * T + tq) * H + h) * DC;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        ushort4 v;
+        v.x = bf16_bits_rne_f32(o[d][4 * qq + 0] * inv);
+        v.y = bf16_bits_rne_f32(o[d][4 * qq + 1] * inv);
+        v.z = bf16_bits_rne_f32(o[d][4 * qq + 2] * inv);
+        v.w = bf16_bits_rne_f32(o[d][4 * qq + 3] * inv);
+        *(ushort4*)(dst + 32 * d + 8 * qq + 4 * g) = v;
+      }
+  }
+}
+
+struct PfLayout {
+  size_t rope, kc, vt, total;
+  int tp;
+  PfLayout(int B, int T) {
+    tp = (T + PS - 1) / PS * PS;
+    rope = 0;
+    kc = align256(rope + (size_t)T * (DR / 2) * sizeof(double2));
+    vt = align256(kc + (size_t)B * H * tp * DC * 2);
+    total = align256(vt + (size_t)B * H * DC * tp * 2);
+  }
+};
+
+}  // namespace v2p
 
 size_t v2_prefill_workspace(int batch, int seq_len) {
-  Layer L{128, 128, 64, 512, 64, true, 0.f, 10000.0};
-  return generic_prefill_workspace(L, batch, seq_len);
+  return v2p::PfLayout(batch, seq_len).total;
 }
 
 hipError_t launch_v2_prefill(const Layer& L, const void* pool, int num_pages, const int32_t* table,
@@ -14,8 +416,30 @@ hipError_t launch_v2_prefill(const Layer& L, const void* pool, int num_pages, co
                              const void* q_rope, const void* c_kv, const void* w_uk,
                              const void* w_uv, void* out, void* ws, void* const* ev,
                              hipStream_t s) {
-  return launch_generic_prefill(L, pool, num_pages, table, max_pages, batch, seq_len, q_nope,
-                                q_rope, c_kv, w_uk, w_uv, out, ws, ev, s);
+  using namespace v2p;
+  const int B = batch, T = seq_len;
+  const PfLayout lay(B, T);
+  char* w = (char*)ws;
+  double2* tab = (double2*)(w + lay.rope);
+  uint16_t* kc = (uint16_t*)(w + lay.kc);
+  uint16_t* vt = (uint16_t*)(w + lay.vt);
+  hipError_t e = mark(ev, 0, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((T * (DR / 2) + 255) / 256)), dim3(256), 0,
+                     s, T, L.rope_base, tab);
+  const int nt = (T + EX_TOK - 1) / EX_TOK;
+  hipLaunchKernelGGL(expand_kernel, dim3((unsigned)(H * B * nt)), dim3(256), 0, s,
+                     (const uint16_t*)c_kv, (const uint16_t*)w_uk, (const uint16_t*)w_uv, B, T,
+                     lay.tp, nt, kc, vt);
+  const int nqb = (T + QB - 1) / QB;
+  const float sc_log2 = L.scale * 1.4426950408889634f;
+  hipLaunchKernelGGL(prefill_attn_kernel, dim3((unsigned)(B * H * nqb)), dim3(256), 0, s,
+                     (const char*)pool, num_pages, table, max_pages, (const uint16_t*)q_nope,
+                     (const uint16_t*)q_rope, (const double2*)tab, (const uint16_t*)kc,
+                     (const uint16_t*)vt, B, T, lay.tp, nqb, sc_log2, (uint16_t*)out);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return mark(ev, 1, s);
 }
 
 }  // namespace mla

@@ -1,0 +1,107 @@
+"""GPU parity of the prefill path (bulk append + K/V expansion + causal
+attention) against the fp64 oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import mla_latent_kv_34_amd as mla
+import mla_synth as syn
+from oracle import append_expected, decode_ref, prefill_ref
+
+pytestmark = pytest.mark.gpu
+
+from gpu_common import DEV, assert_close, canary_pool, f64, lib_dims, pool_bits  # noqa: E402
+
+
+def _run(case: syn.PrefillCase):
+    dims = lib_dims(case.dims)
+    pool = canary_pool(case.dims, case.num_pages)
+    table = torch.from_numpy(case.table).to(DEV)
+    out = mla.prefill(dims, pool, table, case.q_c.to(DEV), case.q_r.to(DEV), case.c_kv.to(DEV),
+                      case.k_r.to(DEV), case.w_uk.to(DEV), case.w_uv.to(DEV))
+    torch.cuda.synchronize()
+    return dims, pool, table, out
+
+
+def _oracle(case, b, rows=None, heads=None):
+    return prefill_ref(f64(case.q_c[b]), f64(case.q_r[b]), f64(case.c_kv[b]), f64(case.k_r[b]),
+                       f64(case.w_uk), f64(case.w_uv), base=case.dims.rope_base, rows=rows,
+                       heads=heads)
+
+
+def _check_pool(case, pool, batches=None):
+    d = case.dims
+    bits = pool_bits(pool)
+    for b in (range(case.batch) if batches is None else batches):
+        pages = case.table[b][: (case.seq_len + d.page_size - 1) // d.page_size]
+        fill = np.nan if d.dtype == "f32" else 0xFFBF
+        sub = np.full((len(pages), d.page_size, d.row), fill,
+                      dtype=np.float32 if d.dtype == "f32" else np.uint16)
+        want = append_expected(sub, np.arange(len(pages)), 0, f64(case.c_kv[b]), f64(case.k_r[b]),
+                               base=d.rope_base, dtype=d.dtype)
+        got = bits[pages]
+        if d.dtype == "f32":
+            assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), f"pool of seq {b}"
+        else:
+            np.testing.assert_array_equal(got, want, err_msg=f"pool of seq {b}")
+
+
+def test_tiny_fp32_prefill():
+    """Tiny fp32 layer, two prompts of 70 tokens: every row and head."""
+    print("case tiny prefill 2x70", flush=True)
+    case = syn.prefill_case(syn.TINY, 2, 70, seed=4)
+    _, pool, _, out = _run(case)
+    _check_pool(case, pool)
+    for b in range(case.batch):
+        assert_close(f64(out[b]), _oracle(case, b), f"tiny prefill seq {b}")
+
+
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 200, 257])
+def test_v2_prefill_small(T):
+    """V2 sizes, short prompts around the 64-token tile and page edges: every
+    row, every head, and the cache bytes."""
+    print(f"case v2 prefill 2x{T}", flush=True)
+    case = syn.prefill_case(syn.V2, 2, T, seed=6)
+    _, pool, _, out = _run(case)
+    _check_pool(case, pool)
+    for b in range(case.batch):
+        assert_close(f64(out[b]), _oracle(case, b), f"v2 prefill T={T} seq {b}")
+
+
+def test_v2_prefill_last_row_matches_decode():
+    """The last prompt row of prefill and a decode step over the cache that
+    prefill wrote are two routes to the same attention output."""
+    print("case prefill/decode cross-path", flush=True)
+    T = 333
+    case = syn.prefill_case(syn.V2, 2, T, seed=8)
+    dims, pool, table, out = _run(case)
+    seq_lens = torch.full((case.batch,), T, dtype=torch.int32, device=DEV)
+    dec = mla.decode(dims, pool, table, seq_lens, case.q_c[:, T - 1].contiguous().to(DEV),
+                     case.q_r[:, T - 1].contiguous().to(DEV), case.w_uk.to(DEV),
+                     case.w_uv.to(DEV))
+    torch.cuda.synchronize()
+    for b in range(case.batch):
+        ref = _oracle(case, b, rows=[T - 1])[0]
+        assert_close(f64(out[b, T - 1]), ref, f"prefill last row seq {b}")
+        assert_close(f64(dec[b]), ref, f"decode seq {b}")
+        ref_dec = decode_ref(f64(case.q_c[b, T - 1]), f64(case.q_r[b, T - 1]), f64(case.c_kv[b]),
+                             f64(case.k_r[b]), f64(case.w_uk), f64(case.w_uv),
+                             base=case.dims.rope_base)
+        np.testing.assert_allclose(ref_dec, ref, rtol=1e-10, atol=1e-12)
+        assert_close(f64(out[b, T - 1]), f64(dec[b]), f"prefill vs decode seq {b}")
+
+
+def test_v2_prefill_2x4k_full_size_sampled():
+    """Two prompts of 4096 tokens: sampled rows (tile edges, the first and last
+    rows) and heads of both prompts against the oracle, plus the cache bytes."""
+    print("case v2_prefill_2x4k", flush=True)
+    case = syn.config_case("v2_prefill_2x4k")
+    _, pool, _, out = _run(case)
+    assert torch.isfinite(out.float()).all()
+    rows = np.array([0, 1, 63, 64, 255, 256, 1000, 2047, 3333, 4095])
+    rng = np.random.default_rng(21)
+    heads = np.sort(rng.choice(case.dims.n_heads, size=6, replace=False))
+    for b in range(case.batch):
+        got = f64(out[b])[rows][:, heads]
+        assert_close(got, _oracle(case, b, rows=rows, heads=heads), f"2x4k seq {b}")
+    _check_pool(case, pool, batches=[1])
