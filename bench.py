@@ -47,6 +47,8 @@ def parse():
                     help="wall-clock budget of the oracle sample (cpu_baseline)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches only")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill measurement")
+    ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device copy of this many bytes (HBM counter calibration)")
     return ap.parse_args()
@@ -195,6 +197,10 @@ def main():
         except Exception:
             traffic = None
 
+    pre = None
+    if not args.no_prefill:
+        pre = prefill_bench(mla, syn, dims, dev, args.prefill_steps)
+
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(case0, args.cpu_seconds)
@@ -239,8 +245,59 @@ def main():
                      "frac": round(kern_tflops / MFMA_BF16_PEAK_TFLOPS, 4)},
         },
         "cpu_baseline": cpu,
+        "prefill": pre,
     }
     print(json.dumps(line), flush=True)
+
+
+def prefill_bench(mla, syn, dims, dev, steps: int):
+    """Un-absorbed causal prefill of two 4096-token prompts (bulk append, K/V
+    expansion, causal attention): prompt tokens/s and the MFMA fraction of the
+    expansion + attention kernels (timed with the library's events)."""
+    import numpy as np
+    import torch
+
+    print("[bench] prefill 2 x 4096", file=sys.stderr, flush=True)
+    case = syn.config_case("v2_prefill_2x4k")
+    B, T, H = case.batch, case.seq_len, case.dims.n_heads
+    d = case.dims
+    pool = torch.zeros((case.num_pages, d.page_size, d.row), dtype=d.torch_dtype, device=dev)
+    table = torch.from_numpy(case.table).to(dev)
+    args = [case.q_c.to(dev), case.q_r.to(dev), case.c_kv.to(dev), case.k_r.to(dev),
+            case.w_uk.to(dev), case.w_uv.to(dev)]
+    del case
+    ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    for e in ev:
+        e.record()
+    call, out = mla.prefill(dims, pool, table, *args, prepare=True)
+    call_t, _ = mla.prefill(dims, pool, table, *args, out=out, timing_events=ev, prepare=True)
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        call()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    kern = []
+    for _ in range(steps):
+        call_t()
+        torch.cuda.synchronize()
+        kern.append(ev[0].elapsed_time(ev[1]))
+    kern_ms = float(np.mean(kern))
+    pairs = B * H * T * (T + 1) // 2                       # causal (query, key) pairs
+    flop = pairs * 2 * (d.d_nope + d.d_rope + d.d_nope)    # scores + weighted sum
+    flop += 2 * B * T * d.d_latent * 2 * H * d.d_nope      # K^C and V^C expansion
+    tflops = flop / (kern_ms * 1e-3) / 1e12
+    return {"workload": "v2_prefill_2x4k: 2 prompts x 4096 tokens, causal, cache written",
+            "value": round(B * T / (ms * 1e-3), 1), "unit": "prompt tokens/s",
+            "ms_per_call": round(ms, 4), "kernels_ms": round(kern_ms, 4),
+            "roofline": {"kernel": "expand + prefill_attn", "bound": "mfma",
+                         "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "algorithmic_flop": flop}}
 
 
 def cpu_baseline(case, budget_s: float):
