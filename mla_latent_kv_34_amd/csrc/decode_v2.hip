@@ -5,23 +5,25 @@
 // 72 KiB.  Maths (haowenji [section 6]; tech note [(4) attention and output]):
 //   q_lat_i = W^UK_i^T q^C_i                        (q_absorb, MFMA GEMM)
 //   s_ij    = ([q_lat_i ; RoPE(q^R_i, t)] . [c_j ; kR_j]) / sqrt(192)
-//   o_lat_i = sum_j softmax_j(s_i) c_j              (decode_splitkv + combine)
-//   o_i     = W^UV_i o_lat_i                        (out_absorb, MFMA GEMM)
+//   o_lat_i = sum_j softmax_j(s_i) c_j              (decode_splitkv + combine_out)
+//   o_i     = W^UV_i o_lat_i                        (combine_out, MFMA GEMM)
 //
 // decode_splitkv is the hot loop.  Its work is balanced in units of 64-token
 // tiles: the tiles of all sequences are laid end to end and workgroup w takes
 // tiles [w*N/W, (w+1)*N/W).  A workgroup is 4 waves; wave v owns heads
 // 32v..32v+31 for both products, so every cache tile is fetched from HBM once
-// into LDS (direct-to-LDS 16-byte loads, double buffered) and read by all
-// four waves.  Per 32-token block a wave computes S^T = K . Q^T with
-// v_mfma_f32_32x32x16_bf16 (A = token-major tile rows, B = the head's query in
-// registers) so each lane owns one head's scores; the online softmax is then
-// lane-local apart from one cross-half max.  The probabilities feed the
-// second product O^T = V^T . P^T directly from registers (the k-slot order of
-// the A operand is chosen to match the S^T result layout), and V^T comes from
-// the same LDS tile through ds_read_b64_tr_b16 transpose reads.  Partial
-// results (running max, sum, un-normalised o_lat) go to slot w + b of the
-// workspace; combine merges the slots of each sequence.
+// into LDS and read by all four waves.  The tiles stream through a ring of
+// four 32-token sub-tiles filled by direct-to-LDS 16-byte loads running three
+// sub-tiles ahead of the compute.  Per sub-tile a wave computes
+// S^T = K . Q^T with v_mfma_f32_32x32x16_bf16 (A = token-major tile rows,
+// B = the head's query in registers) so each lane owns one head's scores; the
+// online softmax is then lane-local apart from one cross-half max.  The
+// probabilities feed the second product O^T = V^T . P^T directly from
+// registers (the k-slot order of the A operand is chosen to match the S^T
+// result layout), and V^T comes from the same LDS tile through
+// ds_read_b64_tr_b16 transpose reads.  Partial results (running max, sum,
+// un-normalised o_lat) go to slot w + b of the workspace; combine_out merges
+// the slots of each sequence and applies W^UV.
 #include "mla_internal.h"
 
 namespace mla {
@@ -59,7 +61,7 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 // Workspace layout
 // ---------------------------------------------------------------------------
 struct WsLayout {
-  size_t plan, plan_wg, q_abs, part_ml, part_o, o_lat, total;
+  size_t plan, plan_wg, q_abs, part_ml, part_o, total;
   WsLayout(int B, int W) {
     const size_t slots = (size_t)W + B;
     plan = 0;
@@ -67,8 +69,7 @@ struct WsLayout {
     q_abs = align256(plan_wg + sizeof(int32_t) * 4 * (size_t)W);
     part_ml = align256(q_abs + (size_t)B * H * ROW * 2);
     part_o = align256(part_ml + slots * H * 2 * sizeof(float));
-    o_lat = align256(part_o + slots * H * DL * sizeof(float));
-    total = align256(o_lat + (size_t)B * H * DL * sizeof(float));
+    total = align256(part_o + slots * H * DL * sizeof(float));
   }
 };
 
@@ -92,45 +93,70 @@ __device__ __forceinline__ int launched_of_logical(int w, int We) {
   return 8 * (w - (x * q8 + min(x, r8))) + x;
 }
 
-__global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ seq_lens, int B,
-                                                    int W, int32_t* __restrict__ plan,
-                                                    int4* __restrict__ wg) {
-  __shared__ int32_t part[1024];
-  __shared__ int32_t carry;
-  if (threadIdx.x == 0) carry = 0;
-  __syncthreads();
-  for (int base = 0; base < B; base += 1024) {
-    const int b = base + threadIdx.x;
+constexpr int PLAN_NT = 256;      // threads of the block that builds the plan
+constexpr int PLAN_CACHE = 4096;  // sequences whose tile count and prefix stay in LDS
+
+// Builds the plan with one block of PLAN_NT threads.  cache: LDS scratch of
+// 2 * PLAN_CACHE ints (tile counts and exclusive prefixes of the first
+// PLAN_CACHE sequences, so the second pass does not read them back from
+// global memory).
+__device__ void plan_block(const int32_t* __restrict__ seq_lens, int B, int W,
+                           int32_t* __restrict__ plan, int4* __restrict__ wg, int32_t* cache) {
+  __shared__ int32_t wsum[PLAN_NT / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int32_t* c_tiles = cache;
+  int32_t* c_pre = cache + PLAN_CACHE;
+  int carry = 0;  // tiles of the sequences before this chunk (same in every thread)
+  for (int base = 0; base < B; base += PLAN_NT) {
+    const int b = base + tid;
     const int len = b < B ? seq_lens[b] : 0;
     const int tiles = len > 0 ? (len + PS - 1) / PS : 0;
-    part[threadIdx.x] = tiles;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {  // inclusive Hillis-Steele scan
-      const int v = threadIdx.x >= off ? part[threadIdx.x - off] : 0;
-      __syncthreads();
-      part[threadIdx.x] += v;
-      __syncthreads();
+    int x = tiles;  // inclusive scan inside the wave
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(x, off);
+      if (lane >= off) x += y;
     }
-    if (b < B) plan[b] = carry + part[threadIdx.x] - tiles;
+    if (lane == 63) wsum[wave] = x;
     __syncthreads();
-    if (threadIdx.x == 1023) carry += part[1023];
-    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int v = 0; v < PLAN_NT / 64; ++v) {
+      before += v < wave ? wsum[v] : 0;
+      total += wsum[v];
+    }
+    const int excl = carry + before + x - tiles;
+    if (b < B) {
+      plan[b] = excl;
+      if (b < PLAN_CACHE) {
+        c_tiles[b] = tiles;
+        c_pre[b] = excl;
+      }
+    }
+    carry += total;
+    __syncthreads();  // wsum is reused by the next chunk; the cache is complete
   }
   // never more workgroups than tiles, so that no workgroup is left empty
   const int We = max(1, min(W, carry));
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     plan[B] = carry;
     plan[3 * B + 1] = We;
   }
-  __syncthreads();
   const long long N = carry;
-  for (int ib = We + threadIdx.x; ib < W; ib += 1024) wg[ib] = make_int4(0, 0, 0, 0);
-  for (int b = threadIdx.x; b < B; b += 1024) {
-    const int len = seq_lens[b];
-    const int tiles = len > 0 ? (len + PS - 1) / PS : 0;
+  for (int ib = We + tid; ib < W; ib += PLAN_NT) wg[ib] = make_int4(0, 0, 0, 0);
+  for (int b = tid; b < B; b += PLAN_NT) {
+    int tiles, x0i;
+    if (b < PLAN_CACHE) {
+      tiles = c_tiles[b];
+      x0i = c_pre[b];
+    } else {
+      const int len = seq_lens[b];
+      tiles = len > 0 ? (len + PS - 1) / PS : 0;
+      x0i = plan[b];  // written by this thread in the first pass
+    }
     int first = 1, last = 0;
     if (tiles > 0) {
-      const long long x0 = plan[b], x1 = x0 + tiles - 1;
+      const long long x0 = x0i, x1 = x0 + tiles - 1;
       first = (int)(((x0 + 1) * We - 1) / N);
       last = (int)(((x1 + 1) * We - 1) / N);
       // the workgroups whose range starts inside this sequence
@@ -143,54 +169,84 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
     plan[B + 1 + 2 * b] = first;
     plan[B + 2 + 2 * b] = last;
   }
-  if (N == 0 && threadIdx.x == 0) wg[0] = make_int4(0, 0, 0, 0);
+  if (N == 0 && tid == 0) wg[0] = make_int4(0, 0, 0, 0);
 }
 
 // ---------------------------------------------------------------------------
 // q_absorb: q_abs[b, i, 0:512] = W^UK_i^T q^C_{b,i}, q_abs[b, i, 512:576] =
-// RoPE(q^R_{b,i}, seq_len_b - 1).  One workgroup per (head, 64-column chunk).
+// RoPE(q^R_{b,i}, seq_len_b - 1).  One workgroup per (head, 128-column chunk),
+// after workgroup 0, which builds the split plan (plan_block).
 // D^T[c][b] = sum_r W[r][c] q[b][r] with W^T read from LDS by transpose reads.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256)
 q_absorb_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_rope,
                 const uint16_t* __restrict__ w_uk, const int32_t* __restrict__ seq_lens, int B,
-                double base, uint16_t* __restrict__ q_abs) {
-  __shared__ __attribute__((aligned(16))) char wl[DC * 128];  // [128 rows r][64 cols], swizzled
-  const int h = blockIdx.x >> 3, chunk = blockIdx.x & 7;
-  const int c0 = chunk * 64;
-  const int tid = threadIdx.x;
-  // stage W^UK_h[:, c0:c0+64]: 128 rows x 8 chunks of 16 bytes
-  for (int i = tid; i < DC * 8; i += 256) {
-    const int r = i >> 3, ch = i & 7;
-    const uint4 v = *(const uint4*)(w_uk + ((size_t)(h * DC + r) * DL + c0 + ch * 8));
-    *(uint4*)(wl + r * 128 + ((ch ^ swz_w(r)) << 4)) = v;
+                double base, uint16_t* __restrict__ q_abs, int W, int32_t* __restrict__ plan,
+                int4* __restrict__ plan_wg) {
+  // workgroup 0 builds the split plan; it is dispatched first, so it runs
+  // beside the absorption workgroups instead of after them
+  // W^UK_h[:, c0:c0+128] as two [128 rows r][64 cols] halves, swizzled
+  __shared__ __attribute__((aligned(16))) char wl[2 * DC * 128];
+  static_assert(2 * DC * 128 >= 2 * PLAN_CACHE * 4, "plan cache must fit the tile buffer");
+  if (blockIdx.x == 0) {
+    plan_block(seq_lens, B, W, plan, plan_wg, (int32_t*)wl);
+    return;
   }
-  if (chunk == 0) {  // rotated query RoPE part
-    for (int i = tid; i < B * (DR / 2); i += 256) {
+  const int h = (blockIdx.x - 1) >> 2, chunk = (blockIdx.x - 1) & 3;
+  const int c0 = chunk * 128;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 5, n = lane & 31;
+  const int nblk = (B + 31) / 32;
+  // B operand q^T[r][b] of an item (32 queries): 8 consecutive r of query b
+  // for each of the 8 k-steps; the first item's loads go out before staging
+  bf16x8 bq[DC / 16], bq_next[DC / 16];
+  auto load_q = [&](int item, bf16x8 (&dst)[DC / 16]) {
+    const int b = (item >> 2) * 32 + n;
+    const uint16_t* qp = q_nope + ((size_t)min(b, B - 1) * H + h) * DC + 8 * g;
+#pragma unroll
+    for (int s = 0; s < DC / 16; ++s) dst[s] = *(const bf16x8*)(qp + 16 * s);
+  };
+  if (wave < 4 * nblk) load_q(wave, bq);
+  // stage the W^UK tile (128 rows x 16 chunks of 16 bytes): all eight loads
+  // of a thread are issued before the first LDS store
+  {
+    uint4 wv[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int i = tid + 256 * k, r = i >> 4, ch = i & 15;
+      wv[k] = *(const uint4*)(w_uk + ((size_t)(h * DC + r) * DL + c0 + ch * 8));
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int i = tid + 256 * k, r = i >> 4, ch = i & 15;
+      *(uint4*)(wl + (ch >> 3) * (DC * 128) + r * 128 + (((ch & 7) ^ swz_w(r)) << 4)) = wv[k];
+    }
+  }
+  {  // rotated query RoPE part: the 4 column-chunk workgroups of the head share it
+    for (int i = chunk * 256 + tid; i < B * (DR / 2); i += 4 * 256) {
       const int b = i / (DR / 2), k = i % (DR / 2);
+      const size_t src = ((size_t)b * H + h) * DR + 2 * k;
+      const uint32_t pair = *(const uint32_t*)(q_rope + src);
       const int len = seq_lens[b];
       const double pos = len > 0 ? (double)(len - 1) : 0.0;
-      const size_t src = ((size_t)b * H + h) * DR + 2 * k;
       double ra, rb;
-      rope_pair_f64((double)bf16_bits_to_f32(q_rope[src]), (double)bf16_bits_to_f32(q_rope[src + 1]),
-                    pos, k, DR, base, &ra, &rb);
+      rope_pair_f64((double)bf16_bits_to_f32((uint16_t)(pair & 0xffff)),
+                    (double)bf16_bits_to_f32((uint16_t)(pair >> 16)), pos, k, DR, base, &ra, &rb);
       const size_t dst = ((size_t)b * H + h) * ROW + DL + 2 * k;
-      q_abs[dst] = bf16_bits_rne_f64(ra);
-      q_abs[dst + 1] = bf16_bits_rne_f64(rb);
+      *(uint32_t*)(q_abs + dst) = (uint32_t)bf16_bits_rne_f64(ra) | ((uint32_t)bf16_bits_rne_f64(rb) << 16);
     }
   }
   __syncthreads();
-  const int wave = tid >> 6, lane = tid & 63;
-  const int g = lane >> 5, n = lane & 31;
   const int G = lane >> 4, s16 = lane & 15;
-  const int nblk = (B + 31) / 32;
   // transpose-read geometry: source row r = 16s + 8*(G/2) + s16/4 (+4), column
   // 16*(G%2) + 4*(s16%4) of the 32-column block mc
   const int rsub = 8 * (G >> 1) + (s16 >> 2);
   const int colsub = 16 * (G & 1) + 4 * (s16 & 3);
-  for (int item = wave; item < 2 * nblk; item += 4) {
-    const int mc = item & 1, nb = item >> 1;
+  for (int item = wave; item < 4 * nblk; item += 4) {
+    const int mc = item & 3, nb = item >> 2;
     const int b = nb * 32 + n;
+    if (item + 4 < 4 * nblk) load_q(item + 4, bq_next);  // the next item's queries
     f32x16 acc = {};
 #pragma unroll
     for (int s = 0; s < DC / 16; ++s) {
@@ -199,22 +255,15 @@ q_absorb_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __restrict_
 #pragma unroll
       for (int hlf = 0; hlf < 2; ++hlf) {
         const int r = 16 * s + rsub + 4 * hlf;
-        const int col = mc * 32 + colsub;
+        const int col = (mc & 1) * 32 + colsub;
         const int ch = col >> 3;
-        const char* p = wl + r * 128 + ((ch ^ swz_w(r)) << 4) + ((col & 4) << 1);
+        const char* p = wl + (mc >> 1) * (DC * 128) + r * 128 + ((ch ^ swz_w(r)) << 4) + ((col & 4) << 1);
         s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) s16x4*)(p));
         a01[hlf] = __builtin_bit_cast(bf16x4, v);
       }
       const bf16x8 a = __builtin_shufflevector(a01[0], a01[1], 0, 1, 2, 3, 4, 5, 6, 7);
-      // B = q^T[r][b]: 8 consecutive r of query b
-      bf16x8 bq;
-      if (b < B) {
-        bq = *(const bf16x8*)(q_nope + ((size_t)b * H + h) * DC + 16 * s + 8 * g);
-      } else {
-        bq = (bf16x8){};
-      }
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[s], acc, 0, 0, 0);
     }
     if (b < B) {
       uint16_t* dst = q_abs + ((size_t)b * H + h) * ROW + c0 + mc * 32;
@@ -229,6 +278,8 @@ q_absorb_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __restrict_
         *(ushort4*)(dst + c) = v;
       }
     }
+#pragma unroll
+    for (int s = 0; s < DC / 16; ++s) bq[s] = bq_next[s];
   }
 }
 
@@ -292,6 +343,14 @@ __device__ __forceinline__ void issue_sub(const char* __restrict__ src, char* bu
                                      0, 0);
 }
 
+// A position in the workgroup's sub-tile stream: sub-tile u (0 or 1, the
+// 32-token halves) of tile t, which is page t - pbeg of sequence b (tiles
+// [pbeg, pend), len tokens).  The second half of a page is skipped when it
+// holds no token.
+struct SubCursor {
+  int b, pbeg, pend, len, t, u;
+};
+
 __global__ void __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(1, 1)))
 decode_splitkv_kernel(const char* __restrict__ pool, int num_pages, const int32_t* __restrict__ table,
@@ -304,7 +363,9 @@ decode_splitkv_kernel(const char* __restrict__ pool, int num_pages, const int32_
   const int t0 = mine.x, t1 = mine.y, w = mine.w;
   if (t0 >= t1) return;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  // wave-uniform (so the copy bases stay scalar and each copy takes a 32-bit
+  // lane offset)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int g = lane >> 5, n = lane & 31;
   const int head = wave * 32 + n;
   // QK A-operand geometry: row n of the sub-tile, 16-byte chunk 2s+g
@@ -327,256 +388,381 @@ decode_splitkv_kernel(const char* __restrict__ pool, int num_pages, const int32_
 
   const DmaPlan dp = make_dma_plan(wave, lane);
   const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)lds);
-  int b = mine.z;
-  int t = t0;
-  while (t < t1) {
-    int pbeg = plan[b], pend = plan[b + 1];
-    while (pend <= t) {  // sequences without pages
-      ++b;
-      pbeg = pend;
-      pend = plan[b + 1];
+
+  auto advance = [&](SubCursor& c) {
+    if (c.u == 0 && PS * (c.t - c.pbeg) + SUB < c.len) {
+      c.u = 1;
+      return;
     }
-    const int seg_end = min(t1, pend);
-    const int32_t* trow_tab = table + (size_t)b * max_pages;
-    const int len = seq_lens[b];
-    // query fragments (B operand of S^T = K Q^T): 8 consecutive dims per lane
-    bf16x8 qreg[KSTEPS];
+    c.u = 0;
+    ++c.t;
+    if (c.t < t1 && c.t >= c.pend) {
+      while (c.pend <= c.t) {  // next sequence with pages
+        ++c.b;
+        c.pbeg = c.pend;
+        c.pend = plan[c.b + 1];
+      }
+      c.len = seq_lens[c.b];
+    }
+  };
+  SubCursor cc;
+  cc.b = mine.z;
+  cc.pbeg = plan[cc.b];
+  cc.pend = plan[cc.b + 1];
+  cc.len = seq_lens[cc.b];
+  cc.t = t0;
+  cc.u = 0;
+
+  // ---- DMA side: sub-tile k of the stream goes to LDS slot k % NBUF
+  SubCursor ic = cc;
+  int issued = 0;
+  int okmask = 0;  // bit s: the sub-tile in slot s comes from a usable page
+  // page id of the issue cursor's tile (-1 if unusable or past the range)
+  auto page_at_ic = [&]() {
+    const int j = ic.t - ic.pbeg;
+    return (ic.t < t1 && j < max_pages) ? table[(size_t)ic.b * max_pages + j] : -1;
+  };
+  auto issue_next = [&]() {
+    if (ic.t >= t1) return;
+    const int p = page_at_ic();
+    const bool ok = p >= 0 && p < num_pages;
+    const int slot = issued & (NBUF - 1);
+    okmask = (okmask & ~(1 << slot)) | ((ok ? 1 : 0) << slot);
+    issue_sub(pool + (size_t)(ok ? p : 0) * TILEB + ic.u * SUBB, lds + slot * SUBB, wave, dp);
+    ++issued;
+    advance(ic);
+  };
+  // The same copy split in three parts spread over a step, so the copies of
+  // the four waves do not all queue up at once in front of the address unit.
+  // copy_begin claims the next sub-tile (page id prefetched by the caller).
+  const char* cp_src = pool;
+  char* cp_dst = lds;
+  bool cp_on = false;
+  auto copy_begin = [&](int p) {
+    cp_on = ic.t < t1;
+    if (!cp_on) return;
+    const bool ok = p >= 0 && p < num_pages;
+    const int slot = issued & (NBUF - 1);
+    okmask = (okmask & ~(1 << slot)) | ((ok ? 1 : 0) << slot);
+    cp_src = pool + (size_t)(ok ? p : 0) * TILEB + ic.u * SUBB + wave * 8 * ROWB;
+    cp_dst = lds + slot * SUBB + wave * 8 * ROWB;
+    ++issued;
+    advance(ic);
+  };
+  auto copy_part = [&](int m0, int m1) {
+    if (!cp_on) return;
+#pragma unroll
+    for (int m = m0; m < m1; ++m)
+      __builtin_amdgcn_global_load_lds((const void*)(cp_src + dp.off[m]),
+                                       (__attribute__((address_space(3))) void*)(cp_dst + m * 1024),
+                                       16, 0, 0);
+  };
+
+  // The first copies: the next sub-tile, or (past the end of the range) a
+  // second copy of sub-tile 0 into a slot that is never read, so that the
+  // number of copies after the query loads is fixed.
+  auto issue_or_repeat = [&]() {
+    if (ic.t < t1) {
+      issue_next();
+    } else {
+      const int slot = issued & (NBUF - 1);  // a slot past the last sub-tile
+      issue_sub(pool, lds + slot * SUBB, wave, dp);  // page 0 always exists
+      ++issued;
+    }
+  };
+  // rows of sub-tile c that hold tokens (0 if its page is unusable)
+  auto valid_rows = [&](const SubCursor& c, int slot) {
+    return ((okmask >> slot) & 1) ? min(SUB, c.len - PS * (c.t - c.pbeg) - SUB * c.u) : 0;
+  };
+  // Rows past the sequence end (or of an unusable page) may hold any bits; a
+  // zero probability times a NaN row would still poison the P.V product, so
+  // each wave clears the rows its own loads wrote.
+  auto sanitize = [&](int slot, int valid) {
+    if (valid < SUB) {
+      char* buf = lds + slot * SUBB;
+      for (int r = max(valid, 8 * wave); r < 8 * wave + 8; ++r)
+        for (int o = lane * 16; o < ROWB; o += 1024) *(uint4*)(buf + r * ROWB + o) = make_uint4(0, 0, 0, 0);
+      wait_lgkmcnt_0();
+    }
+  };
+  auto qk_addr = [&](int slot, uint32_t (&a)[4]) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) a[k] = lds_base + (uint32_t)slot * SUBB + (uint32_t)xo[k];
+  };
+  auto pv_addr = [&](int slot, uint32_t (&v)[4]) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = lds_base + (uint32_t)slot * SUBB + (uint32_t)vo[k];
+  };
+  // query fragments (B operand of S^T = K Q^T): 8 consecutive dims per lane
+  bf16x8 qreg[KSTEPS];
+  auto qptr = [&](int b) { return q_abs + ((size_t)b * H + head) * ROW + 8 * g; };
+
+  // ---- prologue: the queries, then three sub-tiles in flight.  The copy
+  // count after the query loads is fixed (issue_or_repeat), so the compiler's
+  // wait for the queries at the first score chain leaves the copies in flight.
+  {
+    const uint16_t* qp = qptr(cc.b);
+#pragma unroll
+    for (int s2 = 0; s2 < KSTEPS; ++s2) qreg[s2] = *(const bf16x8*)(qp + 16 * s2);
+  }
+  issue_or_repeat();
+  issue_or_repeat();
+  issue_or_repeat();
+  f32x16 acc[DL / 32];
+#pragma unroll
+  for (int cb = 0; cb < DL / 32; ++cb) acc[cb] = (f32x16){};
+  float m_run = -INFINITY, l_part = 0.f;
+
+  // ---- the stream: the copies run up to three sub-tiles ahead
+  for (int i = 0;; ++i) {
+    const int slot = i & (NBUF - 1);
+    SubCursor nx = cc;
+    advance(nx);
+    const bool has_next = nx.t < t1;
+    const bool seg_end = !has_next || nx.b != cc.b;
+    const int pg_next = page_at_ic();  // requested now, used after the waits below
+    // sub-tiles issued after i: up to two
     {
-      const uint16_t* qp = q_abs + ((size_t)b * H + head) * ROW + 8 * g;
-#pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) qreg[s] = *(const bf16x8*)(qp + 16 * s);
-    }
-    // sub-tiles of this segment: pages [t - pbeg, seg_end - pbeg), two per
-    // page, none past the sequence end
-    const int u0 = 2 * (t - pbeg);
-    const int u1 = min(2 * (seg_end - pbeg), (len + SUB - 1) / SUB);
-    f32x16 acc[DL / 32];
-#pragma unroll
-    for (int cb = 0; cb < DL / 32; ++cb) acc[cb] = (f32x16){};
-    float m_run = -INFINITY, l_part = 0.f;
-
-    // The segment runs in windows of up to 64 pages: the window's page ids are
-    // loaded once, one per lane, and read back with readlane.
-    for (int wu = u0; wu < u1; wu += 128) {
-    const int nsub = min(128, u1 - wu);
-    const int pbase = wu >> 1;
-    const int pvec = pbase + lane < max_pages ? trow_tab[pbase + lane] : -1;
-    // physical page of sub-tile u of this window (-1 if the entry is unusable)
-    auto page_of = [&](int u) -> int {
-      const int j = u >> 1;
-      const int p = __builtin_amdgcn_readlane(pvec, j - pbase);
-      return (j < max_pages && p >= 0 && p < num_pages) ? p : -1;
-    };
-    int okmask = 0;  // bit i: the sub-tile in LDS buffer i has a usable page
-    auto issue = [&](int u, int p, int slot) {
-      okmask = (okmask & ~(1 << slot)) | ((p >= 0 ? 1 : 0) << slot);
-      issue_sub(pool + (size_t)(p >= 0 ? p : 0) * TILEB + (u & 1) * SUBB, lds + slot * SUBB, wave, dp);
-    };
-    // all prologue page ids first, so no copy is issued before the ids arrive
-    int pro[NBUF - 1];
-#pragma unroll
-    for (int i = 0; i < NBUF - 1; ++i) pro[i] = page_of(wu + i);
-    raw_barrier();  // every wave is done with every buffer
-#pragma unroll
-    for (int i = 0; i < NBUF - 1; ++i)
-      if (i < nsub) issue(wu + i, pro[i], i);
-
-    for (int k = 0; k < nsub; ++k) {
-      const int u = wu + k;
-      char* buf = lds + (k & (NBUF - 1)) * SUBB;
-      // sub-tiles issued after this one: min(2, nsub - 1 - k)
-      const int later = min(2, nsub - 1 - k);
-      if (later >= 2) wait_vmcnt<2 * DMA_SUB>();
-      else if (later == 1) wait_vmcnt<DMA_SUB>();
+      const int after = issued - i - 1;
+      if (after >= 2) wait_vmcnt<2 * DMA_SUB>();
+      else if (after == 1) wait_vmcnt<DMA_SUB>();
       else wait_vmcnt<0>();
-      const bool page_ok = (okmask >> (k & (NBUF - 1))) & 1;
-      const int valid = page_ok ? min(SUB, len - SUB * u) : 0;
-      if (valid < SUB) {
-        // Rows past the sequence end (or of an unusable page) may hold any
-        // bits; a zero probability times a NaN row would still poison the
-        // P.V product, so each wave clears the rows its own loads wrote.
-        for (int r = max(valid, 8 * wave); r < 8 * wave + 8; ++r)
-          for (int o = lane * 16; o < ROWB; o += 1024) *(uint4*)(buf + r * ROWB + o) = make_uint4(0, 0, 0, 0);
-        wait_lgkmcnt_0();
-      }
-      raw_barrier();  // sub-tile k is in LDS and every wave is done with sub-tile k-1
-      if (k + NBUF - 1 < nsub) issue(u + NBUF - 1, page_of(u + NBUF - 1), (k + NBUF - 1) & (NBUF - 1));
-
-      // ---- S^T = K Q^T for the 32 tokens
-      const uint32_t boff = lds_base + (uint32_t)(k & (NBUF - 1)) * SUBB;
+    }
+    const int valid = valid_rows(cc, slot);
+    sanitize(slot, valid);
+    raw_barrier();  // sub-tile i is in LDS; every wave is done with sub-tile i - 1
+    // sub-tile i + 3 goes into the slot of sub-tile i - 1 (at the end of a
+    // segment only after the next sequence's queries are in, below)
+    if (!seg_end) copy_begin(pg_next);
+    else cp_on = false;
+    copy_part(0, 3);
+    // ---- S^T = K Q^T for the 32 tokens
+    f32x16 sacc;
+    {
       uint32_t qa[4];
+      qk_addr(slot, qa);
+      qk_chain(qreg, qa, sacc);
+    }
+    copy_part(3, 6);
+    // ---- online softmax in log2 units; lane = one head, 16 tokens per lane
+    if (valid < SUB) {
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) qa[kk] = boff + (uint32_t)xo[kk];
-      f32x16 s_even, s_odd;
-      qk_subtile(qreg, qa, s_even, s_odd);
-      f32x16 sacc = s_even + s_odd;
-      // ---- online softmax in log2 units; lane = one head, 16 tokens per lane
-      if (valid < SUB) {
+      for (int r = 0; r < 16; ++r)
+        if (8 * (r >> 2) + 4 * g + (r & 3) >= valid) sacc[r] = -INFINITY;
+    }
+    float mx = sacc[0];
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (8 * (i >> 2) + 4 * g + (i & 3) >= valid) sacc[i] = -INFINITY;
-      }
-      float mx = sacc[0];
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
+    {  // the other 16 tokens of this head sit in lane n ^ 32
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                       false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * sc_log2;
+    }
+    // The reference m_run moves only when some head's maximum rose by more
+    // than 8 (probabilities stay below 2^8); the rescale of the running sums
+    // is written as AGPR read / multiply / write so the accumulators stay in
+    // AGPRs.
+    if (__any(mx > m_run + 8.0f)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = (m_run == -INFINITY) ? 0.f : exp2_fast(m_run - m_new);
 #pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * sc_log2;
-      // The reference m_run moves only when some head's maximum rose by more
-      // than 8 (probabilities stay below 2^8); the rescale of the running sums
-      // is written as AGPR read / multiply / write so the accumulators stay in
-      // AGPRs.
-      if (__any(mx > m_run + 8.0f)) {
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = (m_run == -INFINITY) ? 0.f : exp2_fast(m_run - m_new);
+      for (int cb = 0; cb < DL / 32; ++cb)
 #pragma unroll
-        for (int cb = 0; cb < DL / 32; ++cb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            float x = acc[cb][i];
-            float tmp;
-            asm volatile(
-                "v_accvgpr_read_b32 %1, %0\n\t"
-                "v_mul_f32 %1, %1, %2\n\t"
-                "v_accvgpr_write_b32 %0, %1"
-                : "+a"(x), "=&v"(tmp)
-                : "v"(alpha));
-            acc[cb][i] = x;
-          }
-        asm volatile("s_nop 7");
-        l_part *= alpha;
-        m_run = m_new;
-      }
-      // (m_run is still -inf only while every token so far was masked; then
-      // every score here is -inf too and every probability 0)
-      const float nm = (m_run == -INFINITY) ? 0.f : -m_run;
-      bf16x8 pb[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          const float p = exp2_fast(__builtin_fmaf(sacc[8 * kb + jj], sc_log2, nm));
-          l_part += p;
-          pb[kb][jj] = (__bf16)p;
+        for (int r = 0; r < 16; ++r) {
+          float x = acc[cb][r];
+          float tmp;
+          asm volatile(
+              "v_accvgpr_read_b32 %1, %0\n\t"
+              "v_mul_f32 %1, %1, %2\n\t"
+              "v_accvgpr_write_b32 %0, %1"
+              : "+a"(x), "=&v"(tmp)
+              : "v"(alpha));
+          acc[cb][r] = x;
         }
-      // ---- O^T += V^T P^T over 16 blocks of 32 latent columns
+      asm volatile("s_nop 7");
+      l_part *= alpha;
+      m_run = m_new;
+    }
+    // (m_run is still -inf only while every token so far was masked; then
+    // every score here is -inf too and every probability 0)
+    const float nm = (m_run == -INFINITY) ? 0.f : -m_run;
+    // probabilities of tokens 0..15 here; those of tokens 16..31 are computed
+    // while the MFMAs of the first half run
+    bf16x8 p0, p1;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const float p = exp2_fast(__builtin_fmaf(sacc[jj], sc_log2, nm));
+      l_part += p;
+      p0[jj] = (__bf16)p;
+    }
+    {
       uint32_t va[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) va[i] = boff + (uint32_t)vo[i];
-      pv_subtile(acc, pb, va);
+      pv_addr(slot, va);
+      pv_half0_exp(acc, p0, va, sacc, sc_log2, nm, l_part, p1);
+      copy_part(6, DMA_SUB);
+      pv_half1(acc, p1, va);
     }
-    }  // window
-    // ---- write this segment's partial result to slot w + b
-    const float l_tot = l_part + __shfl_xor(l_part, 32);
-    const size_t slot = (size_t)w + b;
-    if (g == 0) {
-      float2 ml;
-      ml.x = m_run;
-      ml.y = l_tot;
-      *(float2*)(part_ml + (slot * H + head) * 2) = ml;
-    }
-    float* po = part_o + (slot * H + head) * DL;
-#pragma unroll
-    for (int cb = 0; cb < DL / 32; ++cb)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        float4 v;
-        v.x = acc[cb][4 * q4 + 0];
-        v.y = acc[cb][4 * q4 + 1];
-        v.z = acc[cb][4 * q4 + 2];
-        v.w = acc[cb][4 * q4 + 3];
-        *(float4*)(po + 32 * cb + 8 * q4 + 4 * g) = v;
+    if (seg_end) {
+      // ---- this segment's partial result to slot w + b
+      const float l_tot = l_part + __shfl_xor(l_part, 32);
+      const size_t pslot = (size_t)w + cc.b;
+      if (g == 0) {
+        float2 ml;
+        ml.x = m_run;
+        ml.y = l_tot;
+        *(float2*)(part_ml + (pslot * H + head) * 2) = ml;
       }
-    t = seg_end;
-    ++b;
+      float* po = part_o + (pslot * H + head) * DL;
+#pragma unroll
+      for (int cb = 0; cb < DL / 32; ++cb)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          float4 v;
+          v.x = acc[cb][4 * q4 + 0];
+          v.y = acc[cb][4 * q4 + 1];
+          v.z = acc[cb][4 * q4 + 2];
+          v.w = acc[cb][4 * q4 + 3];
+          *(float4*)(po + 32 * cb + 8 * q4 + 4 * g) = v;
+        }
+      if (!has_next) break;
+      // the next sequence's queries (waited for inside the block, which also
+      // waits for the stores above and the two copies in flight), then the
+      // held-back copy
+      load_q_sync(qreg, qptr(nx.b));
+      copy_begin(pg_next);
+      copy_part(0, DMA_SUB);
+#pragma unroll
+      for (int cb = 0; cb < DL / 32; ++cb) acc[cb] = (f32x16){};
+      m_run = -INFINITY;
+      l_part = 0.f;
+    }
+    cc = nx;
   }
 }
 
 // ---------------------------------------------------------------------------
-// combine: o_lat[b, i, :] = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s over
-// the slots (w + b) of the workgroups w that covered sequence b.
+// combine_out: one workgroup per (head h, block of 32 sequences).
+//  1. combine: o_lat[b] = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s over
+//     the partial slots (w + b) of the workgroups w that covered sequence b
+//     (M = max_s m_s), kept in LDS as bf16 hi + lo parts (hi = bf16(x), lo =
+//     bf16(x - hi)) so the bf16 MFMA below sees o_lat to ~16 bits.
+//  2. out_absorb: out[b, h, r] = sum_c W^UV[h, r, c] o_lat[b, c] as
+//     O^T = W^UV_h o_lat^T; wave v owns rows 32v..32v+31, its W^UV fragments
+//     are loaded before step 1 so their latency hides behind it.
+// LDS rows are 1 KiB (512 bf16); chunk c of row b sits at chunk c ^ (b & 15),
+// so a 16-lane read of one chunk of 16 rows hits 16 distinct bank groups.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(64)
-combine_kernel(const int32_t* __restrict__ plan, int B, const float* __restrict__ part_ml,
-               const float* __restrict__ part_o, float* __restrict__ o_lat) {
-  const int b = blockIdx.x / H, h = blockIdx.x % H;
-  const int first = plan[B + 1 + 2 * b], last = plan[B + 2 + 2 * b];
-  const int c = threadIdx.x * 8;
-  float* dst = o_lat + ((size_t)b * H + h) * DL + c;
-  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  if (first <= last) {
-    float M = -INFINITY;
-    for (int w = first; w <= last; ++w) M = fmaxf(M, part_ml[(((size_t)w + b) * H + h) * 2]);
-    float L = 0.f;
+constexpr int CO_NB = 32;
+
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+combine_out_kernel(const int32_t* __restrict__ plan, int B, const float* __restrict__ part_ml,
+                   const float* __restrict__ part_o, const uint16_t* __restrict__ w_uv,
+                   uint16_t* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) char ohi[CO_NB * DL * 2];
+  __shared__ __attribute__((aligned(16))) char olo[CO_NB * DL * 2];
+  __shared__ float s_max[CO_NB], s_inv[CO_NB];
+  __shared__ int s_first[CO_NB], s_last[CO_NB];
+  const int nbb = (B + CO_NB - 1) / CO_NB;
+  const int h = blockIdx.x / nbb, b0 = (blockIdx.x % nbb) * CO_NB;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 5, n = lane & 31;
+
+  // W^UV_h rows 32 * wave + n: the A operand of every k-step
+  bf16x8 wf[DL / 16];
+  {
+    const uint16_t* wr = w_uv + ((size_t)h * DC + 32 * wave + n) * DL + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < DL / 16; ++ks) wf[ks] = *(const bf16x8*)(wr + 16 * ks);
+  }
+
+  // ---- 1a. per sequence: reference maximum and 1 / sum
+  if (tid < CO_NB) {
+    const int b = b0 + tid;
+    int first = 1, last = 0;
+    float M = -INFINITY, Lsum = 0.f;
+    if (b < B) {
+      first = plan[B + 1 + 2 * b];
+      last = plan[B + 2 + 2 * b];
+      for (int w = first; w <= last; ++w) M = fmaxf(M, part_ml[(((size_t)w + b) * H + h) * 2]);
+      for (int w = first; w <= last; ++w) {
+        const size_t sl = ((size_t)w + b) * H + h;
+        const float m = part_ml[sl * 2];
+        Lsum += (m == -INFINITY ? 0.f : exp2_fast(m - M)) * part_ml[sl * 2 + 1];
+      }
+    }
+    s_first[tid] = first;
+    s_last[tid] = last;
+    s_max[tid] = M;
+    s_inv[tid] = Lsum > 0.f ? 1.f / Lsum : 0.f;
+  }
+  __syncthreads();
+  // ---- 1b. merged latent vectors into LDS.  Thread t merges sequence t / 8,
+  // float4 columns t % 8 + 8j (j = 0..15): the 8 threads of a sequence read
+  // 128 contiguous bytes per load, and a thread has 16 loads in flight per slot.
+  {
+    const int i = tid >> 3, cq = tid & 7;
+    const int b = b0 + i;
+    float4 o[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) o[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    const int first = s_first[i], last = s_last[i];
+    const float M = s_max[i];
     for (int w = first; w <= last; ++w) {
       const size_t sl = ((size_t)w + b) * H + h;
-      const float m = part_ml[sl * 2], l = part_ml[sl * 2 + 1];
-      const float e = (m == -INFINITY) ? 0.f : exp2_fast(m - M);
-      L += e * l;
-      const float4 a = *(const float4*)(part_o + sl * DL + c);
-      const float4 bb = *(const float4*)(part_o + sl * DL + c + 4);
-      o[0] += e * a.x; o[1] += e * a.y; o[2] += e * a.z; o[3] += e * a.w;
-      o[4] += e * bb.x; o[5] += e * bb.y; o[6] += e * bb.z; o[7] += e * bb.w;
-    }
-    const float inv = L > 0.f ? 1.f / L : 0.f;
+      const float m = part_ml[sl * 2];
+      const float e = m == -INFINITY ? 0.f : exp2_fast(m - M);
+      const float4* src = (const float4*)(part_o + sl * DL) + cq;
+      float4 v[16];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) o[k] *= inv;
-  }
-  *(float4*)dst = make_float4(o[0], o[1], o[2], o[3]);
-  *(float4*)(dst + 4) = make_float4(o[4], o[5], o[6], o[7]);
-}
-
-// ---------------------------------------------------------------------------
-// out_absorb: out[b, i, r] = sum_c W^UV[i, r, c] o_lat[b, i, c].
-// One wave per (head, 32 output rows); D[b][r] with both operands read as
-// 16-byte rows straight from global memory.  o_lat is kept in fp32 and fed to
-// the bf16 MFMA as hi + lo parts (hi = bf16(x), lo = bf16(x - hi)), so its
-// rounding does not add to the output error.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ void split_bf16x8(const float* src, bf16x8* hi, bf16x8* lo) {
-  const float4 a = *(const float4*)src;
-  const float4 b = *(const float4*)(src + 4);
-  const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      for (int j = 0; j < 16; ++j) v[j] = src[8 * j];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const __bf16 h = (__bf16)v[k];
-    (*hi)[k] = h;
-    (*lo)[k] = (__bf16)(v[k] - (float)h);
-  }
-}
-
-__global__ void __launch_bounds__(64)
-out_absorb_kernel(const float* __restrict__ o_lat, const uint16_t* __restrict__ w_uv, int B,
-                  uint16_t* __restrict__ out) {
-  const int h = blockIdx.x >> 2, rb = blockIdx.x & 3;
-  const int lane = threadIdx.x, g = lane >> 5, n = lane & 31;
-  const int r = rb * 32 + n;
-  const uint16_t* wrow = w_uv + ((size_t)h * DC + r) * DL + 8 * g;
-  const int nblk = (B + 31) / 32;
-  for (int mb0 = 0; mb0 < nblk; mb0 += 4) {
-    const int cnt = min(4, nblk - mb0);
-    f32x16 acc[4] = {};
-#pragma unroll 2
-    for (int s = 0; s < DL / 16; ++s) {
-      const bf16x8 wf = *(const bf16x8*)(wrow + 16 * s);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        if (k < cnt) {
-          const int b = (mb0 + k) * 32 + n;
-          bf16x8 hi = (bf16x8){}, lo = (bf16x8){};
-          if (b < B) split_bf16x8(o_lat + ((size_t)b * H + h) * DL + 16 * s + 8 * g, &hi, &lo);
-          acc[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hi, wf, acc[k], 0, 0, 0);
-          acc[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lo, wf, acc[k], 0, 0, 0);
-        }
+      for (int j = 0; j < 16; ++j) {
+        o[j].x += e * v[j].x;
+        o[j].y += e * v[j].y;
+        o[j].z += e * v[j].z;
+        o[j].w += e * v[j].w;
       }
     }
+    const float inv = s_inv[i];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      if (k < cnt) {
+    for (int j = 0; j < 16; ++j) {
+      const int c = 4 * (cq + 8 * j);
+      const float x[4] = {o[j].x * inv, o[j].y * inv, o[j].z * inv, o[j].w * inv};
+      uint32_t hi2[2], lo2[2];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int b = (mb0 + k) * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-          if (b < B) out[((size_t)b * H + h) * DC + r] = bf16_bits_rne_f32(acc[k][i]);
-        }
+      for (int k = 0; k < 2; ++k) {
+        const __bf16 h0 = (__bf16)x[2 * k], h1 = (__bf16)x[2 * k + 1];
+        const __bf16 l0 = (__bf16)(x[2 * k] - (float)h0), l1 = (__bf16)(x[2 * k + 1] - (float)h1);
+        hi2[k] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+        lo2[k] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
       }
+      const int byte = i * (DL * 2) + (((c >> 3) ^ (i & 15)) << 4) + (c & 7) * 2;
+      *(uint2*)(ohi + byte) = make_uint2(hi2[0], hi2[1]);
+      *(uint2*)(olo + byte) = make_uint2(lo2[0], lo2[1]);
+    }
+  }
+  __syncthreads();
+  // ---- 2. O^T[r][b] = sum_c W[r][c] o_lat[b][c]
+  f32x16 acc = {};
+#pragma unroll
+  for (int ks = 0; ks < DL / 16; ++ks) {
+    const int byte = n * (DL * 2) + (((2 * ks + g) ^ (n & 15)) << 4);
+    const bf16x8 bh = *(const bf16x8*)(ohi + byte);
+    const bf16x8 bl = *(const bf16x8*)(olo + byte);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ks], bh, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ks], bl, acc, 0, 0, 0);
+  }
+  const int b = b0 + n;
+  if (b < B) {
+    uint16_t* dst = out + ((size_t)b * H + h) * DC + 32 * wave + 4 * g;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      ushort4 v;
+      v.x = bf16_bits_rne_f32(acc[4 * q4 + 0]);
+      v.y = bf16_bits_rne_f32(acc[4 * q4 + 1]);
+      v.z = bf16_bits_rne_f32(acc[4 * q4 + 2]);
+      v.w = bf16_bits_rne_f32(acc[4 * q4 + 3]);
+      *(ushort4*)(dst + 8 * q4) = v;
     }
   }
 }
@@ -596,13 +782,11 @@ hipError_t launch_v2_decode(const Layer& L, const void* pool, int num_pages, con
   uint16_t* q_abs = (uint16_t*)(base + lay.q_abs);
   float* part_ml = (float*)(base + lay.part_ml);
   float* part_o = (float*)(base + lay.part_o);
-  float* o_lat = (float*)(base + lay.o_lat);
   const float sc_log2 = L.scale * 1.4426950408889634f;
   int4* plan_wg = (int4*)(base + lay.plan_wg);
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, seq_lens, batch, n_wg, plan, plan_wg);
-  hipLaunchKernelGGL(q_absorb_kernel, dim3(H * 8), dim3(256), 0, s, (const uint16_t*)q_nope,
+  hipLaunchKernelGGL(q_absorb_kernel, dim3(H * 4 + 1), dim3(256), 0, s, (const uint16_t*)q_nope,
                      (const uint16_t*)q_rope, (const uint16_t*)w_uk, seq_lens, batch, L.rope_base,
-                     q_abs);
+                     q_abs, n_wg, plan, plan_wg);
   hipError_t e = mark(ev, 0, s);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_splitkv_kernel, dim3(n_wg), dim3(256), 0, s, (const char*)pool,
@@ -610,10 +794,8 @@ hipError_t launch_v2_decode(const Layer& L, const void* pool, int num_pages, con
                      (const int4*)plan_wg, part_ml, part_o, sc_log2);
   e = mark(ev, 1, s);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(combine_kernel, dim3(batch * H), dim3(64), 0, s, plan, batch, part_ml, part_o,
-                     o_lat);
-  hipLaunchKernelGGL(out_absorb_kernel, dim3(H * 4), dim3(64), 0, s, o_lat,
-                     (const uint16_t*)w_uv, batch, (uint16_t*)out);
+  hipLaunchKernelGGL(combine_out_kernel, dim3(H * ((batch + CO_NB - 1) / CO_NB)), dim3(256), 0, s,
+                     plan, batch, part_ml, part_o, (const uint16_t*)w_uv, (uint16_t*)out);
   return hipGetLastError();
 }
 

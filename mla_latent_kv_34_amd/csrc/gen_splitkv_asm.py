@@ -1,109 +1,187 @@
-"""Generate splitkv_asm.h: the two inner MFMA chains of decode_splitkv as
+"""Generate splitkv_asm.h: the inner MFMA chains of decode_splitkv as
 inline-assembly blocks for gfx950.
 
-Each block issues its own LDS reads, waits for them inside the block
-(s_waitcnt lgkmcnt) before the MFMA that consumes them, and ends with enough
-wait states for a following VALU or accumulator read of its MFMA results, so
-no load is ever in flight when the block returns.  The reads land in the
-fixed scratch registers v240..v255 (declared clobbered); four 4-register
-slots rotate so that an LDS read never targets the operand of the MFMA
-issued just before it.
+Every block issues its own LDS reads and waits for them inside the block
+(s_waitcnt lgkmcnt) before the MFMA that consumes them, so no LDS read is in
+flight when a block returns.  The reads land in the fixed scratch registers
+v232..v255 (declared clobbered): six 4-register slots rotate so that a read
+never targets an operand of an MFMA still to be issued; reads run five MFMAs
+ahead, which covers the LDS latency when four waves read at once.
+
+Per 32-token sub-tile the kernel runs qk_chain (S^T = K Q^T), the row
+maximum and the first half's probabilities in C++, then pv_half0_exp: the
+MFMAs of the first 16 tokens' P.V while the VALU computes the second half's
+probabilities (exp2(s * c - m), their sum and their bf16 packing), and
+pv_half1.  The VALU instructions are interleaved between the MFMAs so they
+issue while the matrix core is busy; they write registers no MFMA of the block
+reads, and a v_exp_f32 result is read no sooner than two instructions later.
+load_q_sync loads a sequence's query fragments and waits for them inside the
+block.
 
 Run: python gen_splitkv_asm.py > splitkv_asm.h
 """
 
 ROWB = 1152        # bytes per cached row
 KSTEPS = 36        # 576 / 16
-NSLOT = 4
-SLOT0 = 240        # first scratch VGPR
+NSLOT = 6
+AHEAD = 5
 XDL_TO_VALU_NOPS = ["s_nop 7", "s_nop 7", "s_nop 7"]  # 24 wait states
+QK_SPLIT = 12      # k-steps of S(i+1) issued in qk_max; the rest in qk_exp
 
 
-def slot(i):
+SLOT0 = 256 - 4 * NSLOT  # first scratch VGPR
+
+
+def _slot(i, half=None):
     b = SLOT0 + 4 * (i % NSLOT)
-    return b
+    if half == 0:
+        return f"v[{b}:{b + 1}]"
+    if half == 1:
+        return f"v[{b + 2}:{b + 3}]"
+    return f"v[{b}:{b + 3}]"
 
 
-def qk_block():
-    """S^T = K Q^T over one 32-token sub-tile: 36 k-steps, two accumulators
-    (even / odd k-steps) so consecutive MFMAs are independent."""
+CLOBBER = ", ".join(f'"v{r}"' for r in range(SLOT0, SLOT0 + 4 * NSLOT))
+
+
+def _emit(lines):
+    return "\n".join(f'      "{l}\\n\\t"' for l in lines)
+
+
+def _qk_read(s):
+    return f"ds_read_b128 {_slot(s)}, %[a{s & 3}] offset:{(s >> 2) * 128}"
+
+
+def _qk_mfma(s, first):
+    src_c = "0" if s == first else "%[s]"
+    return f"v_mfma_f32_32x32x16_bf16 %[s], {_slot(s)}, %[q{s}], {src_c}"
+
+
+def _qk_lines(s0, s1, valu):
+    """MFMAs for k-steps s0..s1-1 into %[s] with their reads, and the VALU
+    instructions in `valu` spread over the MFMA slots."""
     lines = ["s_waitcnt lgkmcnt(0)"]
+    n = s1 - s0
+    for s in range(s0, min(s0 + AHEAD, s1)):
+        lines.append(_qk_read(s))
+    per = [[] for _ in range(n)]
+    for j, v in enumerate(valu):
+        per[min(n - 1, j * n // max(1, len(valu)))].append(v)
+    for i, s in enumerate(range(s0, s1)):
+        lines.append(f"s_waitcnt lgkmcnt({min(AHEAD - 1, s1 - 1 - s)})")
+        lines.append(_qk_mfma(s, 0))
+        if s + AHEAD < s1:
+            lines.append(_qk_read(s + AHEAD))
+        lines += per[i]
+    return lines
 
-    def rd(s):
-        b = slot(s)
-        return f"ds_read_b128 v[{b}:{b + 3}], %[a{s & 3}] offset:{(s >> 2) * 128}"
 
-    for s in range(3):
-        lines.append(rd(s))
-    for s in range(KSTEPS):
-        lines.append(f"s_waitcnt lgkmcnt({min(2, KSTEPS - 1 - s)})")
-        b = slot(s)
-        acc = "%[s0]" if s % 2 == 0 else "%[s1]"
-        src_c = "0" if s < 2 else acc
-        lines.append(f"v_mfma_f32_32x32x16_bf16 {acc}, v[{b}:{b + 3}], %[q{s}], {src_c}")
-        if s + 3 < KSTEPS:
-            lines.append(rd(s + 3))
-    lines += XDL_TO_VALU_NOPS
-    body = "\n".join(f'      "{l}\\n\\t"' for l in lines)
-    outs = '[s0] "=&v"(s0), [s1] "=&v"(s1)'
-    ins = ", ".join([f'[q{s}] "v"(q[{s}])' for s in range(KSTEPS)] +
-                    [f'[a{k}] "v"(a[{k}])' for k in range(4)])
-    clob = ", ".join(f'"v{r}"' for r in range(SLOT0, SLOT0 + 4 * NSLOT))
+def _qins(s0, s1):
+    return [f'[q{s}] "v"(q[{s}])' for s in range(s0, s1)] + [f'[a{k}] "v"(a[{k}])' for k in range(4)]
+
+
+def qk_chain():
+    """S = K Q^T over one 32-token sub-tile, 36 MFMAs into one accumulator
+    (a dependent chain issues at the full rate), ending with the wait states
+    for a VALU read of S."""
+    lines = _qk_lines(0, KSTEPS, []) + XDL_TO_VALU_NOPS
+    outs = '[s] "=&v"(s)'
+    ins = ", ".join(_qins(0, KSTEPS))
     return f"""// S^T (32 tokens x 32 heads) = K Q^T for one sub-tile.  a[k]: LDS byte
-// address of this lane's row chunk for k-steps s with s % 4 == k (line
-// s / 4 is the immediate offset); q[s]: the query fragment of k-step s.
-// s0 / s1 receive the even / odd k-step partial sums.
-__device__ __forceinline__ void qk_subtile(const bf16x8 (&q)[{KSTEPS}], const uint32_t (&a)[4],
-                                           f32x16& s0, f32x16& s1) {{
+// address of this lane's row chunk for k-steps s with s % 4 == k (line s / 4
+// is the immediate offset); q[s]: the query fragment of k-step s.
+__device__ __forceinline__ void qk_chain(const bf16x8 (&q)[{KSTEPS}], const uint32_t (&a)[4],
+                                         f32x16& s) {{
   asm volatile(
-{body}
+{_emit(lines)}
       : {outs}
       : {ins}
-      : {clob});
+      : {CLOBBER});
 }}
 """
 
 
-def pv_block():
-    """O^T += V^T P^T over one sub-tile: 32 MFMAs (two 16-token halves x 16
-    blocks of 32 latent columns), the V^T operand from two transpose reads."""
+def pv_half(kb, with_exp):
+    """O^T += V^T P^T for one 16-token half kb of the sub-tile: 16 MFMAs over
+    the blocks of 32 latent columns.  With with_exp the probabilities of the
+    other half (tokens 16..31, S^T entries 8..15 of this lane) are computed on
+    the VALU meanwhile: p = exp2(s * sc + nm), packed to bf16 into p1, summed
+    into l; the 8 score registers are overwritten."""
+    name = f"pv_half{kb}" + ("_exp" if with_exp else "")
     lines = ["s_waitcnt lgkmcnt(0)", "s_nop 4"]
-    n = 32
+    n = 16
 
     def rd(i):
-        kb, cb = i // 16, i % 16
-        b = slot(i)
+        cb = i
         off = 16 * kb * ROWB + (cb >> 1) * 128
-        return [f"ds_read_b64_tr_b16 v[{b}:{b + 1}], %[v{cb & 1}] offset:{off}",
-                f"ds_read_b64_tr_b16 v[{b + 2}:{b + 3}], %[w{cb & 1}] offset:{off}"]
+        return [f"ds_read_b64_tr_b16 {_slot(i, 0)}, %[v{cb & 1}] offset:{off}",
+                f"ds_read_b64_tr_b16 {_slot(i, 1)}, %[w{cb & 1}] offset:{off}"]
 
-    for i in range(3):
+    valu = []
+    if with_exp:
+        valu = [f"v_fma_f32 %[e{k}], %[e{k}], %[sc], %[nm]" for k in range(8)]
+        valu += [f"v_exp_f32 %[e{k}], %[e{k}]" for k in range(8)]
+        valu += [f"v_cvt_pk_bf16_f32 %[q{k}], %[e{2 * k}], %[e{2 * k + 1}]" for k in range(4)]
+        valu += [f"v_add_f32 %[e{2 * k}], %[e{2 * k}], %[e{2 * k + 1}]" for k in range(4)]
+        valu += ["v_add_f32 %[e0], %[e0], %[e2]", "v_add_f32 %[e4], %[e4], %[e6]",
+                 "v_add_f32 %[e0], %[e0], %[e4]", "v_add_f32 %[l], %[l], %[e0]"]
+    per = [[] for _ in range(n)]
+    for j, v in enumerate(valu):
+        per[min(n - 1, j * n // max(1, len(valu)))].append(v)
+    for i in range(AHEAD):
         lines += rd(i)
     for i in range(n):
-        kb, cb = i // 16, i % 16
-        lines.append(f"s_waitcnt lgkmcnt({2 * min(2, n - 1 - i)})")
-        b = slot(i)
-        lines.append(f"v_mfma_f32_32x32x16_bf16 %[c{cb}], v[{b}:{b + 3}], %[p{kb}], %[c{cb}]")
-        if i + 3 < n:
-            lines += rd(i + 3)
+        cb = i
+        lines.append(f"s_waitcnt lgkmcnt({2 * min(AHEAD - 1, n - 1 - i)})")
+        lines.append(f"v_mfma_f32_32x32x16_bf16 %[c{cb}], {_slot(i)}, %[p], %[c{cb}]")
+        if i + AHEAD < n:
+            lines += rd(i + AHEAD)
+        lines += per[i]
     lines += XDL_TO_VALU_NOPS
-    body = "\n".join(f'      "{l}\\n\\t"' for l in lines)
-    outs = ", ".join(f'[c{c}] "+a"(acc[{c}])' for c in range(16))
-    ins = ('[p0] "v"(p[0]), [p1] "v"(p[1]), [v0] "v"(v[0]), [v1] "v"(v[1]), '
-           '[w0] "v"(v[2]), [w1] "v"(v[3])')
-    clob = ", ".join(f'"v{r}"' for r in range(SLOT0, SLOT0 + 4 * NSLOT))
-    return f"""// O^T (512 latent columns x 32 heads) += V^T P^T for one sub-tile.  v[par]
-// and v[2 + par]: LDS byte addresses of this lane's first and second
-// transpose-read sources (rows trow and trow + 8) for column blocks of parity
-// par (16-token halves and column pairs are immediates); p[kb]: the bf16
-// probabilities of tokens 16kb..16kb+15 in k-slot order.
-__device__ __forceinline__ void pv_subtile(f32x16 (&acc)[16], const bf16x8 (&p)[2],
-                                           const uint32_t (&v)[4]) {{
-  asm volatile(
+    outs = [f'[c{c}] "+a"(acc[{c}])' for c in range(16)]
+    ins = ['[p] "v"(p)', '[v0] "v"(v[0])', '[v1] "v"(v[1])', '[w0] "v"(v[2])', '[w1] "v"(v[3])']
+    if with_exp:
+        outs += ['[l] "+v"(l)'] + [f'[e{k}] "+v"(s[{8 + k}])' for k in range(8)]
+        outs += [f'[q{k}] "=&v"(pw[{k}])' for k in range(4)]
+        ins += ['[sc] "v"(sc)', '[nm] "v"(nm)']
+        sig = ("f32x16 (&acc)[16], const bf16x8& p, const uint32_t (&v)[4], f32x16& s, float sc, "
+               "float nm, float& l, bf16x8& p1")
+        pre = "  uint32_t pw[4];\n"
+        post = "  p1 = __builtin_bit_cast(bf16x8, (u32x4){pw[0], pw[1], pw[2], pw[3]});\n"
+    else:
+        sig = "f32x16 (&acc)[16], const bf16x8& p, const uint32_t (&v)[4]"
+        pre = post = ""
+    body = _emit(lines)
+    return f"""// O^T (512 latent columns x 32 heads) += V^T P^T for the 16-token half {kb} of
+// a sub-tile.  v[par] and v[2 + par]: LDS byte addresses of this lane's first
+// and second transpose-read sources (rows trow and trow + 8) for column blocks
+// of parity par; p: the bf16 probabilities of the half's tokens in k-slot order.
+__device__ __forceinline__ void {name}({sig}) {{
+{pre}  asm volatile(
 {body}
+      : {", ".join(outs)}
+      : {", ".join(ins)}
+      : {CLOBBER});
+{post}}}
+"""
+
+
+def load_q_sync():
+    """The 36 query fragments of a lane (bytes 32s .. 32s + 15 of its row
+    segment) loaded into the same registers and waited for inside one block,
+    so that no query load is ever in flight outside it (the wait also covers
+    older copies).  The fragments are in-out operands: they keep their
+    registers, and the address operand cannot share one of them."""
+    lines = [f"global_load_dwordx4 %[q{s}], %[p], off offset:{32 * s}" for s in range(KSTEPS)]
+    lines.append("s_waitcnt vmcnt(0)")
+    outs = ", ".join(f'[q{s}] "+v"(q[{s}])' for s in range(KSTEPS))
+    return f"""// q[s] = the 16 bytes at p + 32 s for s = 0..{KSTEPS - 1}, complete on return.
+__device__ __forceinline__ void load_q_sync(bf16x8 (&q)[{KSTEPS}], const uint16_t* p) {{
+  asm volatile(
+{_emit(lines)}
       : {outs}
-      : {ins}
-      : {clob});
+      : [p] "v"(p)
+      : "memory");
 }}
 """
 
@@ -113,8 +191,10 @@ def main():
     print("// Inner MFMA chains of decode_splitkv (see that script for the scheme).")
     print("#pragma once")
     print()
-    print(qk_block())
-    print(pv_block())
+    print(qk_chain())
+    print(pv_half(0, True))
+    print(load_q_sync())
+    print(pv_half(1, False))
 
 
 if __name__ == "__main__":

@@ -164,3 +164,19 @@ def test_v2_b4_128k_long_context_sampled():
     assert torch.isfinite(out.float()).all()
     heads = np.array([0, 77, 127])
     assert_close(f64(out[2])[heads], _oracle(case, 2, heads=heads), "128k seq 2")
+
+
+@pytest.mark.parametrize("batch,hi,n_wg", [(300, 150, 0), (300, 150, 1000), (4500, 40, 0)])
+def test_v2_many_short_sequences(batch, hi, n_wg):
+    """More sequences than one pass of the plan's prefix scan (and, at 4500,
+    more than the plan keeps in LDS); with 1000 workgroups there are fewer
+    tiles than workgroups.  A sample of sequences is checked."""
+    print(f"case many short: batch {batch}, lengths 1..{hi}, n_wg {n_wg}", flush=True)
+    lens = syn.ragged_lengths(batch, 1, hi, seed=batch)
+    case = syn.decode_case(syn.V2, lens, append=True, seed=13, shuffle=True)
+    dims, pool, table, seq_lens = device_case(case)
+    out = run_decode(case, dims, pool, table, seq_lens, n_workgroups=n_wg)
+    assert torch.isfinite(out.float()).all()
+    rng = np.random.default_rng(batch + n_wg)
+    for b in list(rng.choice(batch, size=6, replace=False)) + [0, batch - 1]:
+        assert_close(f64(out[b]), _oracle(case, b), f"seq {b} len {case.attended[b]}")
