@@ -675,25 +675,37 @@ combine_out_kernel(const int32_t* __restrict__ plan, int B, const float* __restr
     for (int ks = 0; ks < DL / 16; ++ks) wf[ks] = *(const bf16x8*)(wr + 16 * ks);
   }
 
-  // ---- 1a. per sequence: reference maximum and 1 / sum
-  if (tid < CO_NB) {
-    const int b = b0 + tid;
+  // ---- 1a. per sequence: reference maximum and 1 / sum.  The 8 threads of a
+  // sequence take its slots first + k, first + k + 8, ... (k = tid % 8) and
+  // combine their results with shuffles inside the 8-lane group.
+  {
+    const int i = tid >> 3, k = tid & 7;
+    const int b = b0 + i;
     int first = 1, last = 0;
-    float M = -INFINITY, Lsum = 0.f;
     if (b < B) {
       first = plan[B + 1 + 2 * b];
       last = plan[B + 2 + 2 * b];
-      for (int w = first; w <= last; ++w) M = fmaxf(M, part_ml[(((size_t)w + b) * H + h) * 2]);
-      for (int w = first; w <= last; ++w) {
-        const size_t sl = ((size_t)w + b) * H + h;
-        const float m = part_ml[sl * 2];
-        Lsum += (m == -INFINITY ? 0.f : exp2_fast(m - M)) * part_ml[sl * 2 + 1];
-      }
     }
-    s_first[tid] = first;
-    s_last[tid] = last;
-    s_max[tid] = M;
-    s_inv[tid] = Lsum > 0.f ? 1.f / Lsum : 0.f;
+    float M = -INFINITY;
+    for (int w = first + k; w <= last; w += 8) M = fmaxf(M, part_ml[(((size_t)w + b) * H + h) * 2]);
+    M = fmaxf(M, __shfl_xor(M, 1));
+    M = fmaxf(M, __shfl_xor(M, 2));
+    M = fmaxf(M, __shfl_xor(M, 4));
+    float Lsum = 0.f;
+    for (int w = first + k; w <= last; w += 8) {
+      const size_t sl = ((size_t)w + b) * H + h;
+      const float2 ml = *(const float2*)(part_ml + sl * 2);
+      Lsum += (ml.x == -INFINITY ? 0.f : exp2_fast(ml.x - M)) * ml.y;
+    }
+    Lsum += __shfl_xor(Lsum, 1);
+    Lsum += __shfl_xor(Lsum, 2);
+    Lsum += __shfl_xor(Lsum, 4);
+    if (k == 0) {
+      s_first[i] = first;
+      s_last[i] = last;
+      s_max[i] = M;
+      s_inv[i] = Lsum > 0.f ? 1.f / Lsum : 0.f;
+    }
   }
   __syncthreads();
   // ---- 1b. merged latent vectors into LDS.  Thread t merges sequence t / 8,
