@@ -24,6 +24,8 @@
 // ds_read_b64_tr_b16 transpose reads.  Partial results (running max, sum,
 // un-normalised o_lat) go to slot w + b of the workspace; combine_out merges
 // the slots of each sequence and applies W^UV.
+#include <cmath>
+
 #include "mla_internal.h"
 
 namespace mla {
@@ -172,6 +174,12 @@ __device__ void plan_block(const int32_t* __restrict__ seq_lens, int B, int W,
   if (N == 0 && tid == 0) wg[0] = make_int4(0, 0, 0, 0);
 }
 
+// RoPE frequencies theta_k = base^(-2k/64), computed in fp64 on the host and
+// passed by value.
+struct RopeThetas {
+  double theta[DR / 2];
+};
+
 // ---------------------------------------------------------------------------
 // q_absorb: q_abs[b, i, 0:512] = W^UK_i^T q^C_{b,i}, q_abs[b, i, 512:576] =
 // RoPE(q^R_{b,i}, seq_len_b - 1).  One workgroup per (head, 128-column chunk),
@@ -181,7 +189,7 @@ __device__ void plan_block(const int32_t* __restrict__ seq_lens, int B, int W,
 __global__ void __launch_bounds__(256)
 q_absorb_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_rope,
                 const uint16_t* __restrict__ w_uk, const int32_t* __restrict__ seq_lens, int B,
-                double base, uint16_t* __restrict__ q_abs, int W, int32_t* __restrict__ plan,
+                RopeThetas rope, uint16_t* __restrict__ q_abs, int W, int32_t* __restrict__ plan,
                 int4* __restrict__ plan_wg) {
   // workgroup 0 builds the split plan; it is dispatched first, so it runs
   // beside the absorption workgroups instead of after them
@@ -223,18 +231,39 @@ q_absorb_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __restrict_
       *(uint4*)(wl + (ch >> 3) * (DC * 128) + r * 128 + (((ch & 7) ^ swz_w(r)) << 4)) = wv[k];
     }
   }
-  {  // rotated query RoPE part: the 4 column-chunk workgroups of the head share it
-    for (int i = chunk * 256 + tid; i < B * (DR / 2); i += 4 * 256) {
-      const int b = i / (DR / 2), k = i % (DR / 2);
-      const size_t src = ((size_t)b * H + h) * DR + 2 * k;
-      const uint32_t pair = *(const uint32_t*)(q_rope + src);
-      const int len = seq_lens[b];
-      const double pos = len > 0 ? (double)(len - 1) : 0.0;
-      double ra, rb;
-      rope_pair_f64((double)bf16_bits_to_f32((uint16_t)(pair & 0xffff)),
-                    (double)bf16_bits_to_f32((uint16_t)(pair >> 16)), pos, k, DR, base, &ra, &rb);
-      const size_t dst = ((size_t)b * H + h) * ROW + DL + 2 * k;
-      *(uint32_t*)(q_abs + dst) = (uint32_t)bf16_bits_rne_f64(ra) | ((uint32_t)bf16_bits_rne_f64(rb) << 16);
+  {  // rotated query RoPE part: the 4 column-chunk workgroups of the head
+     // share it.  The angle pos * theta_k is formed and reduced to [-pi, pi]
+     // in fp64 (two-part 2 pi), then rotated in fp32: the result is rounded
+     // to bf16, far coarser than the fp32 error.
+    constexpr int PER = DR / 2;
+    for (int i0 = chunk * 256 + tid; i0 < B * PER; i0 += 2 * 4 * 256) {
+      uint32_t pair[2];
+      int len[2];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {  // both pairs' loads before any arithmetic
+        const int i = min(i0 + r * 4 * 256, B * PER - 1);
+        const int b = i / PER, k = i % PER;
+        pair[r] = *(const uint32_t*)(q_rope + ((size_t)b * H + h) * DR + 2 * k);
+        len[r] = seq_lens[b];
+      }
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int i = i0 + r * 4 * 256;
+        if (i >= B * PER) break;
+        const int b = i / PER, k = i % PER;
+        const double pos = len[r] > 0 ? (double)(len[r] - 1) : 0.0;
+        const double ang = pos * rope.theta[k];
+        const double nq = __builtin_rint(ang * 0.15915494309189535);  // 1 / (2 pi)
+        const double red = __builtin_fma(-nq, 2.4492935982947064e-16,
+                                         __builtin_fma(-nq, 6.283185307179586, ang));
+        float sn, cs;
+        sincosf((float)red, &sn, &cs);
+        const float a = bf16_bits_to_f32((uint16_t)(pair[r] & 0xffff));
+        const float bb = bf16_bits_to_f32((uint16_t)(pair[r] >> 16));
+        const float ra = a * cs - bb * sn, rb = a * sn + bb * cs;
+        *(uint32_t*)(q_abs + ((size_t)b * H + h) * ROW + DL + 2 * k) =
+            (uint32_t)bf16_bits_rne_f32(ra) | ((uint32_t)bf16_bits_rne_f32(rb) << 16);
+      }
     }
   }
   __syncthreads();
@@ -588,7 +617,7 @@ decode_splitkv_kernel(const char* __restrict__ pool, int num_pages, const int32_
     const float nm = (m_run == -INFINITY) ? 0.f : -m_run;
     // probabilities of tokens 0..15 here; those of tokens 16..31 are computed
     // while the MFMAs of the first half run
-    bf16x8 p0, p1;
+    bf16x8 p0;
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) {
       const float p = exp2_fast(__builtin_fmaf(sacc[jj], sc_log2, nm));
@@ -598,12 +627,13 @@ decode_splitkv_kernel(const char* __restrict__ pool, int num_pages, const int32_
     {
       uint32_t va[4];
       pv_addr(slot, va);
-      pv_half0_exp(acc, p0, va, sacc, sc_log2, nm, l_part, p1);
+      pv_full(acc, p0, va, sacc, sc_log2, nm, l_part);
       copy_part(6, DMA_SUB);
-      pv_half1(acc, p1, va);
     }
     if (seg_end) {
-      // ---- this segment's partial result to slot w + b
+      // ---- this segment's partial result to slot w + b (after the wait
+      // states for reading the accumulators the last MFMAs wrote)
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
       const float l_tot = l_part + __shfl_xor(l_part, 32);
       const size_t pslot = (size_t)w + cc.b;
       if (g == 0) {
@@ -660,8 +690,6 @@ combine_out_kernel(const int32_t* __restrict__ plan, int B, const float* __restr
                    uint16_t* __restrict__ out) {
   __shared__ __attribute__((aligned(16))) char ohi[CO_NB * DL * 2];
   __shared__ __attribute__((aligned(16))) char olo[CO_NB * DL * 2];
-  __shared__ float s_max[CO_NB], s_inv[CO_NB];
-  __shared__ int s_first[CO_NB], s_last[CO_NB];
   const int nbb = (B + CO_NB - 1) / CO_NB;
   const int h = blockIdx.x / nbb, b0 = (blockIdx.x % nbb) * CO_NB;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -675,67 +703,44 @@ combine_out_kernel(const int32_t* __restrict__ plan, int B, const float* __restr
     for (int ks = 0; ks < DL / 16; ++ks) wf[ks] = *(const bf16x8*)(wr + 16 * ks);
   }
 
-  // ---- 1a. per sequence: reference maximum and 1 / sum.  The 8 threads of a
-  // sequence take its slots first + k, first + k + 8, ... (k = tid % 8) and
-  // combine their results with shuffles inside the 8-lane group.
+  // ---- 1. merged latent vectors into LDS.  Thread t merges sequence t / 8,
+  // float4 columns t % 8 + 8j (j = 0..15): the 8 threads of a sequence read
+  // 128 contiguous bytes per load, and a thread has 16 loads in flight per
+  // slot.  The slots are merged online (running reference maximum, the sums
+  // rescaled when it rises), so each slot's (m, l) arrives with its vector.
   {
-    const int i = tid >> 3, k = tid & 7;
+    const int i = tid >> 3, cq = tid & 7;
     const int b = b0 + i;
     int first = 1, last = 0;
     if (b < B) {
       first = plan[B + 1 + 2 * b];
       last = plan[B + 2 + 2 * b];
     }
-    float M = -INFINITY;
-    for (int w = first + k; w <= last; w += 8) M = fmaxf(M, part_ml[(((size_t)w + b) * H + h) * 2]);
-    M = fmaxf(M, __shfl_xor(M, 1));
-    M = fmaxf(M, __shfl_xor(M, 2));
-    M = fmaxf(M, __shfl_xor(M, 4));
-    float Lsum = 0.f;
-    for (int w = first + k; w <= last; w += 8) {
-      const size_t sl = ((size_t)w + b) * H + h;
-      const float2 ml = *(const float2*)(part_ml + sl * 2);
-      Lsum += (ml.x == -INFINITY ? 0.f : exp2_fast(ml.x - M)) * ml.y;
-    }
-    Lsum += __shfl_xor(Lsum, 1);
-    Lsum += __shfl_xor(Lsum, 2);
-    Lsum += __shfl_xor(Lsum, 4);
-    if (k == 0) {
-      s_first[i] = first;
-      s_last[i] = last;
-      s_max[i] = M;
-      s_inv[i] = Lsum > 0.f ? 1.f / Lsum : 0.f;
-    }
-  }
-  __syncthreads();
-  // ---- 1b. merged latent vectors into LDS.  Thread t merges sequence t / 8,
-  // float4 columns t % 8 + 8j (j = 0..15): the 8 threads of a sequence read
-  // 128 contiguous bytes per load, and a thread has 16 loads in flight per slot.
-  {
-    const int i = tid >> 3, cq = tid & 7;
-    const int b = b0 + i;
     float4 o[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) o[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-    const int first = s_first[i], last = s_last[i];
-    const float M = s_max[i];
+    float M = -INFINITY, Lsum = 0.f;
     for (int w = first; w <= last; ++w) {
       const size_t sl = ((size_t)w + b) * H + h;
-      const float m = part_ml[sl * 2];
-      const float e = m == -INFINITY ? 0.f : exp2_fast(m - M);
+      const float2 ml = *(const float2*)(part_ml + sl * 2);
       const float4* src = (const float4*)(part_o + sl * DL) + cq;
       float4 v[16];
 #pragma unroll
       for (int j = 0; j < 16; ++j) v[j] = src[8 * j];
+      const float m_new = fmaxf(M, ml.x);
+      const float a = M == -INFINITY ? 0.f : exp2_fast(M - m_new);
+      const float e = ml.x == -INFINITY ? 0.f : exp2_fast(ml.x - m_new);
+      Lsum = Lsum * a + e * ml.y;
+      M = m_new;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        o[j].x += e * v[j].x;
-        o[j].y += e * v[j].y;
-        o[j].z += e * v[j].z;
-        o[j].w += e * v[j].w;
+        o[j].x = o[j].x * a + e * v[j].x;
+        o[j].y = o[j].y * a + e * v[j].y;
+        o[j].z = o[j].z * a + e * v[j].z;
+        o[j].w = o[j].w * a + e * v[j].w;
       }
     }
-    const float inv = s_inv[i];
+    const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int c = 4 * (cq + 8 * j);
@@ -796,9 +801,11 @@ hipError_t launch_v2_decode(const Layer& L, const void* pool, int num_pages, con
   float* part_o = (float*)(base + lay.part_o);
   const float sc_log2 = L.scale * 1.4426950408889634f;
   int4* plan_wg = (int4*)(base + lay.plan_wg);
+  RopeThetas th;
+  for (int k = 0; k < DR / 2; ++k) th.theta[k] = std::pow(L.rope_base, -2.0 * k / DR);
   hipLaunchKernelGGL(q_absorb_kernel, dim3(H * 4 + 1), dim3(256), 0, s, (const uint16_t*)q_nope,
-                     (const uint16_t*)q_rope, (const uint16_t*)w_uk, seq_lens, batch, L.rope_base,
-                     q_abs, n_wg, plan, plan_wg);
+                     (const uint16_t*)q_rope, (const uint16_t*)w_uk, seq_lens, batch, th, q_abs,
+                     n_wg, plan, plan_wg);
   hipError_t e = mark(ev, 0, s);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_splitkv_kernel, dim3(n_wg), dim3(256), 0, s, (const char*)pool,

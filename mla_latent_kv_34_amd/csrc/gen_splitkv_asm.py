@@ -42,6 +42,7 @@ def _slot(i, half=None):
 
 
 CLOBBER = ", ".join(f'"v{r}"' for r in range(SLOT0, SLOT0 + 4 * NSLOT))
+P1 = SLOT0 - 4     # v[228:231]: second-half probabilities inside pv_full
 
 
 def _emit(lines):
@@ -166,6 +167,65 @@ __device__ __forceinline__ void {name}({sig}) {{
 """
 
 
+def pv_full():
+    """O^T += V^T P^T over a whole 32-token sub-tile in one block: the 16 MFMAs
+    of tokens 0..15 (probabilities p0) while the VALU computes the
+    probabilities of tokens 16..31 from S^T entries 8..15 (exp2(s * sc + nm),
+    packed to bf16 into the fixed registers v[228:231], summed into l), then
+    the 16 MFMAs of tokens 16..31 with them.  The transpose reads run ahead
+    across the two halves.  No trailing wait states: the accumulators are next
+    read by MFMAs, or by code that waits first."""
+    lines = ["s_waitcnt lgkmcnt(0)", "s_nop 4"]
+    n = 32
+
+    def rd(i):
+        kb, cb = i // 16, i % 16
+        off = 16 * kb * ROWB + (cb >> 1) * 128
+        return [f"ds_read_b64_tr_b16 {_slot(i, 0)}, %[v{cb & 1}] offset:{off}",
+                f"ds_read_b64_tr_b16 {_slot(i, 1)}, %[w{cb & 1}] offset:{off}"]
+
+    valu = [f"v_fma_f32 %[e{k}], %[e{k}], %[sc], %[nm]" for k in range(8)]
+    valu += [f"v_exp_f32 %[e{k}], %[e{k}]" for k in range(8)]
+    valu += [f"v_cvt_pk_bf16_f32 v{P1 + k}, %[e{2 * k}], %[e{2 * k + 1}]" for k in range(4)]
+    valu += [f"v_add_f32 %[e{2 * k}], %[e{2 * k}], %[e{2 * k + 1}]" for k in range(4)]
+    valu += ["v_add_f32 %[e0], %[e0], %[e2]", "v_add_f32 %[e4], %[e4], %[e6]",
+             "v_add_f32 %[e0], %[e0], %[e4]", "v_add_f32 %[l], %[l], %[e0]"]
+    per = [[] for _ in range(16)]
+    for j, v in enumerate(valu):
+        per[j * 12 // len(valu)].append(v)  # all issued by MFMA 11
+    for i in range(AHEAD):
+        lines += rd(i)
+    for i in range(n):
+        kb, cb = i // 16, i % 16
+        lines.append(f"s_waitcnt lgkmcnt({2 * min(AHEAD - 1, n - 1 - i)})")
+        p = "%[p0]" if kb == 0 else f"v[{P1}:{P1 + 3}]"
+        lines.append(f"v_mfma_f32_32x32x16_bf16 %[c{cb}], {_slot(i)}, {p}, %[c{cb}]")
+        if i + AHEAD < n:
+            lines += rd(i + AHEAD)
+        if i < 16:
+            lines += per[i]
+    outs = [f'[c{c}] "+a"(acc[{c}])' for c in range(16)]
+    outs += ['[l] "+v"(l)'] + [f'[e{k}] "+v"(s[{8 + k}])' for k in range(8)]
+    ins = ['[p0] "v"(p0)', '[v0] "v"(v[0])', '[v1] "v"(v[1])', '[w0] "v"(v[2])', '[w1] "v"(v[3])',
+           '[sc] "v"(sc)', '[nm] "v"(nm)']
+    clob = ", ".join(f'"v{r}"' for r in range(P1, P1 + 4)) + ", " + CLOBBER
+    return f"""// O^T (512 latent columns x 32 heads) += V^T P^T for one 32-token sub-tile.
+// v[par] and v[2 + par]: LDS byte addresses of this lane's first and second
+// transpose-read sources (rows trow and trow + 8) for column blocks of parity
+// par; p0: bf16 probabilities of tokens 0..15 in k-slot order; s: the scores,
+// whose entries 8..15 (tokens 16..31) become probabilities here (overwritten);
+// l: running sum, increased by those probabilities.
+__device__ __forceinline__ void pv_full(f32x16 (&acc)[16], const bf16x8& p0, const uint32_t (&v)[4],
+                                        f32x16& s, float sc, float nm, float& l) {{
+  asm volatile(
+{_emit(lines)}
+      : {", ".join(outs)}
+      : {", ".join(ins)}
+      : {clob});
+}}
+"""
+
+
 def load_q_sync():
     """The 36 query fragments of a lane (bytes 32s .. 32s + 15 of its row
     segment) loaded into the same registers and waited for inside one block,
@@ -192,9 +252,8 @@ def main():
     print("#pragma once")
     print()
     print(qk_chain())
-    print(pv_half(0, True))
+    print(pv_full())
     print(load_q_sync())
-    print(pv_half(1, False))
 
 
 if __name__ == "__main__":
