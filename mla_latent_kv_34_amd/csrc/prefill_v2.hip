@@ -10,7 +10,7 @@
 // append has written for positions 0..T-1 before these kernels run.
 //
 // Workspace (per prompt b and head h, T rounded up to Tp = 64 * ceil(T/64)):
-//   rope  [T][32] (cos, sin) in fp64 of the query rotation angles
+//   rope  [T][32] (cos, sin) of the query rotation angles (fp64, stored fp32)
 //   K^C   [b][h][Tp][128] bf16, the 128 dims of every 16-dim group stored in
 //         the order 0-3, 8-11, 4-7, 12-15 (the k-slot order of the MFMA result
 //         layout, so the expansion writes 16-byte pieces; the query is read in
@@ -63,9 +63,10 @@ __device__ __forceinline__ void dma16(const void* src, char* lds_block) {
 }
 
 // ---------------------------------------------------------------------------
-// rope_table: tab[t][k] = (cos, sin) of t * base^(-2k/64) in fp64.
+// rope_table: tab[t][k] = (cos, sin) of t * base^(-2k/64), computed in fp64
+// and stored in fp32 (the rotated query is rounded to bf16 afterwards).
 // ---------------------------------------------------------------------------
-__global__ void rope_table_kernel(int T, double base, double2* __restrict__ tab) {
+__global__ void rope_table_kernel(int T, double base, float2* __restrict__ tab) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= T * (DR / 2)) return;
   const int t = i / (DR / 2), k = i % (DR / 2);
@@ -73,7 +74,7 @@ __global__ void rope_table_kernel(int T, double base, double2* __restrict__ tab)
   const double ang = __dmul_rn((double)t, theta);
   double s, c;
   sincos(ang, &s, &c);
-  tab[i] = make_double2(c, s);
+  tab[i] = make_float2((float)c, (float)s);
 }
 
 // ---------------------------------------------------------------------------
@@ -204,7 +205,7 @@ constexpr int AT_DMA = STAGEB / 1024 / 4;  // 10 one-KiB loads per wave per tile
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_attn_kernel(const char* __restrict__ pool, int num_pages, const int32_t* __restrict__ table,
                     int max_pages, const uint16_t* __restrict__ q_nope,
-                    const uint16_t* __restrict__ q_rope, const double2* __restrict__ rope_tab,
+                    const uint16_t* __restrict__ q_rope, const float2* __restrict__ rope_tab,
                     const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vt, int B, int T,
                     int tp, int nqb, float sc_log2, uint16_t* __restrict__ out) {
   __shared__ __attribute__((aligned(1024))) char lds[2 * STAGEB];
@@ -227,29 +228,38 @@ prefill_attn_kernel(const char* __restrict__ pool, int num_pages, const int32_t*
   {
     char* qs = lds + (wave * 64 + lane) * 192;  // 12 fragments of 16 bytes
     const uint16_t* qc = q_nope + (((size_t)b * T + lim) * H + h) * DC;
+    const uint16_t* qr = q_rope + (((size_t)b * T + lim) * H + h) * DR;
+    const float2* cs = rope_tab + (size_t)lim * (DR / 2) + 4 * g;
+    // every load first, so the staging costs one memory round trip
+    uint2 lo[8], hi[8];
+    uint4 rr[4];
+    float2 cs2[16];
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const uint2 lo = *(const uint2*)(qc + 16 * s + 4 * g);
-      const uint2 hi = *(const uint2*)(qc + 16 * s + 4 * g + 8);
-      *(uint4*)(qs + 16 * s) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      lo[s] = *(const uint2*)(qc + 16 * s + 4 * g);
+      hi[s] = *(const uint2*)(qc + 16 * s + 4 * g + 8);
     }
-    const uint16_t* qr = q_rope + (((size_t)b * T + lim) * H + h) * DR;
 #pragma unroll
-    for (int s = 8; s < 12; ++s) {
-      const int e0 = 16 * (s - 8) + 8 * g;
-      const uint4 raw = *(const uint4*)(qr + e0);
-      const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+    for (int s = 0; s < 4; ++s) {
+      rr[s] = *(const uint4*)(qr + 16 * s + 8 * g);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) cs2[4 * s + k] = cs[8 * s + k];
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) *(uint4*)(qs + 16 * s) = make_uint4(lo[s].x, lo[s].y, hi[s].x, hi[s].y);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {  // rotated q^R dims 16s + 8g .. +7 (pairs 8s + 4g + k)
+      const uint32_t w4[4] = {rr[s].x, rr[s].y, rr[s].z, rr[s].w};
       uint32_t rot[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const double2 cs = rope_tab[(size_t)lim * (DR / 2) + e0 / 2 + k];
-        const double a = (double)bf16_bits_to_f32((uint16_t)(w4[k] & 0xffff));
-        const double bb = (double)bf16_bits_to_f32((uint16_t)(w4[k] >> 16));
-        const double ra = __dsub_rn(__dmul_rn(a, cs.x), __dmul_rn(bb, cs.y));
-        const double rb = __dadd_rn(__dmul_rn(a, cs.y), __dmul_rn(bb, cs.x));
-        rot[k] = (uint32_t)bf16_bits_rne_f64(ra) | ((uint32_t)bf16_bits_rne_f64(rb) << 16);
+        const float2 c = cs2[4 * s + k];
+        const float a = bf16_bits_to_f32((uint16_t)(w4[k] & 0xffff));
+        const float bb = bf16_bits_to_f32((uint16_t)(w4[k] >> 16));
+        rot[k] = (uint32_t)bf16_bits_rne_f32(a * c.x - bb * c.y) |
+                 ((uint32_t)bf16_bits_rne_f32(a * c.y + bb * c.x) << 16);
       }
-      *(uint4*)(qs + 16 * s) = make_uint4(rot[0], rot[1], rot[2], rot[3]);
+      *(uint4*)(qs + 16 * (8 + s)) = make_uint4(rot[0], rot[1], rot[2], rot[3]);
     }
     __syncthreads();
 #pragma unroll
@@ -399,7 +409,7 @@ struct PfLayout {
   PfLayout(int B, int T) {
     tp = (T + PS - 1) / PS * PS;
     rope = 0;
-    kc = align256(rope + (size_t)T * (DR / 2) * sizeof(double2));
+    kc = align256(rope + (size_t)T * (DR / 2) * sizeof(float2));
     vt = align256(kc + (size_t)B * H * tp * DC * 2);
     total = align256(vt + (size_t)B * H * DC * tp * 2);
   }
@@ -420,7 +430,7 @@ hipError_t launch_v2_prefill(const Layer& L, const void* pool, int num_pages, co
   const int B = batch, T = seq_len;
   const PfLayout lay(B, T);
   char* w = (char*)ws;
-  double2* tab = (double2*)(w + lay.rope);
+  float2* tab = (float2*)(w + lay.rope);
   uint16_t* kc = (uint16_t*)(w + lay.kc);
   uint16_t* vt = (uint16_t*)(w + lay.vt);
   hipError_t e = mark(ev, 0, s);
@@ -435,7 +445,7 @@ hipError_t launch_v2_prefill(const Layer& L, const void* pool, int num_pages, co
   const float sc_log2 = L.scale * 1.4426950408889634f;
   hipLaunchKernelGGL(prefill_attn_kernel, dim3((unsigned)(B * H * nqb)), dim3(256), 0, s,
                      (const char*)pool, num_pages, table, max_pages, (const uint16_t*)q_nope,
-                     (const uint16_t*)q_rope, (const double2*)tab, (const uint16_t*)kc,
+                     (const uint16_t*)q_rope, (const float2*)tab, (const uint16_t*)kc,
                      (const uint16_t*)vt, B, T, lay.tp, nqb, sc_log2, (uint16_t*)out);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
