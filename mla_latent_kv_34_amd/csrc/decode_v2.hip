@@ -341,6 +341,11 @@ __device__ __forceinline__ void wait_lgkmcnt_0() {
   __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
 }
 
+// Cache policy of the cache-tile copies: non-temporal (every tile is read
+// once per decode step), so the stream does not push the weights, queries
+// and partial results out of the caches.
+constexpr int kStreamPolicy = 2;
+
 // Direct-to-LDS copy of one 32-token sub-tile: wave v copies rows 8v..8v+7
 // (nine one-KiB LDS blocks, 9216 bytes = 8 rows).  Lane i of block m writes
 // LDS bytes 1024m + 16i and reads the 16-byte chunk that the row swizzle puts
@@ -369,7 +374,7 @@ __device__ __forceinline__ void issue_sub(const char* __restrict__ src, char* bu
   for (int m = 0; m < DMA_SUB; ++m)
     __builtin_amdgcn_global_load_lds((const void*)(src0 + dp.off[m]),
                                      (__attribute__((address_space(3))) void*)(dst0 + m * 1024), 16,
-                                     0, 0);
+                                     0, kStreamPolicy);
 }
 
 // A position in the workgroup's sub-tile stream: sub-tile u (0 or 1, the
@@ -484,7 +489,7 @@ decode_splitkv_kernel(const char* __restrict__ pool, int num_pages, const int32_
     for (int m = m0; m < m1; ++m)
       __builtin_amdgcn_global_load_lds((const void*)(cp_src + dp.off[m]),
                                        (__attribute__((address_space(3))) void*)(cp_dst + m * 1024),
-                                       16, 0, 0);
+                                       16, 0, kStreamPolicy);
   };
 
   // The first copies: the next sub-tile, or (past the end of the range) a
@@ -671,79 +676,94 @@ decode_splitkv_kernel(const char* __restrict__ pool, int num_pages, const int32_
 }
 
 // ---------------------------------------------------------------------------
-// combine_out: one workgroup per (head h, block of 32 sequences).
+// combine_out: one workgroup of 8 waves per (head h, block of 32 sequences).
 //  1. combine: o_lat[b] = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s over
 //     the partial slots (w + b) of the workgroups w that covered sequence b
 //     (M = max_s m_s), kept in LDS as bf16 hi + lo parts (hi = bf16(x), lo =
-//     bf16(x - hi)) so the bf16 MFMA below sees o_lat to ~16 bits.
-//  2. out_absorb: out[b, h, r] = sum_c W^UV[h, r, c] o_lat[b, c] as
-//     O^T = W^UV_h o_lat^T; wave v owns rows 32v..32v+31, its W^UV fragments
-//     are loaded before step 1 so their latency hides behind it.
+//     bf16(x - hi)) so the bf16 MFMA below sees o_lat to ~16 bits.  Thread t
+//     merges sequence t / 16, float4 columns t % 16 + 16j (j = 0..7); the
+//     slots are taken two at a time (both sets of loads in flight together)
+//     and merged online (running reference maximum, the sums rescaled when it
+//     rises).
+//  2. out_absorb (waves 0-3): out[b, h, r] = sum_c W^UV[h, r, c] o_lat[b, c]
+//     as O^T = W^UV_h o_lat^T; wave v owns rows 32v..32v+31, its W^UV
+//     fragments are loaded before step 1 so their latency hides behind it.
 // LDS rows are 1 KiB (512 bf16); chunk c of row b sits at chunk c ^ (b & 15),
 // so a 16-lane read of one chunk of 16 rows hits 16 distinct bank groups.
 // ---------------------------------------------------------------------------
 constexpr int CO_NB = 32;
+constexpr int CO_NT = 512;
 
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(CO_NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 combine_out_kernel(const int32_t* __restrict__ plan, int B, const float* __restrict__ part_ml,
                    const float* __restrict__ part_o, const uint16_t* __restrict__ w_uv,
                    uint16_t* __restrict__ out) {
   __shared__ __attribute__((aligned(16))) char ohi[CO_NB * DL * 2];
   __shared__ __attribute__((aligned(16))) char olo[CO_NB * DL * 2];
   const int nbb = (B + CO_NB - 1) / CO_NB;
-  const int h = blockIdx.x / nbb, b0 = (blockIdx.x % nbb) * CO_NB;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // launched workgroup ib runs on XCD ib % 8: the sequence blocks of one head
+  // get neighbouring logical indices on one XCD, so W^UV_h is fetched into
+  // that XCD's L2 once
+  const int G8 = (int)gridDim.x, ib = (int)blockIdx.x;
+  const int L = (ib & 7) * (G8 >> 3) + min(ib & 7, G8 & 7) + (ib >> 3);
+  const int h = L / nbb, b0 = (L % nbb) * CO_NB;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int g = lane >> 5, n = lane & 31;
 
-  // W^UV_h rows 32 * wave + n: the A operand of every k-step
+  // W^UV_h rows 32 * wave + n: the A operand of every k-step (waves 0-3)
   bf16x8 wf[DL / 16];
-  {
+  if (wave < 4) {
     const uint16_t* wr = w_uv + ((size_t)h * DC + 32 * wave + n) * DL + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < DL / 16; ++ks) wf[ks] = *(const bf16x8*)(wr + 16 * ks);
   }
 
-  // ---- 1. merged latent vectors into LDS.  Thread t merges sequence t / 8,
-  // float4 columns t % 8 + 8j (j = 0..15): the 8 threads of a sequence read
-  // 128 contiguous bytes per load, and a thread has 16 loads in flight per
-  // slot.  The slots are merged online (running reference maximum, the sums
-  // rescaled when it rises), so each slot's (m, l) arrives with its vector.
+  // ---- 1. merged latent vectors into LDS
   {
-    const int i = tid >> 3, cq = tid & 7;
+    const int i = tid >> 4, cq = tid & 15;
     const int b = b0 + i;
     int first = 1, last = 0;
     if (b < B) {
       first = plan[B + 1 + 2 * b];
       last = plan[B + 2 + 2 * b];
     }
-    float4 o[16];
+    float4 o[8];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) o[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < 8; ++j) o[j] = make_float4(0.f, 0.f, 0.f, 0.f);
     float M = -INFINITY, Lsum = 0.f;
-    for (int w = first; w <= last; ++w) {
-      const size_t sl = ((size_t)w + b) * H + h;
-      const float2 ml = *(const float2*)(part_ml + sl * 2);
-      const float4* src = (const float4*)(part_o + sl * DL) + cq;
-      float4 v[16];
+    for (int w = first; w <= last; w += 2) {
+      const bool two = w + 1 <= last;
+      const size_t s0 = ((size_t)w + b) * H + h;
+      const size_t s1 = two ? s0 + H : s0;  // slot w + 1 (or w again, weight 0)
+      const float2 ml0 = *(const float2*)(part_ml + s0 * 2);
+      const float2 ml1 = *(const float2*)(part_ml + s1 * 2);
+      const float4* src0 = (const float4*)(part_o + s0 * DL) + cq;
+      const float4* src1 = (const float4*)(part_o + s1 * DL) + cq;
+      float4 v0[8], v1[8];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) v[j] = src[8 * j];
-      const float m_new = fmaxf(M, ml.x);
+      for (int j = 0; j < 8; ++j) {
+        v0[j] = src0[16 * j];
+        v1[j] = src1[16 * j];
+      }
+      const float m1 = two ? ml1.x : -INFINITY;
+      const float m_new = fmaxf(M, fmaxf(ml0.x, m1));
       const float a = M == -INFINITY ? 0.f : exp2_fast(M - m_new);
-      const float e = ml.x == -INFINITY ? 0.f : exp2_fast(ml.x - m_new);
-      Lsum = Lsum * a + e * ml.y;
+      const float e0 = ml0.x == -INFINITY ? 0.f : exp2_fast(ml0.x - m_new);
+      const float e1 = m1 == -INFINITY ? 0.f : exp2_fast(m1 - m_new);
+      Lsum = Lsum * a + e0 * ml0.y + e1 * (two ? ml1.y : 0.f);
       M = m_new;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        o[j].x = o[j].x * a + e * v[j].x;
-        o[j].y = o[j].y * a + e * v[j].y;
-        o[j].z = o[j].z * a + e * v[j].z;
-        o[j].w = o[j].w * a + e * v[j].w;
+      for (int j = 0; j < 8; ++j) {
+        o[j].x = o[j].x * a + e0 * v0[j].x + e1 * v1[j].x;
+        o[j].y = o[j].y * a + e0 * v0[j].y + e1 * v1[j].y;
+        o[j].z = o[j].z * a + e0 * v0[j].z + e1 * v1[j].z;
+        o[j].w = o[j].w * a + e0 * v0[j].w + e1 * v1[j].w;
       }
     }
     const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int c = 4 * (cq + 8 * j);
+    for (int j = 0; j < 8; ++j) {
+      const int c = 4 * (cq + 16 * j);
       const float x[4] = {o[j].x * inv, o[j].y * inv, o[j].z * inv, o[j].w * inv};
       uint32_t hi2[2], lo2[2];
 #pragma unroll
@@ -759,6 +779,7 @@ combine_out_kernel(const int32_t* __restrict__ plan, int B, const float* __restr
     }
   }
   __syncthreads();
+  if (wave >= 4) return;
   // ---- 2. O^T[r][b] = sum_c W[r][c] o_lat[b][c]
   f32x16 acc = {};
 #pragma unroll
@@ -813,7 +834,7 @@ hipError_t launch_v2_decode(const Layer& L, const void* pool, int num_pages, con
                      (const int4*)plan_wg, part_ml, part_o, sc_log2);
   e = mark(ev, 1, s);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(combine_out_kernel, dim3(H * ((batch + CO_NB - 1) / CO_NB)), dim3(256), 0, s,
+  hipLaunchKernelGGL(combine_out_kernel, dim3(H * ((batch + CO_NB - 1) / CO_NB)), dim3(CO_NT), 0, s,
                      plan, batch, part_ml, part_o, (const uint16_t*)w_uv, (uint16_t*)out);
   return hipGetLastError();
 }
