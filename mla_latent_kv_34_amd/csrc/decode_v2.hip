@@ -59,6 +59,26 @@ __device__ __forceinline__ int swz_w(int t) { return ((t & 3) << 1) | ((t >> 2) 
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// An accumulator element read into a VGPR (the explicit read keeps the
+// accumulators in AGPRs, which the MFMAs write).
+__device__ __forceinline__ float agpr_read(float a) {
+  float v;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+  return v;
+}
+
+// Two floats to fp16 (round to nearest even; out of range gives +-inf), packed.
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
+}
+__device__ __forceinline__ float f16_lo(uint32_t u) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(u & 0xffffu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t u) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(u >> 16));
+}
+
 // ---------------------------------------------------------------------------
 // Workspace layout
 // ---------------------------------------------------------------------------
@@ -71,7 +91,7 @@ struct WsLayout {
     q_abs = align256(plan_wg + sizeof(int32_t) * 4 * (size_t)W);
     part_ml = align256(q_abs + (size_t)B * H * ROW * 2);
     part_o = align256(part_ml + slots * H * 2 * sizeof(float));
-    total = align256(part_o + slots * H * DL * sizeof(float));
+    total = align256(part_o + slots * H * DL * sizeof(uint16_t));
   }
 };
 
@@ -391,7 +411,7 @@ decode_splitkv_kernel(const char* __restrict__ pool, int num_pages, const int32_
                       int max_pages, const int32_t* __restrict__ seq_lens, int B,
                       const uint16_t* __restrict__ q_abs, const int32_t* __restrict__ plan,
                       const int4* __restrict__ wg, float* __restrict__ part_ml,
-                      float* __restrict__ part_o, float sc_log2) {
+                      uint16_t* __restrict__ part_o, float sc_log2) {
   __shared__ __attribute__((aligned(1024))) char lds[NBUF * SUBB];
   const int4 mine = wg[blockIdx.x];  // (t0, t1, first sequence, logical index)
   const int t0 = mine.x, t1 = mine.y, w = mine.w;
@@ -647,17 +667,26 @@ decode_splitkv_kernel(const char* __restrict__ pool, int num_pages, const int32_
         ml.y = l_tot;
         *(float2*)(part_ml + (pslot * H + head) * 2) = ml;
       }
-      float* po = part_o + (pslot * H + head) * DL;
+      // o_lat / l in fp16 (a convex combination of cached rows, so bounded
+      // by their largest magnitude).  Accumulator element 8p + k of block cb
+      // is dimension 32cb + 16p + 4g + (k & 3) + 8(k >> 2); the eight go to
+      // halves 32cb + 16p + 8g + k, i.e. every aligned group of 16
+      // dimensions is stored with its middle two quarters swapped.
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      uint16_t* po = part_o + (pslot * H + head) * DL;
 #pragma unroll
       for (int cb = 0; cb < DL / 32; ++cb)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          float4 v;
-          v.x = acc[cb][4 * q4 + 0];
-          v.y = acc[cb][4 * q4 + 1];
-          v.z = acc[cb][4 * q4 + 2];
-          v.w = acc[cb][4 * q4 + 3];
-          *(float4*)(po + 32 * cb + 8 * q4 + 4 * g) = v;
+        for (int p = 0; p < 2; ++p) {
+          float x[8];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) x[k] = agpr_read(acc[cb][8 * p + k]) * inv;
+          uint4 v;
+          v.x = pack_f16x2(x[0], x[1]);
+          v.y = pack_f16x2(x[2], x[3]);
+          v.z = pack_f16x2(x[4], x[5]);
+          v.w = pack_f16x2(x[6], x[7]);
+          *(uint4*)(po + 32 * cb + 16 * p + 8 * g) = v;
         }
       if (!has_next) break;
       // the next sequence's queries (waited for inside the block, which also
@@ -696,7 +725,7 @@ constexpr int CO_NT = 512;
 
 __global__ void __launch_bounds__(CO_NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 combine_out_kernel(const int32_t* __restrict__ plan, int B, const float* __restrict__ part_ml,
-                   const float* __restrict__ part_o, const uint16_t* __restrict__ w_uv,
+                   const uint16_t* __restrict__ part_o, const uint16_t* __restrict__ w_uv,
                    uint16_t* __restrict__ out) {
   __shared__ __attribute__((aligned(16))) char ohi[CO_NB * DL * 2];
   __shared__ __attribute__((aligned(16))) char olo[CO_NB * DL * 2];
@@ -727,9 +756,13 @@ combine_out_kernel(const int32_t* __restrict__ plan, int B, const float* __restr
       first = plan[B + 1 + 2 * b];
       last = plan[B + 2 + 2 * b];
     }
-    float4 o[8];
+    // 16-byte unit u = cq + 16j of a slot row holds dimensions
+    // 16(u >> 1) + 4(u & 1) + {0..3} and the same + 8 (the partial layout)
+    float o[4][8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) o[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) o[j][k] = 0.f;
     float M = -INFINITY, Lsum = 0.f;
     for (int w = first; w <= last; w += 2) {
       const bool two = w + 1 <= last;
@@ -737,45 +770,54 @@ combine_out_kernel(const int32_t* __restrict__ plan, int B, const float* __restr
       const size_t s1 = two ? s0 + H : s0;  // slot w + 1 (or w again, weight 0)
       const float2 ml0 = *(const float2*)(part_ml + s0 * 2);
       const float2 ml1 = *(const float2*)(part_ml + s1 * 2);
-      const float4* src0 = (const float4*)(part_o + s0 * DL) + cq;
-      const float4* src1 = (const float4*)(part_o + s1 * DL) + cq;
-      float4 v0[8], v1[8];
+      const uint4* src0 = (const uint4*)(part_o + s0 * DL) + cq;
+      const uint4* src1 = (const uint4*)(part_o + s1 * DL) + cq;
+      uint4 v0[4], v1[4];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < 4; ++j) {
         v0[j] = src0[16 * j];
         v1[j] = src1[16 * j];
       }
       const float m1 = two ? ml1.x : -INFINITY;
       const float m_new = fmaxf(M, fmaxf(ml0.x, m1));
       const float a = M == -INFINITY ? 0.f : exp2_fast(M - m_new);
-      const float e0 = ml0.x == -INFINITY ? 0.f : exp2_fast(ml0.x - m_new);
-      const float e1 = m1 == -INFINITY ? 0.f : exp2_fast(m1 - m_new);
-      Lsum = Lsum * a + e0 * ml0.y + e1 * (two ? ml1.y : 0.f);
+      // slot weights 2^(m_s - M) l_s on the normalised vectors
+      const float e0 = ml0.x == -INFINITY ? 0.f : exp2_fast(ml0.x - m_new) * ml0.y;
+      const float e1 = m1 == -INFINITY ? 0.f : exp2_fast(m1 - m_new) * ml1.y;
+      Lsum = Lsum * a + e0 + e1;
       M = m_new;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        o[j].x = o[j].x * a + e0 * v0[j].x + e1 * v1[j].x;
-        o[j].y = o[j].y * a + e0 * v0[j].y + e1 * v1[j].y;
-        o[j].z = o[j].z * a + e0 * v0[j].z + e1 * v1[j].z;
-        o[j].w = o[j].w * a + e0 * v0[j].w + e1 * v1[j].w;
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t w0[4] = {v0[j].x, v0[j].y, v0[j].z, v0[j].w};
+        const uint32_t w1[4] = {v1[j].x, v1[j].y, v1[j].z, v1[j].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          o[j][2 * q] = o[j][2 * q] * a + e0 * f16_lo(w0[q]) + e1 * f16_lo(w1[q]);
+          o[j][2 * q + 1] = o[j][2 * q + 1] * a + e0 * f16_hi(w0[q]) + e1 * f16_hi(w1[q]);
+        }
       }
     }
     const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int c = 4 * (cq + 16 * j);
-      const float x[4] = {o[j].x * inv, o[j].y * inv, o[j].z * inv, o[j].w * inv};
-      uint32_t hi2[2], lo2[2];
+    for (int j = 0; j < 4; ++j) {
+      const int u = cq + 16 * j;
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const __bf16 h0 = (__bf16)x[2 * k], h1 = (__bf16)x[2 * k + 1];
-        const __bf16 l0 = (__bf16)(x[2 * k] - (float)h0), l1 = (__bf16)(x[2 * k + 1] - (float)h1);
-        hi2[k] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-        lo2[k] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+      for (int half = 0; half < 2; ++half) {
+        const int c = 16 * (u >> 1) + 4 * (u & 1) + 8 * half;
+        const float x[4] = {o[j][4 * half] * inv, o[j][4 * half + 1] * inv, o[j][4 * half + 2] * inv,
+                            o[j][4 * half + 3] * inv};
+        uint32_t hi2[2], lo2[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const __bf16 h0 = (__bf16)x[2 * k], h1 = (__bf16)x[2 * k + 1];
+          const __bf16 l0 = (__bf16)(x[2 * k] - (float)h0), l1 = (__bf16)(x[2 * k + 1] - (float)h1);
+          hi2[k] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+          lo2[k] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+        }
+        const int byte = i * (DL * 2) + (((c >> 3) ^ (i & 15)) << 4) + (c & 7) * 2;
+        *(uint2*)(ohi + byte) = make_uint2(hi2[0], hi2[1]);
+        *(uint2*)(olo + byte) = make_uint2(lo2[0], lo2[1]);
       }
-      const int byte = i * (DL * 2) + (((c >> 3) ^ (i & 15)) << 4) + (c & 7) * 2;
-      *(uint2*)(ohi + byte) = make_uint2(hi2[0], hi2[1]);
-      *(uint2*)(olo + byte) = make_uint2(lo2[0], lo2[1]);
     }
   }
   __syncthreads();
@@ -819,7 +861,7 @@ hipError_t launch_v2_decode(const Layer& L, const void* pool, int num_pages, con
   int32_t* plan = (int32_t*)(base + lay.plan);
   uint16_t* q_abs = (uint16_t*)(base + lay.q_abs);
   float* part_ml = (float*)(base + lay.part_ml);
-  float* part_o = (float*)(base + lay.part_o);
+  uint16_t* part_o = (uint16_t*)(base + lay.part_o);
   const float sc_log2 = L.scale * 1.4426950408889634f;
   int4* plan_wg = (int4*)(base + lay.plan_wg);
   RopeThetas th;

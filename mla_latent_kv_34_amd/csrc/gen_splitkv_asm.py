@@ -230,11 +230,12 @@ def load_q_sync():
     """The 36 query fragments of a lane (bytes 32s .. 32s + 15 of its row
     segment) loaded into the same registers and waited for inside one block,
     so that no query load is ever in flight outside it (the wait also covers
-    older copies).  The fragments are in-out operands: they keep their
-    registers, and the address operand cannot share one of them."""
+    older copies).  The fragments are early-clobber outputs, so the address
+    operand cannot share a register with any of them, and the previous
+    query need not stay live up to the block."""
     lines = [f"global_load_dwordx4 %[q{s}], %[p], off offset:{32 * s}" for s in range(KSTEPS)]
     lines.append("s_waitcnt vmcnt(0)")
-    outs = ", ".join(f'[q{s}] "+v"(q[{s}])' for s in range(KSTEPS))
+    outs = ", ".join(f'[q{s}] "=&v"(q[{s}])' for s in range(KSTEPS))
     return f"""// q[s] = the 16 bytes at p + 32 s for s = 0..{KSTEPS - 1}, complete on return.
 __device__ __forceinline__ void load_q_sync(bf16x8 (&q)[{KSTEPS}], const uint16_t* p) {{
   asm volatile(
