@@ -129,6 +129,22 @@ mla_status mla_decode(const mla_dims* dims, const mla_paged_cache* cache, int32_
                       size_t workspace_bytes, int32_t n_workgroups, void* const* timing_events,
                       void* stream);
 
+/* One decode step: append the newest token of every sequence, then decode.
+ * Equivalent to mla_cache_append with start_pos[b] = seq_lens[b] - 1 and
+ * n_new = 1 (sequences with seq_lens[b] == 0 append nothing) followed by
+ * mla_decode with the same seq_lens, so each query attends its own token
+ * ("atyun.com MLA explainer" [KV cache]: a step writes the new token's entry
+ * and reuses the cached rest).  For the V2 sizes the append runs inside the
+ * first decode kernel, beside the query absorption, instead of as a launch
+ * of its own.
+ * c_kv_new: [batch, d_latent]   k_rope_new: [batch, d_rope] (pre-RoPE)
+ * Every other argument, the workspace size and the errors are as for
+ * mla_decode.                                                                */
+mla_status mla_decode_step(const mla_dims* dims, const mla_paged_cache* cache, int32_t batch,
+                           const int32_t* seq_lens, const void* c_kv_new, const void* k_rope_new,
+                           const void* q_nope, const void* q_rope, const void* w_uk,
+                           const void* w_uv, void* out, void* workspace, size_t workspace_bytes,
+                           int32_t n_workgroups, void* const* timing_events, void* stream);
 /* Bytes of device workspace mla_prefill needs. */
 size_t mla_prefill_workspace_size(const mla_dims* dims, int32_t batch, int32_t seq_len);
 

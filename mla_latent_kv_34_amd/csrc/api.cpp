@@ -209,6 +209,57 @@ mla_status mla_decode(const mla_dims* dims, const mla_paged_cache* cache, int32_
                   "decode launch");
 }
 
+mla_status mla_decode_step(const mla_dims* dims, const mla_paged_cache* cache, int32_t batch,
+                           const int32_t* seq_lens, const void* c_kv_new, const void* k_rope_new,
+                           const void* q_nope, const void* q_rope, const void* w_uk,
+                           const void* w_uv, void* out, void* workspace, size_t workspace_bytes,
+                           int32_t n_workgroups, void* const* timing_events, void* stream) {
+  mla::Layer L;
+  Family fam;
+  MLA_TRY(check_dims(dims, &L, &fam));
+  MLA_TRY(check_cache(cache));
+  if (batch < 1) return fail(MLA_ERR_INVALID_ARG, "batch must be >= 1");
+  if ((long long)batch * L.n_heads > 0x7fffffffLL) return fail(MLA_ERR_INVALID_ARG, "batch too large");
+  MLA_TRY(check_idx(seq_lens, "seq_lens"));
+  MLA_TRY(check_ptr(c_kv_new, "c_kv_new"));
+  MLA_TRY(check_ptr(k_rope_new, "k_rope_new"));
+  MLA_TRY(check_ptr(q_nope, "q_nope"));
+  MLA_TRY(check_ptr(q_rope, "q_rope"));
+  MLA_TRY(check_ptr(w_uk, "w_uk"));
+  MLA_TRY(check_ptr(w_uv, "w_uv"));
+  MLA_TRY(check_ptr(out, "out"));
+  if (n_workgroups < 0 || n_workgroups > 65536)
+    return fail(MLA_ERR_INVALID_ARG, "n_workgroups must be in [0, 65536]");
+  hipStream_t s = (hipStream_t)stream;
+  if (fam == Family::Generic) {
+    const size_t need = mla::generic_decode_workspace(L, batch);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+      return fail(MLA_ERR_WORKSPACE, "workspace smaller than mla_decode_workspace_size()");
+    g_err.clear();
+    // the new token at position seq_lens[b] - 1, then the decode
+    MLA_TRY(launched(mla::launch_append(L, cache->pool, cache->num_pages, cache->page_table,
+                                        cache->max_pages, batch, seq_lens, 1, c_kv_new, k_rope_new,
+                                        s, -1),
+                     "append launch"));
+    return launched(mla::launch_generic_decode(L, cache->pool, cache->num_pages, cache->page_table,
+                                               cache->max_pages, batch, seq_lens, q_nope, q_rope,
+                                               w_uk, w_uv, out, workspace, timing_events, s),
+                    "generic decode launch");
+  }
+  int wg = 0;
+  if (resolve_wg(n_workgroups, &wg) != 0) return fail(MLA_ERR_HIP, "cannot query the device");
+  const size_t need = mla::v2_decode_workspace(batch, wg);
+  if (!workspace || workspace_bytes < need)
+    return fail(MLA_ERR_WORKSPACE, "workspace smaller than mla_decode_workspace_size()");
+  MLA_TRY(check_ptr(workspace, "workspace"));
+  g_err.clear();
+  return launched(mla::launch_v2_decode(L, cache->pool, cache->num_pages, cache->page_table,
+                                        cache->max_pages, batch, seq_lens, q_nope, q_rope, w_uk,
+                                        w_uv, out, workspace, wg, timing_events, s, c_kv_new,
+                                        k_rope_new),
+                  "decode step launch");
+}
+
 size_t mla_prefill_workspace_size(const mla_dims* dims, int32_t batch, int32_t seq_len) {
   mla::Layer L;
   Family fam;

@@ -16,11 +16,11 @@ __global__ void __launch_bounds__(64)
 append_kernel(void* __restrict__ pool, int num_pages, const int32_t* __restrict__ table,
               int max_pages, const int32_t* __restrict__ start_pos, int n_new,
               const void* __restrict__ c_kv, const void* __restrict__ k_rope, int d_latent,
-              int d_rope, int page_size, double base, bool vec_ok) {
+              int d_rope, int page_size, double base, bool vec_ok, int pos_offset) {
   const long long tok = blockIdx.x;  // b * n_new + k
   const int b = (int)(tok / n_new);
   const int k = (int)(tok - (long long)b * n_new);
-  const long long pos = (start_pos ? (long long)start_pos[b] : 0LL) + k;
+  const long long pos = (start_pos ? (long long)start_pos[b] : 0LL) + pos_offset + k;
   if (pos < 0) return;
   const long long pidx = pos / page_size;
   if (pidx >= max_pages) return;
@@ -67,7 +67,7 @@ append_kernel(void* __restrict__ pool, int num_pages, const int32_t* __restrict_
 
 hipError_t launch_append(const Layer& L, void* pool, int num_pages, const int32_t* table,
                          int max_pages, int batch, const int32_t* start_pos, int n_new,
-                         const void* c_kv, const void* k_rope, hipStream_t s) {
+                         const void* c_kv, const void* k_rope, hipStream_t s, int pos_offset) {
   const long long blocks = (long long)batch * n_new;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   const int esz = L.bf16 ? 2 : 4;
@@ -76,11 +76,11 @@ hipError_t launch_append(const Layer& L, void* pool, int num_pages, const int32_
   if (L.bf16)
     hipLaunchKernelGGL(append_kernel<true>, dim3((unsigned)blocks), dim3(64), 0, s, pool,
                        num_pages, table, max_pages, start_pos, n_new, c_kv, k_rope, L.d_latent,
-                       L.d_rope, L.page_size, L.rope_base, vec_ok);
+                       L.d_rope, L.page_size, L.rope_base, vec_ok, pos_offset);
   else
     hipLaunchKernelGGL(append_kernel<false>, dim3((unsigned)blocks), dim3(64), 0, s, pool,
                        num_pages, table, max_pages, start_pos, n_new, c_kv, k_rope, L.d_latent,
-                       L.d_rope, L.page_size, L.rope_base, vec_ok);
+                       L.d_rope, L.page_size, L.rope_base, vec_ok, pos_offset);
   return hipGetLastError();
 }
 

@@ -210,7 +210,9 @@ __global__ void __launch_bounds__(256)
 q_absorb_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_rope,
                 const uint16_t* __restrict__ w_uk, const int32_t* __restrict__ seq_lens, int B,
                 RopeThetas rope, uint16_t* __restrict__ q_abs, int W, int32_t* __restrict__ plan,
-                int4* __restrict__ plan_wg) {
+                int4* __restrict__ plan_wg, uint16_t* __restrict__ pool, int num_pages,
+                const int32_t* __restrict__ table, int max_pages, const uint16_t* __restrict__ c_new,
+                const uint16_t* __restrict__ k_new, double rope_base) {
   // workgroup 0 builds the split plan; it is dispatched first, so it runs
   // beside the absorption workgroups instead of after them
   // W^UK_h[:, c0:c0+128] as two [128 rows r][64 cols] halves, swizzled
@@ -218,6 +220,31 @@ q_absorb_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __restrict_
   static_assert(2 * DC * 128 >= 2 * PLAN_CACHE * 4, "plan cache must fit the tile buffer");
   if (blockIdx.x == 0) {
     plan_block(seq_lens, B, W, plan, plan_wg, (int32_t*)wl);
+    return;
+  }
+  if (blockIdx.x > 4 * H) {
+    // the new token of sequence b (position seq_lens[b] - 1) into its cache
+    // slot, exactly as the cache append writes it: c^KV verbatim, k^R rotated
+    // in fp64 and rounded to bf16; 64 threads per sequence
+    const int b = 4 * ((int)blockIdx.x - 1 - 4 * H) + ((int)threadIdx.x >> 6);
+    const int t = threadIdx.x & 63;
+    if (b >= B) return;
+    const long long pos = (long long)seq_lens[b] - 1;
+    if (pos < 0) return;
+    const long long pidx = pos / PS;
+    if (pidx >= max_pages) return;
+    const int page = table[(size_t)b * max_pages + pidx];
+    if (page < 0 || page >= num_pages) return;
+    uint16_t* P = pool + ((size_t)page * PS + (size_t)(pos - pidx * PS)) * ROW;
+    ((uint4*)P)[t] = ((const uint4*)(c_new + (size_t)b * DL))[t];  // 64 x 16 bytes = d_c
+    if (t < DR / 2) {
+      const uint16_t* K = k_new + (size_t)b * DR;
+      double ra, rb;
+      rope_pair_f64((double)bf16_bits_to_f32(K[2 * t]), (double)bf16_bits_to_f32(K[2 * t + 1]),
+                    (double)pos, t, DR, rope_base, &ra, &rb);
+      P[DL + 2 * t] = bf16_bits_rne_f64(ra);
+      P[DL + 2 * t + 1] = bf16_bits_rne_f64(rb);
+    }
     return;
   }
   const int h = (blockIdx.x - 1) >> 2, chunk = (blockIdx.x - 1) & 3;
@@ -235,57 +262,74 @@ q_absorb_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __restrict_
 #pragma unroll
     for (int s = 0; s < DC / 16; ++s) dst[s] = *(const bf16x8*)(qp + 16 * s);
   };
+  // All loads first, in the order of first use (a wait for a load waits for
+  // every older one): the rotated-query inputs, the first item's queries,
+  // the W^UK tile.
+  constexpr int PER = DR / 2;
+  const int i0_first = chunk * 256 + tid;
+  uint32_t pair[2];
+  int len[2];
+  double th[2];
+  auto rope_loads = [&](int i0) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int i = min(i0 + r * 4 * 256, B * PER - 1);
+      const int b = i / PER, k = i % PER;
+      pair[r] = *(const uint32_t*)(q_rope + ((size_t)b * H + h) * DR + 2 * k);
+      len[r] = seq_lens[b];
+      th[r] = rope.theta[k];
+    }
+  };
+  rope_loads(i0_first);
   if (wave < 4 * nblk) load_q(wave, bq);
-  // stage the W^UK tile (128 rows x 16 chunks of 16 bytes): all eight loads
-  // of a thread are issued before the first LDS store
+  // W^UK_h[:, c0:c0+128] straight into LDS as two [128 rows r][64 cols]
+  // halves with 16-byte chunk c of row r at chunk c ^ swz_w(r): 16-byte unit
+  // U = (4m + wave) * 64 + lane of the tile is written by load m of the wave
   {
-    uint4 wv[8];
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int i = tid + 256 * k, r = i >> 4, ch = i & 15;
-      wv[k] = *(const uint4*)(w_uk + ((size_t)(h * DC + r) * DL + c0 + ch * 8));
-    }
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int i = tid + 256 * k, r = i >> 4, ch = i & 15;
-      *(uint4*)(wl + (ch >> 3) * (DC * 128) + r * 128 + (((ch & 7) ^ swz_w(r)) << 4)) = wv[k];
-    }
-  }
-  {  // rotated query RoPE part: the 4 column-chunk workgroups of the head
-     // share it.  The angle pos * theta_k is formed and reduced to [-pi, pi]
-     // in fp64 (two-part 2 pi), then rotated in fp32: the result is rounded
-     // to bf16, far coarser than the fp32 error.
-    constexpr int PER = DR / 2;
-    for (int i0 = chunk * 256 + tid; i0 < B * PER; i0 += 2 * 4 * 256) {
-      uint32_t pair[2];
-      int len[2];
-#pragma unroll
-      for (int r = 0; r < 2; ++r) {  // both pairs' loads before any arithmetic
-        const int i = min(i0 + r * 4 * 256, B * PER - 1);
-        const int b = i / PER, k = i % PER;
-        pair[r] = *(const uint32_t*)(q_rope + ((size_t)b * H + h) * DR + 2 * k);
-        len[r] = seq_lens[b];
-      }
-#pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const int i = i0 + r * 4 * 256;
-        if (i >= B * PER) break;
-        const int b = i / PER, k = i % PER;
-        const double pos = len[r] > 0 ? (double)(len[r] - 1) : 0.0;
-        const double ang = pos * rope.theta[k];
-        const double nq = __builtin_rint(ang * 0.15915494309189535);  // 1 / (2 pi)
-        const double red = __builtin_fma(-nq, 2.4492935982947064e-16,
-                                         __builtin_fma(-nq, 6.283185307179586, ang));
-        float sn, cs;
-        sincosf((float)red, &sn, &cs);
-        const float a = bf16_bits_to_f32((uint16_t)(pair[r] & 0xffff));
-        const float bb = bf16_bits_to_f32((uint16_t)(pair[r] >> 16));
-        const float ra = a * cs - bb * sn, rb = a * sn + bb * cs;
-        *(uint32_t*)(q_abs + ((size_t)b * H + h) * ROW + DL + 2 * k) =
-            (uint32_t)bf16_bits_rne_f32(ra) | ((uint32_t)bf16_bits_rne_f32(rb) << 16);
-      }
+    for (int m = 0; m < 8; ++m) {
+      const int U = (4 * m + wv) * 64 + lane;
+      const int half = U >> 10, r = (U >> 3) & (DC - 1), cs = U & 7;
+      const int ch = ((cs ^ swz_w(r)) | (half << 3));
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(w_uk + ((size_t)(h * DC + r) * DL + c0 + ch * 8)),
+          (__attribute__((address_space(3))) void*)(wl + (4 * m + wv) * 1024), 16, 0, 0);
     }
   }
+  // Rotated query RoPE part: the 4 column-chunk workgroups of the head share
+  // it.  The angle pos * theta_k is formed and reduced to [-pi, pi] in fp64
+  // (two-part 2 pi), then rotated in fp32: the result is rounded to bf16, far
+  // coarser than the fp32 error.
+  auto rope_round = [&](int i0) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int i = i0 + r * 4 * 256;
+      if (i >= B * PER) break;
+      const int b = i / PER, k = i % PER;
+      const double pos = len[r] > 0 ? (double)(len[r] - 1) : 0.0;
+      const double ang = pos * th[r];
+      const double nq = __builtin_rint(ang * 0.15915494309189535);  // 1 / (2 pi)
+      const double red = __builtin_fma(-nq, 2.4492935982947064e-16,
+                                       __builtin_fma(-nq, 6.283185307179586, ang));
+      float sn, cs;
+      sincosf((float)red, &sn, &cs);
+      const float a = bf16_bits_to_f32((uint16_t)(pair[r] & 0xffff));
+      const float bb = bf16_bits_to_f32((uint16_t)(pair[r] >> 16));
+      const float ra = a * cs - bb * sn, rb = a * sn + bb * cs;
+      *(uint32_t*)(q_abs + ((size_t)b * H + h) * ROW + DL + 2 * k) =
+          (uint32_t)bf16_bits_rne_f32(ra) | ((uint32_t)bf16_bits_rne_f32(rb) << 16);
+    }
+  };
+  // the first round outside the loop, so that its wait covers only its own
+  // loads and not the tile copies behind them
+  rope_round(i0_first);
+  for (int i0 = i0_first + 2 * 4 * 256; i0 < B * PER; i0 += 2 * 4 * 256) {
+    rope_loads(i0);
+    rope_round(i0);
+  }
+  // the tile copies (the oldest loads of this thread) are complete
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
   __syncthreads();
   const int G = lane >> 4, s16 = lane & 15;
   // transpose-read geometry: source row r = 16s + 8*(G/2) + s16/4 (+4), column
@@ -854,7 +898,8 @@ size_t v2_decode_workspace(int batch, int n_wg) { return v2::WsLayout(batch, n_w
 hipError_t launch_v2_decode(const Layer& L, const void* pool, int num_pages, const int32_t* table,
                             int max_pages, int batch, const int32_t* seq_lens, const void* q_nope,
                             const void* q_rope, const void* w_uk, const void* w_uv, void* out,
-                            void* ws, int n_wg, void* const* ev, hipStream_t s) {
+                            void* ws, int n_wg, void* const* ev, hipStream_t s, const void* c_new,
+                            const void* k_new) {
   using namespace v2;
   const WsLayout lay(batch, n_wg);
   char* base = (char*)ws;
@@ -866,9 +911,13 @@ hipError_t launch_v2_decode(const Layer& L, const void* pool, int num_pages, con
   int4* plan_wg = (int4*)(base + lay.plan_wg);
   RopeThetas th;
   for (int k = 0; k < DR / 2; ++k) th.theta[k] = std::pow(L.rope_base, -2.0 * k / DR);
-  hipLaunchKernelGGL(q_absorb_kernel, dim3(H * 4 + 1), dim3(256), 0, s, (const uint16_t*)q_nope,
-                     (const uint16_t*)q_rope, (const uint16_t*)w_uk, seq_lens, batch, th, q_abs,
-                     n_wg, plan, plan_wg);
+  // block 0: split plan; blocks 1 .. 4H: absorption; then (with a new token
+  // to append) one block per 4 sequences
+  const unsigned app_blocks = c_new ? (unsigned)((batch + 3) / 4) : 0u;
+  hipLaunchKernelGGL(q_absorb_kernel, dim3(H * 4 + 1 + app_blocks), dim3(256), 0, s,
+                     (const uint16_t*)q_nope, (const uint16_t*)q_rope, (const uint16_t*)w_uk,
+                     seq_lens, batch, th, q_abs, n_wg, plan, plan_wg, (uint16_t*)pool, num_pages,
+                     table, max_pages, (const uint16_t*)c_new, (const uint16_t*)k_new, L.rope_base);
   hipError_t e = mark(ev, 0, s);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_splitkv_kernel, dim3(n_wg), dim3(256), 0, s, (const char*)pool,

@@ -82,10 +82,13 @@ struct Layer {
   }
 };
 
-// start_pos == nullptr means position 0 for every sequence.
+// start_pos == nullptr means position 0 for every sequence; token k of
+// sequence b goes to position start_pos[b] + pos_offset + k (pos_offset -1
+// with seq_lens as start_pos writes the last cached token of a decode step).
 hipError_t launch_append(const Layer& L, void* pool, int num_pages, const int32_t* table,
                          int max_pages, int batch, const int32_t* start_pos, int n_new,
-                         const void* c_kv, const void* k_rope, hipStream_t s);
+                         const void* c_kv, const void* k_rope, hipStream_t s, int pos_offset = 0);
+
 
 // generic fp32-arithmetic family
 size_t generic_decode_workspace(const Layer& L, int batch);
@@ -103,10 +106,14 @@ hipError_t launch_generic_prefill(const Layer& L, const void* pool, int num_page
 
 // MFMA family for the V2 sizes
 size_t v2_decode_workspace(int batch, int n_wg);
+// c_new / k_new: NULL, or the token at position seq_lens[b] - 1 of every
+// sequence ([batch, d_latent], [batch, d_rope]), appended to the cache by the
+// first kernel of the decode (before any cache read).
 hipError_t launch_v2_decode(const Layer& L, const void* pool, int num_pages, const int32_t* table,
                             int max_pages, int batch, const int32_t* seq_lens, const void* q_nope,
                             const void* q_rope, const void* w_uk, const void* w_uv, void* out,
-                            void* ws, int n_wg, void* const* ev, hipStream_t s);
+                            void* ws, int n_wg, void* const* ev, hipStream_t s,
+                            const void* c_new = nullptr, const void* k_new = nullptr);
 size_t v2_prefill_workspace(int batch, int seq_len);
 hipError_t launch_v2_prefill(const Layer& L, const void* pool, int num_pages, const int32_t* table,
                              int max_pages, int batch, int seq_len, const void* q_nope,

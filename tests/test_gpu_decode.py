@@ -180,3 +180,54 @@ def test_v2_many_short_sequences(batch, hi, n_wg):
     rng = np.random.default_rng(batch + n_wg)
     for b in list(rng.choice(batch, size=6, replace=False)) + [0, batch - 1]:
         assert_close(f64(out[b]), _oracle(case, b), f"seq {b} len {case.attended[b]}")
+
+
+def _step_inputs(case):
+    """The step's new token rows [batch, d_c] and [batch, d_h^R] (position cached[b])."""
+    c_new = torch.stack([case.seq_rows(b)[0][-1] for b in range(case.batch)]).to(DEV)
+    k_new = torch.stack([case.seq_rows(b)[1][-1] for b in range(case.batch)]).to(DEV)
+    return c_new.contiguous(), k_new.contiguous()
+
+
+def _step_vs_separate(case):
+    """mla_decode_step on a cache holding the cached tokens, against
+    mla_cache_append + mla_decode on a second copy: identical cache bytes and
+    identical outputs, and both against the oracle."""
+    from gpu_common import canary_pool, fill_cache, lib_dims
+    import mla_latent_kv_34_amd as mla
+    assert case.append
+    dims = lib_dims(case.dims)
+    table = torch.from_numpy(case.table).to(DEV)
+    pool_a = canary_pool(case.dims, case.num_pages)
+    fill_cache(case, dims, pool_a, table)
+    pool_b = pool_a.clone()
+    seq_lens = torch.tensor(case.attended, dtype=torch.int32, device=DEV)
+    c_new, k_new = _step_inputs(case)
+    args = (case.q_c.to(DEV), case.q_r.to(DEV), case.w_uk.to(DEV), case.w_uv.to(DEV))
+    out_step = mla.decode_step(dims, pool_a, table, seq_lens, c_new, k_new, *args)
+    start = (seq_lens - 1).clamp(min=0)
+    mla.cache_append(dims, pool_b, table, start, c_new.unsqueeze(1), k_new.unsqueeze(1))
+    out_sep = mla.decode(dims, pool_b, table, seq_lens, *args)
+    torch.cuda.synchronize()
+    bits_a, bits_b = pool_bits(pool_a), pool_bits(pool_b)
+    assert _same_bits(bits_a, bits_b), "decode_step cache differs from append + decode"
+    assert _same_bits(bits_a, _expected_pool(case, tuple(pool_a.shape))), "cache vs oracle"
+    assert torch.equal(out_step.view(torch.int16) if out_step.dtype == torch.bfloat16 else out_step,
+                       out_sep.view(torch.int16) if out_sep.dtype == torch.bfloat16 else out_sep)
+    for b in range(case.batch):
+        assert_close(f64(out_step[b]), _oracle(case, b), f"step seq {b} (len {case.attended[b]})")
+
+
+def test_decode_step_tiny_fp32():
+    """Fused step on the tiny fp32 layer (append launch + generic decode)."""
+    print("case decode_step tiny", flush=True)
+    _step_vs_separate(syn.config_case("tiny_decode"))
+
+
+@pytest.mark.parametrize("lens", [[1, 63, 64, 65, 300], [0, 700, 5]])
+def test_decode_step_v2(lens):
+    """Fused step for the V2 sizes: the append inside the first decode kernel
+    writes the same bytes as mla_cache_append (also for a sequence with no
+    cached token, which then attends only its new token)."""
+    print(f"case decode_step v2 {lens}", flush=True)
+    _step_vs_separate(syn.decode_case(syn.V2, lens, append=True, seed=11, shuffle=True))
