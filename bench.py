@@ -34,8 +34,18 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 BYTES_PER_TOKEN = 1152          # one cached row: 576 bf16
 FLOP_PER_TOKEN = 278528         # 2*128*576 (scores) + 2*128*512 (latent sum)
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_splitkv_traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "mla_latent_kv_34_amd", "csrc", "decode_v2.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_splitkv_v2_b64_ragged_traffic.json")
+KERNEL_SRCS = [os.path.join(ROOT, "mla_latent_kv_34_amd", "csrc", f)
+               for f in ("decode_v2.hip", "splitkv_asm.h")]
+
+
+def kernel_source_sha256() -> str:
+    """Hash of the sources of the split-KV kernel (the traffic figures in
+    TRAFFIC_FILE are only valid for the kernel they were counted on)."""
+    h = hashlib.sha256()
+    for f in KERNEL_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
 
 
 def parse():
@@ -52,6 +62,10 @@ def parse():
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device copy of this many bytes (HBM counter calibration)")
+    ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="only write the traffic file from four rocprofv3 --pmc output folders "
+                         "(FETCH_SIZE and WRITE_SIZE of this bench, then of --copy-bytes)")
+    ap.add_argument("--traffic-command", default="", help="the profiling commands, recorded in the file")
     return ap.parse_args()
 
 
@@ -67,10 +81,51 @@ def copy_calibration(nbytes: int, reps: int = 3):
     print(json.dumps({"copy_bytes": src.numel() * 4, "reps": reps}), flush=True)
 
 
+def _pmc_rows(folder: str, counter: str):
+    import csv
+    path = os.path.join(folder, "run_counter_collection.csv")
+    return [(r["Kernel_Name"], float(r["Counter_Value"])) for r in csv.DictReader(open(path))
+            if r["Counter_Name"] == counter]
+
+
+def write_traffic(args):
+    """Per-launch HBM traffic of decode_splitkv from FETCH_SIZE / WRITE_SIZE
+    (KiB per dispatch), each scaled by what the same counter reads for a plain
+    copy of known size (copy bytes / counted bytes of the largest dispatch)."""
+    fetch_dir, write_dir, cfetch_dir, cwrite_dir = args.traffic_from
+    copy_bytes = 1 << 30
+
+    def per_launch(folder, counter):
+        v = [x for k, x in _pmc_rows(folder, counter) if "decode_splitkv" in k]
+        return sum(v) / len(v), len(v)
+
+    def copy_factor(folder, counter):
+        counted = max(x for _, x in _pmc_rows(folder, counter)) * 1024.0
+        return copy_bytes / counted
+
+    f_kib, nf = per_launch(fetch_dir, "FETCH_SIZE")
+    w_kib, nw = per_launch(write_dir, "WRITE_SIZE")
+    ff, fw = copy_factor(cfetch_dir, "FETCH_SIZE"), copy_factor(cwrite_dir, "WRITE_SIZE")
+    rec = {
+        "kernel": "decode_splitkv", "workload": "v2_b64_ragged",
+        "fetch_kib_per_dispatch": f_kib, "write_kib_per_dispatch": w_kib, "dispatches": [nf, nw],
+        "copy_bytes": copy_bytes, "fetch_scale": ff, "write_scale": fw,
+        "bytes_per_launch": f_kib * 1024.0 * ff + w_kib * 1024.0 * fw,
+        "kernel_source_sha256": kernel_source_sha256(), "command": args.traffic_command,
+    }
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_bytes:
         copy_calibration(args.copy_bytes)
+        return
+    if args.traffic_from:
+        write_traffic(args)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -190,8 +245,8 @@ def main():
     if os.path.exists(TRAFFIC_FILE):
         try:
             tf = json.load(open(TRAFFIC_FILE))
-            src_sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
-            if tf.get("kernel_source_sha256") == src_sha and tf.get("workload") == "v2_b64_ragged":
+            if (tf.get("kernel_source_sha256") == kernel_source_sha256()
+                    and tf.get("workload") == "v2_b64_ragged"):
                 traffic = tf.get("bytes_per_launch")
         except Exception:
             traffic = None
