@@ -54,6 +54,16 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 // reads (4 consecutive rows, 4 chunks each) is conflict-free because rows t
 // and t + 2 of every aligned quad differ in bit 2 of swz.
 __device__ __forceinline__ int swz(int t) { return (((t >> 1) & 1) << 2) | ((t >> 2) & 3); }
+// Absorbed queries are stored fragment-major, in the order the split-KV waves
+// load them: element d of head h of sequence b sits at
+//   ((((b * 4 + h / 32) * 36 + d / 16) * 64 + 32 * ((d / 8) & 1) + h % 32) * 8 + d % 8,
+// so fragment s of wave v (16 bytes per lane: dims 16s + 8g .. +7 of head
+// 32v + n for lane 32g + n) is one contiguous KiB.
+__device__ __forceinline__ size_t qfrag_index(int b, int h, int d) {
+  return ((((size_t)b * 4 + (h >> 5)) * KSTEPS + (d >> 4)) * 64 + 32 * ((d >> 3) & 1) + (h & 31)) * 8 +
+         (d & 7);
+}
+
 // Swizzle of the 128-byte-row weight tile of q_absorb.
 __device__ __forceinline__ int swz_w(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
 
@@ -317,7 +327,7 @@ q_absorb_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __restrict_
       const float a = bf16_bits_to_f32((uint16_t)(pair[r] & 0xffff));
       const float bb = bf16_bits_to_f32((uint16_t)(pair[r] >> 16));
       const float ra = a * cs - bb * sn, rb = a * sn + bb * cs;
-      *(uint32_t*)(q_abs + ((size_t)b * H + h) * ROW + DL + 2 * k) =
+      *(uint32_t*)(q_abs + qfrag_index(b, h, DL + 2 * k)) =
           (uint32_t)bf16_bits_rne_f32(ra) | ((uint32_t)bf16_bits_rne_f32(rb) << 16);
     }
   };
@@ -359,16 +369,15 @@ q_absorb_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __restrict_
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[s], acc, 0, 0, 0);
     }
     if (b < B) {
-      uint16_t* dst = q_abs + ((size_t)b * H + h) * ROW + c0 + mc * 32;
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const int c = 8 * q4 + 4 * g;
+        const int c = c0 + mc * 32 + 8 * q4 + 4 * g;  // 4 dims inside one 8-dim group
         ushort4 v;
         v.x = bf16_bits_rne_f32(acc[4 * q4 + 0]);
         v.y = bf16_bits_rne_f32(acc[4 * q4 + 1]);
         v.z = bf16_bits_rne_f32(acc[4 * q4 + 2]);
         v.w = bf16_bits_rne_f32(acc[4 * q4 + 3]);
-        *(ushort4*)(dst + c) = v;
+        *(ushort4*)(q_abs + qfrag_index(b, h, c)) = v;
       }
     }
 #pragma unroll
@@ -593,7 +602,8 @@ decode_splitkv_kernel(const char* __restrict__ pool, int num_pages, const int32_
   };
   // query fragments (B operand of S^T = K Q^T): 8 consecutive dims per lane
   bf16x8 qreg[KSTEPS];
-  auto qptr = [&](int b) { return q_abs + ((size_t)b * H + head) * ROW + 8 * g; };
+  // fragment s of this lane: qptr(b) + 512 s (one KiB per fragment and wave)
+  auto qptr = [&](int b) { return q_abs + (((size_t)b * 4 + wave) * KSTEPS * 64 + lane) * 8; };
 
   // ---- prologue: the queries, then three sub-tiles in flight.  The copy
   // count after the query loads is fixed (issue_or_repeat), so the compiler's
@@ -601,7 +611,7 @@ decode_splitkv_kernel(const char* __restrict__ pool, int num_pages, const int32_
   {
     const uint16_t* qp = qptr(cc.b);
 #pragma unroll
-    for (int s2 = 0; s2 < KSTEPS; ++s2) qreg[s2] = *(const bf16x8*)(qp + 16 * s2);
+    for (int s2 = 0; s2 < KSTEPS; ++s2) qreg[s2] = *(const bf16x8*)(qp + 512 * s2);
   }
   issue_or_repeat();
   issue_or_repeat();

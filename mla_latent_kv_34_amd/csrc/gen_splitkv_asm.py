@@ -227,21 +227,27 @@ __device__ __forceinline__ void pv_full(f32x16 (&acc)[16], const bf16x8& p0, con
 
 
 def load_q_sync():
-    """The 36 query fragments of a lane (bytes 32s .. 32s + 15 of its row
-    segment) loaded into the same registers and waited for inside one block,
-    so that no query load is ever in flight outside it (the wait also covers
-    older copies).  The fragments are early-clobber outputs, so the address
-    operand cannot share a register with any of them, and the previous
-    query need not stay live up to the block."""
-    lines = [f"global_load_dwordx4 %[q{s}], %[p], off offset:{32 * s}" for s in range(KSTEPS)]
+    """The 36 query fragments of a lane (16 bytes each, consecutive fragments
+    one KiB apart) loaded into fresh registers and waited for inside one
+    block, so that no query load is ever in flight outside it (the wait also
+    covers older copies).  The address advances 4 KiB after every fourth load
+    (immediate offsets stay below 4 KiB).  The fragments are early-clobber
+    outputs, so the address operand cannot share a register with any of them,
+    and the previous query need not stay live up to the block."""
+    lines = []
+    for s in range(KSTEPS):
+        if s and s % 4 == 0:
+            lines.append("v_lshl_add_u64 %[p], %[p], 0, %[step]")
+        lines.append(f"global_load_dwordx4 %[q{s}], %[p], off offset:{1024 * (s % 4)}")
     lines.append("s_waitcnt vmcnt(0)")
-    outs = ", ".join(f'[q{s}] "=&v"(q[{s}])' for s in range(KSTEPS))
-    return f"""// q[s] = the 16 bytes at p + 32 s for s = 0..{KSTEPS - 1}, complete on return.
+    outs = ", ".join([f'[q{s}] "=&v"(q[{s}])' for s in range(KSTEPS)] + ['[p] "+&v"(p)'])
+    return f"""// q[s] = the 16 bytes at p + 1024 s for s = 0..{KSTEPS - 1}, complete on return.
 __device__ __forceinline__ void load_q_sync(bf16x8 (&q)[{KSTEPS}], const uint16_t* p) {{
+  const unsigned long long step = 4096;
   asm volatile(
 {_emit(lines)}
       : {outs}
-      : [p] "v"(p)
+      : [step] "s"(step)
       : "memory");
 }}
 """
