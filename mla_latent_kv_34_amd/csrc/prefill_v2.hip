@@ -18,6 +18,8 @@
 //   V^T   [b][h][128][Tp] bf16, keys in the same order within 16-key groups,
 //         so one 16-byte LDS read gives a lane the 8 keys its probabilities
 //         cover; rows past T hold zeros.
+#include <type_traits>
+
 #include "mla_internal.h"
 
 namespace mla {
@@ -50,6 +52,14 @@ __device__ __forceinline__ void wait_vmcnt0() {
 }
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// An accumulator element read into a VGPR (the explicit read keeps the
+// accumulators in AGPRs, which the MFMAs write).
+__device__ __forceinline__ float agpr_read(float a) {
+  float v;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+  return v;
+}
+
 // Launched workgroup ib runs on XCD ib % 8; give every XCD a contiguous range
 // of logical indices so neighbouring work shares that XCD's L2.
 __device__ __forceinline__ int logical_of_launched(int ib, int n) {
@@ -78,20 +88,24 @@ __global__ void rope_table_kernel(int T, double base, float2* __restrict__ tab) 
 }
 
 // ---------------------------------------------------------------------------
-// expand: one workgroup per (head h, 128-token tile of prompt b).  Waves 0-1
-// compute K^C for tokens 0-63 / 64-127 of the tile as K^T = W^UK_h C^T (rows =
-// key dims, so a lane ends with 8 key dims of one token in k-slot order);
-// waves 2-3 compute V = C W^UV_h^T (rows = tokens, so a lane ends with 8
-// tokens of one value dim).  The latent dimension runs in 8 stages of 64
-// columns, double-buffered in LDS with direct-to-LDS loads: C rows of the
-// tile [128][64] then W^UK_h and W^UV_h rows [256][64], 128 bytes per row.
+// expand: one workgroup of 8 waves (two per SIMD) per (head h, 256-token tile
+// of prompt b).  Waves 0-3 compute K^C for tokens 64w..64w+63 of the tile as
+// K^T = W^UK_h C^T (rows = key dims, so a lane ends with 8 key dims of one
+// token in k-slot order); waves 4-7 compute V = C W^UV_h^T for the same token
+// blocks (rows = tokens, so a lane ends with 8 tokens of one value dim).  The
+// latent dimension runs in 8 stages of 64 columns, double-buffered in LDS with
+// direct-to-LDS loads: C rows of the tile [256][64] then W^UK_h and W^UV_h
+// rows [256][64], 128 bytes per row.  Two waves per SIMD keep the MFMA pipe
+// fed while the other waits for its stage.
 // ---------------------------------------------------------------------------
-constexpr int EX_TOK = 128;
-constexpr int EX_CB = EX_TOK * 128;       // 16384 bytes of C per stage
+constexpr int EX_TOK = 256;
+constexpr int EX_NW = 8;                   // waves per workgroup
+constexpr int EX_CB = EX_TOK * 128;        // 32768 bytes of C per stage
 constexpr int EX_STAGEB = EX_CB + 256 * 128;  // + 32768 bytes of W
-constexpr int EX_DMA = EX_STAGEB / 1024 / 4;  // 12 one-KiB loads per wave per stage
+constexpr int EX_DMA = EX_STAGEB / 1024 / EX_NW;  // 8 one-KiB loads per wave per stage
+constexpr int EX_CU = EX_CB / 16;          // 16-byte units of C per stage
 
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(64 * EX_NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 expand_kernel(const uint16_t* __restrict__ c_kv, const uint16_t* __restrict__ w_uk,
               const uint16_t* __restrict__ w_uv, int B, int T, int tp, int nt,
               uint16_t* __restrict__ kc, uint16_t* __restrict__ vt) {
@@ -102,18 +116,18 @@ expand_kernel(const uint16_t* __restrict__ c_kv, const uint16_t* __restrict__ w_
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int g = lane >> 5, n = lane & 31;
 
-  // direct-to-LDS plan: load m of wave w fills LDS unit u = (4m + w) * 64 +
-  // lane (16 bytes each); units 0..1023 are C rows, 1024..3071 W rows
+  // direct-to-LDS plan: load m of wave w fills LDS unit u = (8m + w) * 64 +
+  // lane (16 bytes each); units 0..2047 are C rows, 2048..4095 W rows
   const char* src[EX_DMA];
 #pragma unroll
   for (int m = 0; m < EX_DMA; ++m) {
-    const int u = (4 * m + wave) * 64 + lane;
-    if (m < 4) {
+    const int u = (EX_NW * m + wave) * 64 + lane;
+    if (m < EX_CU / (64 * EX_NW)) {
       const int r = u >> 3, c = (u & 7) ^ swz8(u >> 3);
       const int t = min(t0 + r, T - 1);
       src[m] = (const char*)(c_kv + ((size_t)b * T + t) * DL) + 16 * c;
     } else {
-      const int v = u - 1024, r = v >> 3, c = (v & 7) ^ swz8(v >> 3);
+      const int v = u - EX_CU, r = v >> 3, c = (v & 7) ^ swz8(v >> 3);
       const uint16_t* w = r < DC ? w_uk + ((size_t)h * DC + r) * DL
                                  : w_uv + ((size_t)h * DC + r - DC) * DL;
       src[m] = (const char*)w + 16 * c;
@@ -122,66 +136,75 @@ expand_kernel(const uint16_t* __restrict__ c_kv, const uint16_t* __restrict__ w_
   auto issue = [&](int stage) {
     char* buf = lds + (stage & 1) * EX_STAGEB;
 #pragma unroll
-    for (int m = 0; m < EX_DMA; ++m) dma16(src[m] + stage * 128, buf + (4 * m + wave) * 1024);
+    for (int m = 0; m < EX_DMA; ++m) dma16(src[m] + stage * 128, buf + (EX_NW * m + wave) * 1024);
   };
 
-  const bool vhalf = wave >= 2;
-  const int tb = 64 * (wave & 1);  // first token of this wave inside the tile
+  const bool vhalf = wave >= 4;
+  const int tb = 64 * (wave & 3);  // first token of this wave inside the tile
   const int x = swz8(n);
   const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)lds);
-  uint32_t cof[4], wof[4];
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    cof[ks] = (uint32_t)((tb + n) * 128 + 16 * ((2 * ks + g) ^ x));
-    wof[ks] = (uint32_t)(EX_CB + (128 * (vhalf ? 1 : 0) + n) * 128 + 16 * ((2 * ks + g) ^ x));
-  }
-  f32x16 acc[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) acc[k] = (f32x16){};
+  const size_t bh = (size_t)b * H + h;
 
-  issue(0);
-  for (int st = 0; st < DL / 64; ++st) {
-    wait_vmcnt0();
-    raw_barrier();  // stage st is in LDS; every wave is done with stage st - 1
-    if (st + 1 < DL / 64) issue(st + 1);
-    const uint32_t base = lds0 + (uint32_t)(st & 1) * EX_STAGEB;
-    uint32_t ca[4], wa[4];
+  // The K and V waves run separate copies of the loop (the branch is uniform
+  // per wave), so each copy keeps its 128 accumulators in fixed AGPRs.
+  auto run = [&](auto vh) {
+    constexpr bool V = decltype(vh)::value;
+    uint32_t cof[4], wof[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      ca[ks] = base + cof[ks];
-      wa[ks] = base + wof[ks];
+      cof[ks] = (uint32_t)((tb + n) * 128 + 16 * ((2 * ks + g) ^ x));
+      wof[ks] = (uint32_t)(EX_CB + (128 * (V ? 1 : 0) + n) * 128 + 16 * ((2 * ks + g) ^ x));
     }
-    if (vhalf) expand_stage_v(acc, ca, wa);
-    else expand_stage_k(acc, ca, wa);
-  }
+    f32x16 acc[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] = (f32x16){};
 
-  const size_t bh = (size_t)b * H + h;
+    issue(0);
+    for (int st = 0; st < DL / 64; ++st) {
+      wait_vmcnt0();
+      raw_barrier();  // stage st is in LDS; every wave is done with stage st - 1
+      if (st + 1 < DL / 64) issue(st + 1);
+      const uint32_t base = lds0 + (uint32_t)(st & 1) * EX_STAGEB;
+      uint32_t ca[4], wa[4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        bf16x8 v;
-        if (!vhalf) {
-          // token t0 + tb + 32i + n; key dims 32j + 16hh + (k-slot order) 8g..8g+7
-          const int t = t0 + tb + 32 * i + n;
-          if (t >= tp) continue;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = t < T ? (__bf16)acc[4 * i + j][8 * hh + e] : (__bf16)0.f;
-          *(bf16x8*)(kc + (bh * tp + t) * DC + 32 * j + 16 * hh + 8 * g) = v;
-        } else {
-          // value dim 32j + n; stored key positions p0 .. p0+7 of the tile
-          const int p0 = t0 + tb + 32 * i + 16 * hh + 8 * g;
-          if (p0 >= tp) continue;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int t = t0 + tb + 32 * i + 16 * hh + 8 * (e >> 2) + 4 * g + (e & 3);
-            v[e] = t < T ? (__bf16)acc[4 * i + j][8 * hh + e] : (__bf16)0.f;
-          }
-          *(bf16x8*)(vt + (bh * DC + 32 * j + n) * tp + p0) = v;
-        }
+      for (int ks = 0; ks < 4; ++ks) {
+        ca[ks] = base + cof[ks];
+        wa[ks] = base + wof[ks];
       }
+      if constexpr (V) expand_stage_v(acc, ca, wa);
+      else expand_stage_k(acc, ca, wa);
+    }
+
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          bf16x8 v;
+          if constexpr (!V) {
+            // token t0 + tb + 32i + n; key dims 32j + 16hh + (k-slot order) 8g..8g+7
+            const int t = t0 + tb + 32 * i + n;
+            if (t >= tp) continue;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              v[e] = t < T ? (__bf16)agpr_read(acc[4 * i + j][8 * hh + e]) : (__bf16)0.f;
+            *(bf16x8*)(kc + (bh * tp + t) * DC + 32 * j + 16 * hh + 8 * g) = v;
+          } else {
+            // value dim 32j + n; stored key positions p0 .. p0+7 of the tile
+            const int p0 = t0 + tb + 32 * i + 16 * hh + 8 * g;
+            if (p0 >= tp) continue;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int t = t0 + tb + 32 * i + 16 * hh + 8 * (e >> 2) + 4 * g + (e & 3);
+              v[e] = t < T ? (__bf16)agpr_read(acc[4 * i + j][8 * hh + e]) : (__bf16)0.f;
+            }
+            *(bf16x8*)(vt + (bh * DC + 32 * j + n) * tp + p0) = v;
+          }
+        }
+  };
+  if (vhalf) run(std::true_type{});
+  else run(std::false_type{});
 }
 
 // ---------------------------------------------------------------------------
@@ -438,7 +461,7 @@ hipError_t launch_v2_prefill(const Layer& L, const void* pool, int num_pages, co
   hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((T * (DR / 2) + 255) / 256)), dim3(256), 0,
                      s, T, L.rope_base, tab);
   const int nt = (T + EX_TOK - 1) / EX_TOK;
-  hipLaunchKernelGGL(expand_kernel, dim3((unsigned)(H * B * nt)), dim3(256), 0, s,
+  hipLaunchKernelGGL(expand_kernel, dim3((unsigned)(H * B * nt)), dim3(64 * EX_NW), 0, s,
                      (const uint16_t*)c_kv, (const uint16_t*)w_uk, (const uint16_t*)w_uv, B, T,
                      lay.tp, nt, kc, vt);
   const int nqb = (T + QB - 1) / QB;
