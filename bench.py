@@ -220,17 +220,30 @@ def main():
                 step(i)
         torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
+        # one graph per step (for a step count that is not a multiple of the
+        # replica count) and one graph holding a step on every replica in
+        # turn, as a serving loop captures consecutive layers
         for i in range(len(reps)):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 step(i)
             graphs.append(g)
-        for i in range(args.warmup):
-            graphs[i % len(graphs)].replay()
+        R = len(reps)
+        g_all = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_all):
+            for i in range(R):
+                step(i)
+
+        def replay_steps(n):  # exactly n steps, replicas in turn from 0
+            for _ in range(n // R):
+                g_all.replay()
+            for i in range(n % R):
+                graphs[i].replay()
+
+        replay_steps(args.warmup)
         torch.cuda.synchronize()
         t0.record()
-        for i in range(args.steps):
-            graphs[i % len(graphs)].replay()
+        replay_steps(args.steps)
         t1.record()
         torch.cuda.synchronize()
         graph_ms = t0.elapsed_time(t1) / args.steps
@@ -280,7 +293,7 @@ def main():
             "attended_tokens": tokens,
             "replicas": len(reps),
             "resident_cache_GB": round(resident, 3),
-            "timing": "hip graph replay" if graph_ms is not None else "eager launches",
+            "timing": "hip graph replay, one graph per %d consecutive steps" % len(reps) if graph_ms is not None else "eager launches",
         },
         "latent_cache_GBps": round(cache_bytes / (ms * 1e-3) / 1e9, 1),
         "step_hbm_frac": round(cache_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
