@@ -40,6 +40,7 @@ constexpr int ROWB = 1152;   // cached row bytes
 constexpr int PS = 64;       // page size
 constexpr int TILEB = PS * ROWB;  // 73728 bytes per page
 constexpr int KSTEPS = ROW / 16;  // 36 MFMA k-steps over a row
+constexpr int SUB = 32;           // tokens per pipelined sub-tile (half a page)
 
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 
@@ -93,11 +94,12 @@ __device__ __forceinline__ float f16_hi(uint32_t u) {
 // Workspace layout
 // ---------------------------------------------------------------------------
 struct WsLayout {
-  size_t plan, plan_wg, q_abs, part_ml, part_o, total;
+  size_t plan, plan_u, plan_wg, q_abs, part_ml, part_o, total;
   WsLayout(int B, int W) {
     const size_t slots = (size_t)W + B;
     plan = 0;
-    plan_wg = align256(plan + sizeof(int32_t) * (size_t)(3 * B + 2));
+    plan_u = align256(plan + sizeof(int32_t) * (size_t)(3 * B + 2));
+    plan_wg = align256(plan_u + sizeof(long long) * (size_t)(B + 1));
     q_abs = align256(plan_wg + sizeof(int32_t) * 4 * (size_t)W);
     part_ml = align256(q_abs + (size_t)B * H * ROW * 2);
     part_o = align256(part_ml + slots * H * 2 * sizeof(float));
@@ -106,13 +108,25 @@ struct WsLayout {
 };
 
 // ---------------------------------------------------------------------------
-// plan: tile prefix over sequences and the first/last workgroup of each one.
-// plan[0..B] = exclusive prefix of ceil(len/64) (plan[B] = N),
-// plan[B+1+2b], plan[B+2+2b] = first, last workgroup of sequence b (first >
-// last when the sequence is empty), plan[3B+1] = W_eff = min(W, N): the number
-// of workgroups that get tiles (each gets at least one).  wg[ib] = (t0, t1, b0,
-// w) for launched workgroup ib: its logical index w and page range [t0, t1)
-// and the sequence holding page t0 (t0 == t1 for an idle workgroup).
+// plan: how the 32-token sub-tiles of all sequences are split over the
+// workgroups.  Sequence b has n_b = ceil(len_b / 32) sub-tiles and weighs
+// 2 n_b + SEG_UNITS units (half sub-tiles): its sub-tiles plus the fixed cost
+// of a segment (loading the sequence's queries, storing a partial result).
+// The units of all sequences are laid end to end and split evenly over W_eff
+// workgroups; unit position x maps to global sub-tile
+//   g(x) = S_b + clamp(ceil((x - P_b - SEG_UNITS) / 2), 0, n_b)
+// for the sequence b with P_b <= x < P_{b+1} (S, P: exclusive prefixes of the
+// sub-tile counts and the units), and workgroup w takes the sub-tiles
+// [g(x_w), g(x_{w+1})) with x_w = floor(w U / W_eff).  W_eff = min(W, U / (SEG_UNITS + 2)),
+// so every workgroup's range spans at least one whole sub-tile.
+//   plan[0..B]             = S (plan[B] = total sub-tiles)
+//   plan[B+1+2b], [B+2+2b] = first, last workgroup of sequence b (first > last
+//                            when the sequence is empty)
+//   plan[3B+1]             = W_eff
+//   plan_u[0..B]           = P
+//   wg[ib] = (s0, s1, b0, w) for launched workgroup ib: logical index w,
+//            sub-tile range [s0, s1), b0 the sequence holding sub-tile s0
+//            (s0 == s1 for an idle workgroup).
 // Logical workgroups are laid out XCD by XCD: launched workgroup ib runs on
 // XCD ib % 8, and XCD x owns the contiguous logical block starting at
 // x * (W_eff / 8) + min(x, W_eff % 8), so neighbouring splits of a sequence
@@ -125,81 +139,106 @@ __device__ __forceinline__ int launched_of_logical(int w, int We) {
   return 8 * (w - (x * q8 + min(x, r8))) + x;
 }
 
+constexpr int SEG_UNITS = 3;      // a segment costs about 1.5 sub-tiles
 constexpr int PLAN_NT = 256;      // threads of the block that builds the plan
-constexpr int PLAN_CACHE = 4096;  // sequences whose tile count and prefix stay in LDS
+constexpr int PLAN_CACHE = 2048;  // sequences whose prefixes stay in LDS for the searches
 
 // Builds the plan with one block of PLAN_NT threads.  cache: LDS scratch of
-// 2 * PLAN_CACHE ints (tile counts and exclusive prefixes of the first
-// PLAN_CACHE sequences, so the second pass does not read them back from
-// global memory).
+// PLAN_CACHE * 12 bytes (S and P of the first PLAN_CACHE sequences, for the
+// binary searches; larger batches search the global copies).
 __device__ void plan_block(const int32_t* __restrict__ seq_lens, int B, int W,
-                           int32_t* __restrict__ plan, int4* __restrict__ wg, int32_t* cache) {
-  __shared__ int32_t wsum[PLAN_NT / 64];
+                           int32_t* __restrict__ plan, long long* __restrict__ plan_u,
+                           int4* __restrict__ wg, char* cache) {
+  __shared__ long long wsum[2][PLAN_NT / 64];
+  __shared__ long long tot_s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int32_t* c_tiles = cache;
-  int32_t* c_pre = cache + PLAN_CACHE;
-  int carry = 0;  // tiles of the sequences before this chunk (same in every thread)
+  long long* c_p = (long long*)cache;                  // P (units)
+  int32_t* c_s = (int32_t*)(cache + PLAN_CACHE * 8);   // S (sub-tiles)
+  long long carry_s = 0, carry_u = 0;
   for (int base = 0; base < B; base += PLAN_NT) {
     const int b = base + tid;
     const int len = b < B ? seq_lens[b] : 0;
-    const int tiles = len > 0 ? (len + PS - 1) / PS : 0;
-    int x = tiles;  // inclusive scan inside the wave
+    const long long n = len > 0 ? (len + SUB - 1) / SUB : 0;
+    const long long u = n > 0 ? 2 * n + SEG_UNITS : 0;
+    long long xs = n, xu = u;  // inclusive scans inside the wave
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(x, off);
-      if (lane >= off) x += y;
+      const long long ys = __shfl_up(xs, off), yu = __shfl_up(xu, off);
+      if (lane >= off) {
+        xs += ys;
+        xu += yu;
+      }
     }
-    if (lane == 63) wsum[wave] = x;
+    if (lane == 63) {
+      wsum[0][wave] = xs;
+      wsum[1][wave] = xu;
+    }
     __syncthreads();
-    int before = 0, total = 0;
+    long long bs = 0, bu = 0, ts = 0, tu = 0;
 #pragma unroll
     for (int v = 0; v < PLAN_NT / 64; ++v) {
-      before += v < wave ? wsum[v] : 0;
-      total += wsum[v];
+      bs += v < wave ? wsum[0][v] : 0;
+      bu += v < wave ? wsum[1][v] : 0;
+      ts += wsum[0][v];
+      tu += wsum[1][v];
     }
-    const int excl = carry + before + x - tiles;
     if (b < B) {
-      plan[b] = excl;
+      const long long es = carry_s + bs + xs - n, eu = carry_u + bu + xu - u;
+      plan[b] = (int32_t)es;
+      plan_u[b] = eu;
+      plan[B + 1 + 2 * b] = 0x7fffffff;  // first / last, lowered / raised below
+      plan[B + 2 + 2 * b] = -1;
       if (b < PLAN_CACHE) {
-        c_tiles[b] = tiles;
-        c_pre[b] = excl;
+        c_s[b] = (int32_t)es;
+        c_p[b] = eu;
       }
     }
-    carry += total;
-    __syncthreads();  // wsum is reused by the next chunk; the cache is complete
+    carry_s += ts;
+    carry_u += tu;
+    __syncthreads();  // wsum is reused by the next chunk
   }
-  // never more workgroups than tiles, so that no workgroup is left empty
-  const int We = max(1, min(W, carry));
+  const long long N = carry_s, U = carry_u;
+  const int We = (int)max(1LL, min((long long)W, U / (SEG_UNITS + 2)));
   if (tid == 0) {
-    plan[B] = carry;
+    plan[B] = (int32_t)N;
+    plan_u[B] = U;
     plan[3 * B + 1] = We;
   }
-  const long long N = carry;
   for (int ib = We + tid; ib < W; ib += PLAN_NT) wg[ib] = make_int4(0, 0, 0, 0);
-  for (int b = tid; b < B; b += PLAN_NT) {
-    int tiles, x0i;
-    if (b < PLAN_CACHE) {
-      tiles = c_tiles[b];
-      x0i = c_pre[b];
-    } else {
-      const int len = seq_lens[b];
-      tiles = len > 0 ? (len + PS - 1) / PS : 0;
-      x0i = plan[b];  // written by this thread in the first pass
+  __syncthreads();  // plan, plan_u and the cache are complete
+  auto S_of = [&](int b) -> long long { return b >= B ? N : (b < PLAN_CACHE ? c_s[b] : plan[b]); };
+  auto P_of = [&](int b) -> long long { return b >= B ? U : (b < PLAN_CACHE ? c_p[b] : plan_u[b]); };
+  // sequence b with P_b <= x < P_{b+1} (the last such b for x == U: B - 1)
+  auto seq_of_unit = [&](long long x) {
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (P_of(mid) <= x) lo = mid;
+      else hi = mid - 1;
     }
-    int first = 1, last = 0;
-    if (tiles > 0) {
-      const long long x0 = x0i, x1 = x0 + tiles - 1;
-      first = (int)(((x0 + 1) * We - 1) / N);
-      last = (int)(((x1 + 1) * We - 1) / N);
-      // the workgroups whose range starts inside this sequence
-      for (int w = first; w <= last; ++w) {
-        const long long s0 = (long long)w * N / We;
-        if (s0 >= x0 && s0 <= x1)
-          wg[launched_of_logical(w, We)] = make_int4((int)s0, (int)((long long)(w + 1) * N / We), b, w);
+    return lo;
+  };
+  auto g_of = [&](long long x, int b) -> long long {
+    if (x >= U) return N;
+    const long long o = x - P_of(b) - SEG_UNITS;
+    const long long n = S_of(b + 1) - S_of(b);
+    const long long j = o <= 0 ? 0 : min(n, (o + 1) >> 1);
+    return S_of(b) + j;
+  };
+  for (int w = tid; w < We; w += PLAN_NT) {
+    const long long x0 = (long long)w * U / We, x1 = (long long)(w + 1) * U / We;
+    int b0 = seq_of_unit(x0);
+    const long long s0 = g_of(x0, b0);
+    const long long s1 = g_of(x1, x1 >= U ? B - 1 : seq_of_unit(x1));
+    while (b0 + 1 < B && S_of(b0 + 1) <= s0) ++b0;  // the sequence holding sub-tile s0
+    wg[launched_of_logical(w, We)] = make_int4((int)s0, (int)s1, b0, w);
+    if (s1 > s0) {
+      for (int b = b0; b < B && S_of(b) < s1; ++b) {
+        if (S_of(b + 1) == S_of(b)) continue;  // empty sequence
+        atomicMin(&plan[B + 1 + 2 * b], w);
+        atomicMax(&plan[B + 2 + 2 * b], w);
       }
     }
-    plan[B + 1 + 2 * b] = first;
-    plan[B + 2 + 2 * b] = last;
   }
   if (N == 0 && tid == 0) wg[0] = make_int4(0, 0, 0, 0);
 }
@@ -220,16 +259,16 @@ __global__ void __launch_bounds__(256)
 q_absorb_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_rope,
                 const uint16_t* __restrict__ w_uk, const int32_t* __restrict__ seq_lens, int B,
                 RopeThetas rope, uint16_t* __restrict__ q_abs, int W, int32_t* __restrict__ plan,
-                int4* __restrict__ plan_wg, uint16_t* __restrict__ pool, int num_pages,
+                long long* __restrict__ plan_u, int4* __restrict__ plan_wg, uint16_t* __restrict__ pool, int num_pages,
                 const int32_t* __restrict__ table, int max_pages, const uint16_t* __restrict__ c_new,
                 const uint16_t* __restrict__ k_new, double rope_base) {
   // workgroup 0 builds the split plan; it is dispatched first, so it runs
   // beside the absorption workgroups instead of after them
   // W^UK_h[:, c0:c0+128] as two [128 rows r][64 cols] halves, swizzled
   __shared__ __attribute__((aligned(16))) char wl[2 * DC * 128];
-  static_assert(2 * DC * 128 >= 2 * PLAN_CACHE * 4, "plan cache must fit the tile buffer");
+  static_assert(2 * DC * 128 >= PLAN_CACHE * 12, "plan cache must fit the tile buffer");
   if (blockIdx.x == 0) {
-    plan_block(seq_lens, B, W, plan, plan_wg, (int32_t*)wl);
+    plan_block(seq_lens, B, W, plan, plan_u, plan_wg, wl);
     return;
   }
   if (blockIdx.x > 4 * H) {
@@ -388,7 +427,6 @@ q_absorb_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __restrict_
 // ---------------------------------------------------------------------------
 // decode_splitkv (see the file header)
 // ---------------------------------------------------------------------------
-constexpr int SUB = 32;                   // tokens per pipelined sub-tile
 constexpr int SUBB = SUB * ROWB;          // 36864 bytes
 constexpr int NBUF = 4;                   // LDS ring of sub-tiles
 constexpr int DMA_SUB = SUBB / 1024 / 4;  // 9 one-KiB loads per wave per sub-tile
@@ -450,12 +488,11 @@ __device__ __forceinline__ void issue_sub(const char* __restrict__ src, char* bu
                                      0, kStreamPolicy);
 }
 
-// A position in the workgroup's sub-tile stream: sub-tile u (0 or 1, the
-// 32-token halves) of tile t, which is page t - pbeg of sequence b (tiles
-// [pbeg, pend), len tokens).  The second half of a page is skipped when it
-// holds no token.
+// A position in the workgroup's sub-tile stream: global sub-tile s, which is
+// sub-tile j = s - sbeg of sequence b (global sub-tiles [sbeg, send), len
+// tokens): the 32-token half j & 1 of its page j >> 1.
 struct SubCursor {
-  int b, pbeg, pend, len, t, u;
+  int b, sbeg, send, len, s;
 };
 
 __global__ void __launch_bounds__(256)
@@ -466,8 +503,8 @@ decode_splitkv_kernel(const char* __restrict__ pool, int num_pages, const int32_
                       const int4* __restrict__ wg, float* __restrict__ part_ml,
                       uint16_t* __restrict__ part_o, float sc_log2) {
   __shared__ __attribute__((aligned(1024))) char lds[NBUF * SUBB];
-  const int4 mine = wg[blockIdx.x];  // (t0, t1, first sequence, logical index)
-  const int t0 = mine.x, t1 = mine.y, w = mine.w;
+  const int4 mine = wg[blockIdx.x];  // (s0, s1, first sequence, logical index)
+  const int t0 = mine.x, t1 = mine.y, w = mine.w;  // sub-tile range [t0, t1)
   if (t0 >= t1) return;
   const int tid = threadIdx.x;
   // wave-uniform (so the copy bases stay scalar and each copy takes a 32-bit
@@ -497,45 +534,40 @@ decode_splitkv_kernel(const char* __restrict__ pool, int num_pages, const int32_
   const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)lds);
 
   auto advance = [&](SubCursor& c) {
-    if (c.u == 0 && PS * (c.t - c.pbeg) + SUB < c.len) {
-      c.u = 1;
-      return;
-    }
-    c.u = 0;
-    ++c.t;
-    if (c.t < t1 && c.t >= c.pend) {
-      while (c.pend <= c.t) {  // next sequence with pages
+    ++c.s;
+    if (c.s < t1 && c.s >= c.send) {
+      while (c.send <= c.s) {  // next sequence with sub-tiles
         ++c.b;
-        c.pbeg = c.pend;
-        c.pend = plan[c.b + 1];
+        c.sbeg = c.send;
+        c.send = plan[c.b + 1];
       }
       c.len = seq_lens[c.b];
     }
   };
   SubCursor cc;
   cc.b = mine.z;
-  cc.pbeg = plan[cc.b];
-  cc.pend = plan[cc.b + 1];
+  cc.sbeg = plan[cc.b];
+  cc.send = plan[cc.b + 1];
   cc.len = seq_lens[cc.b];
-  cc.t = t0;
-  cc.u = 0;
+  cc.s = t0;
 
   // ---- DMA side: sub-tile k of the stream goes to LDS slot k % NBUF
   SubCursor ic = cc;
   int issued = 0;
   int okmask = 0;  // bit s: the sub-tile in slot s comes from a usable page
-  // page id of the issue cursor's tile (-1 if unusable or past the range)
+  // page id of the issue cursor's sub-tile (-1 if unusable or past the range)
   auto page_at_ic = [&]() {
-    const int j = ic.t - ic.pbeg;
-    return (ic.t < t1 && j < max_pages) ? table[(size_t)ic.b * max_pages + j] : -1;
+    const int j = (ic.s - ic.sbeg) >> 1;
+    return (ic.s < t1 && j < max_pages) ? table[(size_t)ic.b * max_pages + j] : -1;
   };
+  auto half_at_ic = [&]() { return (ic.s - ic.sbeg) & 1; };
   auto issue_next = [&]() {
-    if (ic.t >= t1) return;
+    if (ic.s >= t1) return;
     const int p = page_at_ic();
     const bool ok = p >= 0 && p < num_pages;
     const int slot = issued & (NBUF - 1);
     okmask = (okmask & ~(1 << slot)) | ((ok ? 1 : 0) << slot);
-    issue_sub(pool + (size_t)(ok ? p : 0) * TILEB + ic.u * SUBB, lds + slot * SUBB, wave, dp);
+    issue_sub(pool + (size_t)(ok ? p : 0) * TILEB + half_at_ic() * SUBB, lds + slot * SUBB, wave, dp);
     ++issued;
     advance(ic);
   };
@@ -546,12 +578,12 @@ decode_splitkv_kernel(const char* __restrict__ pool, int num_pages, const int32_
   char* cp_dst = lds;
   bool cp_on = false;
   auto copy_begin = [&](int p) {
-    cp_on = ic.t < t1;
+    cp_on = ic.s < t1;
     if (!cp_on) return;
     const bool ok = p >= 0 && p < num_pages;
     const int slot = issued & (NBUF - 1);
     okmask = (okmask & ~(1 << slot)) | ((ok ? 1 : 0) << slot);
-    cp_src = pool + (size_t)(ok ? p : 0) * TILEB + ic.u * SUBB + wave * 8 * ROWB;
+    cp_src = pool + (size_t)(ok ? p : 0) * TILEB + half_at_ic() * SUBB + wave * 8 * ROWB;
     cp_dst = lds + slot * SUBB + wave * 8 * ROWB;
     ++issued;
     advance(ic);
@@ -569,7 +601,7 @@ decode_splitkv_kernel(const char* __restrict__ pool, int num_pages, const int32_
   // second copy of sub-tile 0 into a slot that is never read, so that the
   // number of copies after the query loads is fixed.
   auto issue_or_repeat = [&]() {
-    if (ic.t < t1) {
+    if (ic.s < t1) {
       issue_next();
     } else {
       const int slot = issued & (NBUF - 1);  // a slot past the last sub-tile
@@ -579,7 +611,7 @@ decode_splitkv_kernel(const char* __restrict__ pool, int num_pages, const int32_
   };
   // rows of sub-tile c that hold tokens (0 if its page is unusable)
   auto valid_rows = [&](const SubCursor& c, int slot) {
-    return ((okmask >> slot) & 1) ? min(SUB, c.len - PS * (c.t - c.pbeg) - SUB * c.u) : 0;
+    return ((okmask >> slot) & 1) ? min(SUB, c.len - SUB * (c.s - c.sbeg)) : 0;
   };
   // Rows past the sequence end (or of an unusable page) may hold any bits; a
   // zero probability times a NaN row would still poison the P.V product, so
@@ -626,7 +658,7 @@ decode_splitkv_kernel(const char* __restrict__ pool, int num_pages, const int32_
     const int slot = i & (NBUF - 1);
     SubCursor nx = cc;
     advance(nx);
-    const bool has_next = nx.t < t1;
+    const bool has_next = nx.s < t1;
     const bool seg_end = !has_next || nx.b != cc.b;
     const int pg_next = page_at_ic();  // requested now, used after the waits below
     // sub-tiles issued after i: up to two
@@ -919,6 +951,7 @@ hipError_t launch_v2_decode(const Layer& L, const void* pool, int num_pages, con
   uint16_t* part_o = (uint16_t*)(base + lay.part_o);
   const float sc_log2 = L.scale * 1.4426950408889634f;
   int4* plan_wg = (int4*)(base + lay.plan_wg);
+  long long* plan_u = (long long*)(base + lay.plan_u);
   RopeThetas th;
   for (int k = 0; k < DR / 2; ++k) th.theta[k] = std::pow(L.rope_base, -2.0 * k / DR);
   // block 0: split plan; blocks 1 .. 4H: absorption; then (with a new token
@@ -926,7 +959,7 @@ hipError_t launch_v2_decode(const Layer& L, const void* pool, int num_pages, con
   const unsigned app_blocks = c_new ? (unsigned)((batch + 3) / 4) : 0u;
   hipLaunchKernelGGL(q_absorb_kernel, dim3(H * 4 + 1 + app_blocks), dim3(256), 0, s,
                      (const uint16_t*)q_nope, (const uint16_t*)q_rope, (const uint16_t*)w_uk,
-                     seq_lens, batch, th, q_abs, n_wg, plan, plan_wg, (uint16_t*)pool, num_pages,
+                     seq_lens, batch, th, q_abs, n_wg, plan, plan_u, plan_wg, (uint16_t*)pool, num_pages,
                      table, max_pages, (const uint16_t*)c_new, (const uint16_t*)k_new, L.rope_base);
   hipError_t e = mark(ev, 0, s);
   if (e != hipSuccess) return e;
