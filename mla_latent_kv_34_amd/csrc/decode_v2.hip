@@ -139,7 +139,8 @@ __device__ __forceinline__ int launched_of_logical(int w, int We) {
   return 8 * (w - (x * q8 + min(x, r8))) + x;
 }
 
-constexpr int SEG_UNITS = 3;      // a segment costs about 1.5 sub-tiles
+constexpr int SEG_UNITS = 10;     // a segment (query load, partial store, pipeline refill)
+                                  // costs about five sub-tiles (measured)
 constexpr int PLAN_NT = 256;      // threads of the block that builds the plan
 constexpr int PLAN_CACHE = 2048;  // sequences whose prefixes stay in LDS for the searches
 
