@@ -118,7 +118,11 @@ struct WsLayout {
 // for the sequence b with P_b <= x < P_{b+1} (S, P: exclusive prefixes of the
 // sub-tile counts and the units), and workgroup w takes the sub-tiles
 // [g(x_w), g(x_{w+1})) with x_w = floor(w U / W_eff).  W_eff = min(W, U / (SEG_UNITS + 2)),
-// so every workgroup's range spans at least one whole sub-tile.
+// so every workgroup's range spans at least one whole sub-tile.  A workload too
+// small to give every workgroup that much (U < (SEG_UNITS + 2) W) is split by
+// sub-tiles alone (segment cost 0, W_eff = min(W, total sub-tiles)): there,
+// spreading the few sub-tiles over more workgroups shortens the kernel more
+// than the extra query loads cost.
 //   plan[0..B]             = S (plan[B] = total sub-tiles)
 //   plan[B+1+2b], [B+2+2b] = first, last workgroup of sequence b (first > last
 //                            when the sequence is empty)
@@ -198,17 +202,23 @@ __device__ void plan_block(const int32_t* __restrict__ seq_lens, int B, int W,
     carry_u += tu;
     __syncthreads();  // wsum is reused by the next chunk
   }
-  const long long N = carry_s, U = carry_u;
-  const int We = (int)max(1LL, min((long long)W, U / (SEG_UNITS + 2)));
+  const long long N = carry_s;
+  const bool weighted = carry_u >= (long long)(SEG_UNITS + 2) * W;
+  const int seg = weighted ? SEG_UNITS : 0;
+  const long long U = weighted ? carry_u : 2 * N;
+  const int We = (int)max(1LL, min((long long)W, U / (seg + 2)));
   if (tid == 0) {
     plan[B] = (int32_t)N;
-    plan_u[B] = U;
+    plan_u[B] = carry_u;
     plan[3 * B + 1] = We;
   }
   for (int ib = We + tid; ib < W; ib += PLAN_NT) wg[ib] = make_int4(0, 0, 0, 0);
   __syncthreads();  // plan, plan_u and the cache are complete
   auto S_of = [&](int b) -> long long { return b >= B ? N : (b < PLAN_CACHE ? c_s[b] : plan[b]); };
-  auto P_of = [&](int b) -> long long { return b >= B ? U : (b < PLAN_CACHE ? c_p[b] : plan_u[b]); };
+  auto P_of = [&](int b) -> long long {
+    if (!weighted) return 2 * S_of(b);
+    return b >= B ? U : (b < PLAN_CACHE ? c_p[b] : plan_u[b]);
+  };
   // sequence b with P_b <= x < P_{b+1} (the last such b for x == U: B - 1)
   auto seq_of_unit = [&](long long x) {
     int lo = 0, hi = B - 1;
@@ -221,7 +231,7 @@ __device__ void plan_block(const int32_t* __restrict__ seq_lens, int B, int W,
   };
   auto g_of = [&](long long x, int b) -> long long {
     if (x >= U) return N;
-    const long long o = x - P_of(b) - SEG_UNITS;
+    const long long o = x - P_of(b) - seg;
     const long long n = S_of(b + 1) - S_of(b);
     const long long j = o <= 0 ? 0 : min(n, (o + 1) >> 1);
     return S_of(b) + j;
@@ -800,7 +810,11 @@ decode_splitkv_kernel(const char* __restrict__ pool, int num_pages, const int32_
 //     merges sequence t / 16, float4 columns t % 16 + 16j (j = 0..7); the
 //     slots are taken two at a time (both sets of loads in flight together)
 //     and merged online (running reference maximum, the sums rescaled when it
-//     rises).
+//     rises).  A block of n < 32 sequences gives each sequence R = 32 / n
+//     groups of 16 threads; group r of a sequence merges slots first + 2r,
+//     first + 2r + 2R, ... and the R partial results (m, l, o) are merged
+//     once more through LDS, so a batch of one still sees 64 slots per
+//     round trip.
 //  2. out_absorb (waves 0-3): out[b, h, r] = sum_c W^UV[h, r, c] o_lat[b, c]
 //     as O^T = W^UV_h o_lat^T; wave v owns rows 32v..32v+31, its W^UV
 //     fragments are loaded before step 1 so their latency hides behind it.
@@ -814,8 +828,12 @@ __global__ void __launch_bounds__(CO_NT) __attribute__((amdgpu_waves_per_eu(2, 2
 combine_out_kernel(const int32_t* __restrict__ plan, int B, const float* __restrict__ part_ml,
                    const uint16_t* __restrict__ part_o, const uint16_t* __restrict__ w_uv,
                    uint16_t* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) char ohi[CO_NB * DL * 2];
-  __shared__ __attribute__((aligned(16))) char olo[CO_NB * DL * 2];
+  // the bf16 hi / lo rows of o_lat; before they are written, the same bytes
+  // hold the per-group partials of a block with fewer than CO_NB sequences
+  __shared__ __attribute__((aligned(16))) char lds[2 * CO_NB * DL * 2];
+  __shared__ float2 grp_ml[CO_NT / 16];
+  char* const ohi = lds;
+  char* const olo = lds + CO_NB * DL * 2;
   const int nbb = (B + CO_NB - 1) / CO_NB;
   // launched workgroup ib runs on XCD ib % 8: the sequence blocks of one head
   // get neighbouring logical indices on one XCD, so W^UV_h is fetched into
@@ -836,12 +854,20 @@ combine_out_kernel(const int32_t* __restrict__ plan, int B, const float* __restr
 
   // ---- 1. merged latent vectors into LDS
   {
-    const int i = tid >> 4, cq = tid & 15;
+    const int gi = tid >> 4, cq = tid & 15;
+    const int nseq = min(CO_NB, B - b0);
+    const int R = CO_NB / nseq;  // groups per sequence (block-uniform)
+    const int i = gi / R, r = gi - i * R;
     const int b = b0 + i;
+    // a sequence with no slots keeps first = INT_MAX, last = -1 from the plan:
+    // the group offset 2r is added only to a real first slot
     int first = 1, last = 0;
-    if (b < B) {
-      first = plan[B + 1 + 2 * b];
-      last = plan[B + 2 + 2 * b];
+    if (i < nseq) {
+      const int f = plan[B + 1 + 2 * b], l = plan[B + 2 + 2 * b];
+      if (f <= l) {
+        first = f + 2 * r;
+        last = l;
+      }
     }
     // 16-byte unit u = cq + 16j of a slot row holds dimensions
     // 16(u >> 1) + 4(u & 1) + {0..3} and the same + 8 (the partial layout)
@@ -851,7 +877,7 @@ combine_out_kernel(const int32_t* __restrict__ plan, int B, const float* __restr
 #pragma unroll
       for (int k = 0; k < 8; ++k) o[j][k] = 0.f;
     float M = -INFINITY, Lsum = 0.f;
-    for (int w = first; w <= last; w += 2) {
+    for (int w = first; w <= last; w += 2 * R) {
       const bool two = w + 1 <= last;
       const size_t s0 = ((size_t)w + b) * H + h;
       const size_t s1 = two ? s0 + H : s0;  // slot w + 1 (or w again, weight 0)
@@ -884,26 +910,70 @@ combine_out_kernel(const int32_t* __restrict__ plan, int B, const float* __restr
         }
       }
     }
-    const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
+    if (R > 1) {
+      // partials float k of thread t at pf[k * CO_NT + t]; group maxima and
+      // sums in grp_ml
+      float* const pf = (float*)lds;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int u = cq + 16 * j;
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int c = 16 * (u >> 1) + 4 * (u & 1) + 8 * half;
-        const float x[4] = {o[j][4 * half] * inv, o[j][4 * half + 1] * inv, o[j][4 * half + 2] * inv,
-                            o[j][4 * half + 3] * inv};
-        uint32_t hi2[2], lo2[2];
+        for (int k = 0; k < 8; ++k) pf[(8 * j + k) * CO_NT + tid] = o[j][k];
+      if (cq == 0) grp_ml[gi] = make_float2(M, Lsum);
+      __syncthreads();
+      if (r == 0 && i < nseq) {
+        float Mt = -INFINITY;
+        for (int q = 0; q < R; ++q) Mt = fmaxf(Mt, grp_ml[gi + q].x);
+        Lsum = 0.f;
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          const __bf16 h0 = (__bf16)x[2 * k], h1 = (__bf16)x[2 * k + 1];
-          const __bf16 l0 = (__bf16)(x[2 * k] - (float)h0), l1 = (__bf16)(x[2 * k + 1] - (float)h1);
-          hi2[k] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-          lo2[k] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int k = 0; k < 8; ++k) o[j][k] = 0.f;
+        for (int q = 0; q < R; ++q) {
+          const float2 ml = grp_ml[gi + q];
+          const float f = ml.x == -INFINITY ? 0.f : exp2_fast(ml.x - Mt);
+          Lsum += f * ml.y;
+          const int t = tid + 16 * q;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int k = 0; k < 8; ++k) o[j][k] += f * pf[(8 * j + k) * CO_NT + t];
         }
-        const int byte = i * (DL * 2) + (((c >> 3) ^ (i & 15)) << 4) + (c & 7) * 2;
-        *(uint2*)(ohi + byte) = make_uint2(hi2[0], hi2[1]);
-        *(uint2*)(olo + byte) = make_uint2(lo2[0], lo2[1]);
+      }
+      __syncthreads();
+    }
+    // group gi writes row i (its sequence) if it holds the merged result;
+    // rows past the block's sequences are cleared (a row only feeds its own
+    // output column, but the MFMA should not read stale bytes)
+    const bool data_row = r == 0 && i < nseq;
+    if (data_row) {
+      const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int u = cq + 16 * j;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int c = 16 * (u >> 1) + 4 * (u & 1) + 8 * half;
+          uint32_t hi2[2], lo2[2];
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            const float x0 = o[j][4 * half + 2 * k] * inv, x1 = o[j][4 * half + 2 * k + 1] * inv;
+            const __bf16 h0 = (__bf16)x0, h1 = (__bf16)x1;
+            const __bf16 l0 = (__bf16)(x0 - (float)h0), l1 = (__bf16)(x1 - (float)h1);
+            hi2[k] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+            lo2[k] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+          }
+          const int byte = i * (DL * 2) + (((c >> 3) ^ (i & 15)) << 4) + (c & 7) * 2;
+          *(uint2*)(ohi + byte) = make_uint2(hi2[0], hi2[1]);
+          *(uint2*)(olo + byte) = make_uint2(lo2[0], lo2[1]);
+        }
+      }
+    }
+    if (gi >= nseq) {
+      // 16 threads x 4 x 16 B clear the 1 KiB hi row and the 1 KiB lo row
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        *(uint4*)(ohi + gi * (DL * 2) + 16 * (cq + 16 * j)) = make_uint4(0, 0, 0, 0);
+        *(uint4*)(olo + gi * (DL * 2) + 16 * (cq + 16 * j)) = make_uint4(0, 0, 0, 0);
       }
     }
   }

@@ -182,6 +182,22 @@ def test_v2_many_short_sequences(batch, hi, n_wg):
         assert_close(f64(out[b]), _oracle(case, b), f"seq {b} len {case.attended[b]}")
 
 
+@pytest.mark.parametrize("batch", [33, 40, 48])
+def test_v2_partial_sequence_blocks(batch):
+    """The combine takes sequences 32 at a time; a last block of 1, 8 or 16
+    sequences spreads each sequence's partial slots over 32, 4 or 2 thread
+    groups and merges their results once more.  Every sequence of the last
+    block, and a few of the first, are checked."""
+    print(f"case partial blocks: batch {batch}", flush=True)
+    lens = syn.ragged_lengths(batch, 1, 900, seed=batch + 5)
+    case = syn.decode_case(syn.V2, lens, append=True, seed=17, shuffle=True)
+    dims, pool, table, seq_lens = device_case(case)
+    out = run_decode(case, dims, pool, table, seq_lens)
+    assert torch.isfinite(out.float()).all()
+    for b in [0, 7, 31] + list(range(32, batch)):
+        assert_close(f64(out[b]), _oracle(case, b), f"seq {b} len {case.attended[b]}")
+
+
 def _step_inputs(case):
     """The step's new token rows [batch, d_c] and [batch, d_h^R] (position cached[b])."""
     c_new = torch.stack([case.seq_rows(b)[0][-1] for b in range(case.batch)]).to(DEV)
