@@ -9,13 +9,13 @@ never targets an operand of an MFMA still to be issued; reads run five MFMAs
 ahead, which covers the LDS latency when four waves read at once.
 
 Per 32-token sub-tile the kernel runs qk_chain (S^T = K Q^T), the row
-maximum and the first half's probabilities in C++, then pv_half0_exp: the
-MFMAs of the first 16 tokens' P.V while the VALU computes the second half's
-probabilities (exp2(s * c - m), their sum and their bf16 packing), and
-pv_half1.  The VALU instructions are interleaved between the MFMAs so they
-issue while the matrix core is busy; they write registers no MFMA of the block
-reads, and a v_exp_f32 result is read no sooner than two instructions later.
-load_q_sync loads a sequence's query fragments and waits for them inside the
+maximum and the first half's probabilities in C++, then pv_full: the 16 MFMAs
+of the first 16 tokens' P.V while the VALU computes the second half's
+probabilities (exp2(s * c - m), their sum and their bf16 packing), then the 16
+MFMAs of the second half.  The VALU instructions are interleaved between the
+MFMAs so they issue while the matrix core is busy; they write registers no
+MFMA of the block reads, and a v_exp_f32 result is read no sooner than two
+instructions later.  load_q_sync loads a sequence's query fragments and waits for them inside the
 block.
 
 Run: python gen_splitkv_asm.py > splitkv_asm.h
@@ -26,7 +26,6 @@ KSTEPS = 36        # 576 / 16
 NSLOT = 6
 AHEAD = 5
 XDL_TO_VALU_NOPS = ["s_nop 7", "s_nop 7", "s_nop 7"]  # 24 wait states
-QK_SPLIT = 12      # k-steps of S(i+1) issued in qk_max; the rest in qk_exp
 
 
 SLOT0 = 256 - 4 * NSLOT  # first scratch VGPR
@@ -99,71 +98,6 @@ __device__ __forceinline__ void qk_chain(const bf16x8 (&q)[{KSTEPS}], const uint
       : {ins}
       : {CLOBBER});
 }}
-"""
-
-
-def pv_half(kb, with_exp):
-    """O^T += V^T P^T for one 16-token half kb of the sub-tile: 16 MFMAs over
-    the blocks of 32 latent columns.  With with_exp the probabilities of the
-    other half (tokens 16..31, S^T entries 8..15 of this lane) are computed on
-    the VALU meanwhile: p = exp2(s * sc + nm), packed to bf16 into p1, summed
-    into l; the 8 score registers are overwritten."""
-    name = f"pv_half{kb}" + ("_exp" if with_exp else "")
-    lines = ["s_waitcnt lgkmcnt(0)", "s_nop 4"]
-    n = 16
-
-    def rd(i):
-        cb = i
-        off = 16 * kb * ROWB + (cb >> 1) * 128
-        return [f"ds_read_b64_tr_b16 {_slot(i, 0)}, %[v{cb & 1}] offset:{off}",
-                f"ds_read_b64_tr_b16 {_slot(i, 1)}, %[w{cb & 1}] offset:{off}"]
-
-    valu = []
-    if with_exp:
-        valu = [f"v_fma_f32 %[e{k}], %[e{k}], %[sc], %[nm]" for k in range(8)]
-        valu += [f"v_exp_f32 %[e{k}], %[e{k}]" for k in range(8)]
-        valu += [f"v_cvt_pk_bf16_f32 %[q{k}], %[e{2 * k}], %[e{2 * k + 1}]" for k in range(4)]
-        valu += [f"v_add_f32 %[e{2 * k}], %[e{2 * k}], %[e{2 * k + 1}]" for k in range(4)]
-        valu += ["v_add_f32 %[e0], %[e0], %[e2]", "v_add_f32 %[e4], %[e4], %[e6]",
-                 "v_add_f32 %[e0], %[e0], %[e4]", "v_add_f32 %[l], %[l], %[e0]"]
-    per = [[] for _ in range(n)]
-    for j, v in enumerate(valu):
-        per[min(n - 1, j * n // max(1, len(valu)))].append(v)
-    for i in range(AHEAD):
-        lines += rd(i)
-    for i in range(n):
-        cb = i
-        lines.append(f"s_waitcnt lgkmcnt({2 * min(AHEAD - 1, n - 1 - i)})")
-        lines.append(f"v_mfma_f32_32x32x16_bf16 %[c{cb}], {_slot(i)}, %[p], %[c{cb}]")
-        if i + AHEAD < n:
-            lines += rd(i + AHEAD)
-        lines += per[i]
-    lines += XDL_TO_VALU_NOPS
-    outs = [f'[c{c}] "+a"(acc[{c}])' for c in range(16)]
-    ins = ['[p] "v"(p)', '[v0] "v"(v[0])', '[v1] "v"(v[1])', '[w0] "v"(v[2])', '[w1] "v"(v[3])']
-    if with_exp:
-        outs += ['[l] "+v"(l)'] + [f'[e{k}] "+v"(s[{8 + k}])' for k in range(8)]
-        outs += [f'[q{k}] "=&v"(pw[{k}])' for k in range(4)]
-        ins += ['[sc] "v"(sc)', '[nm] "v"(nm)']
-        sig = ("f32x16 (&acc)[16], const bf16x8& p, const uint32_t (&v)[4], f32x16& s, float sc, "
-               "float nm, float& l, bf16x8& p1")
-        pre = "  uint32_t pw[4];\n"
-        post = "  p1 = __builtin_bit_cast(bf16x8, (u32x4){pw[0], pw[1], pw[2], pw[3]});\n"
-    else:
-        sig = "f32x16 (&acc)[16], const bf16x8& p, const uint32_t (&v)[4]"
-        pre = post = ""
-    body = _emit(lines)
-    return f"""// O^T (512 latent columns x 32 heads) += V^T P^T for the 16-token half {kb} of
-// a sub-tile.  v[par] and v[2 + par]: LDS byte addresses of this lane's first
-// and second transpose-read sources (rows trow and trow + 8) for column blocks
-// of parity par; p: the bf16 probabilities of the half's tokens in k-slot order.
-__device__ __forceinline__ void {name}({sig}) {{
-{pre}  asm volatile(
-{body}
-      : {", ".join(outs)}
-      : {", ".join(ins)}
-      : {CLOBBER});
-{post}}}
 """
 
 
