@@ -56,7 +56,7 @@ def test_tiny_fp32_prefill():
         assert_close(f64(out[b]), _oracle(case, b), f"tiny prefill seq {b}")
 
 
-@pytest.mark.parametrize("T", [1, 63, 64, 65, 200, 257])
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 200, 257, 600])
 def test_v2_prefill_small(T):
     """V2 sizes, short prompts around the 64-token tile and page edges: every
     row, every head, and the cache bytes."""
