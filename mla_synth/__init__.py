@@ -29,7 +29,7 @@ import torch
 __all__ = [
     "Dims", "TINY", "V2", "DecodeCase", "PrefillCase", "draw", "to_storage",
     "weights", "decode_case", "prefill_case", "ragged_lengths", "page_table",
-    "CONFIGS",
+    "CONFIGS", "front_weights", "hidden", "HiddenCase", "hidden_case",
 ]
 
 
@@ -65,6 +65,7 @@ V2 = Dims(n_heads=128, d_nope=128, d_rope=64, d_latent=512, d_cq=1536, d_model=5
 
 # tensor ids of the per-tensor random streams
 _T_QC, _T_QR, _T_C, _T_KR, _T_WUK, _T_WUV, _T_LENS, _T_PERM = range(1, 9)
+_T_H, _T_WDKV, _T_WKR, _T_WDQ, _T_WUQ, _T_WQR = range(9, 15)
 
 
 def draw(shape, seed: int, tensor_id: int, std: float = 1.0) -> np.ndarray:
@@ -88,6 +89,22 @@ def weights(dims: Dims, seed: int = 0):
     std = 1.0 / np.sqrt(dims.d_latent)
     return (to_storage(draw(shp, seed, _T_WUK, std), dims),
             to_storage(draw(shp, seed, _T_WUV, std), dims))
+
+
+def front_weights(dims: Dims, seed: int = 0):
+    """The projections in front of the path, out x in, each N(0, 1/fan_in):
+    W^DKV [d_c, d], W^KR [d_h^R, d], W^DQ [d_c', d], W^UQ [n_h d_h^C, d_c'],
+    W^QR [n_h d_h^R, d_c'] (storage tensors)."""
+    d, dq = dims.d_model, dims.d_cq
+    shapes = ((_T_WDKV, (dims.d_latent, d), d), (_T_WKR, (dims.d_rope, d), d),
+              (_T_WDQ, (dq, d), d), (_T_WUQ, (dims.n_heads * dims.d_nope, dq), dq),
+              (_T_WQR, (dims.n_heads * dims.d_rope, dq), dq))
+    return tuple(to_storage(draw(shp, seed, tid, 1.0 / np.sqrt(fan)), dims) for tid, shp, fan in shapes)
+
+
+def hidden(batch: int, dims: Dims, seed: int = 0) -> torch.Tensor:
+    """Hidden states h [batch, d] ~ N(0, 1) (storage tensor)."""
+    return to_storage(draw((batch, dims.d_model), seed, _T_H), dims)
 
 
 def ragged_lengths(batch: int, lo: int, hi: int, seed: int) -> np.ndarray:
@@ -175,6 +192,23 @@ def decode_case(dims: Dims, cached, append: bool, seed: int = 0, shuffle: bool =
     return DecodeCase(dims, cached, append, to_storage(q_c, dims), to_storage(q_r, dims),
                       to_storage(c, dims), to_storage(kr, dims), w_uk, w_uv, table, npages,
                       offsets)
+
+
+@dataclass
+class HiddenCase:
+    """A decode step that starts from the hidden state of each sequence's new
+    token.  ``base`` is the append-mode decode case whose cached rows (every
+    row but the last of each sequence) fill the cache and whose page table has
+    room for the new token; its own last rows and q^C / q^R are not used.
+    ``h`` [B, d]; ``front`` = (W^DKV, W^KR, W^DQ, W^UQ, W^QR)."""
+    base: DecodeCase
+    h: torch.Tensor
+    front: tuple
+
+
+def hidden_case(dims: Dims, cached, seed: int = 0, shuffle: bool = False) -> HiddenCase:
+    base = decode_case(dims, cached, append=True, seed=seed, shuffle=shuffle)
+    return HiddenCase(base, hidden(base.batch, dims, seed), front_weights(dims, seed))
 
 
 @dataclass

@@ -56,7 +56,7 @@ import math
 import numpy as np
 
 __all__ = [
-    "rope_frequencies", "rotate_pairs", "rope",
+    "rope_frequencies", "rotate_pairs", "rope", "front_end",
     "expand_heads", "decode_ref", "prefill_ref", "absorbed_decode_ref",
     "bf16_bits_rne", "f32_rne", "append_expected",
     "cache_elements_per_token", "kv_cache_bytes",
@@ -104,6 +104,36 @@ def rope(x: np.ndarray, positions, base: float) -> np.ndarray:
     pos = np.asarray(positions, dtype=np.float64)
     angles = pos[..., None] * theta
     return rotate_pairs(x, angles)
+
+
+# ----------------------------------------------------------------------------
+# The projections in front of the path: tech note [three-branch computation]
+# ----------------------------------------------------------------------------
+
+def front_end(h, w_dkv, w_kr, w_dq, w_uq, w_qr, *, n_heads: int):
+    """Projections of hidden states, as the tech note's three branches give them.
+
+    (1) Query: c^Q = W^DQ h; q^C = W^UQ c^Q, split by heads; q^R = W^QR c^Q,
+        split by heads (RoPE at the query position is applied by the attention).
+    (2) Key: c^KV = W^DKV h; k^R = W^KR h, taken from h and not from c^KV, one
+        vector shared by all heads (RoPE at the token position is applied when
+        the row is cached).
+    Every weight is stored out x in (y = W x): w_dkv [d_c, d], w_kr [d_h^R, d],
+    w_dq [d_c', d], w_uq [n_h d_h^C, d_c'], w_qr [n_h d_h^R, d_c']; head i owns
+    the rows i*d_h .. (i+1)*d_h - 1 of W^UQ and W^QR (the page's reshape of the
+    16384- and 8192-long outputs into [128, 128] and [128, 64]).
+    h: [..., d].  Returns fp64 (c_kv [..., d_c], k_r [..., d_h^R],
+    q_c [..., n_h, d_h^C], q_r [..., n_h, d_h^R]).
+    """
+    h = np.asarray(h, dtype=np.float64)
+    f = lambda w: np.asarray(w, dtype=np.float64)  # noqa: E731
+    c_q = h @ f(w_dq).T                                                  # [..., d_c']
+    q_c = c_q @ f(w_uq).T                                                # [..., n_h d_C]
+    q_r = c_q @ f(w_qr).T                                                # [..., n_h d_R]
+    c_kv = h @ f(w_dkv).T                                                # [..., d_c]
+    k_r = h @ f(w_kr).T                                                  # [..., d_R]
+    lead = h.shape[:-1]
+    return (c_kv, k_r, q_c.reshape(lead + (n_heads, -1)), q_r.reshape(lead + (n_heads, -1)))
 
 
 # ----------------------------------------------------------------------------
