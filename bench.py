@@ -59,6 +59,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches only")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill measurement")
+    ap.add_argument("--no-hidden", action="store_true",
+                    help="skip the decode-from-hidden-states measurement")
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device copy of this many bytes (HBM counter calibration)")
@@ -268,6 +270,11 @@ def main():
     if not args.no_prefill:
         pre = prefill_bench(mla, syn, dims, dev, args.prefill_steps)
 
+    hid = None
+    n_reps = len(reps)
+    if not args.no_hidden:
+        hid = hidden_bench(mla, syn, dims, dev, lens, args.steps, args.warmup, args.replicas)
+
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(case0, args.cpu_seconds)
@@ -291,9 +298,9 @@ def main():
                         "append 1 token + absorbed decode",
             "batch": B,
             "attended_tokens": tokens,
-            "replicas": len(reps),
+            "replicas": n_reps,
             "resident_cache_GB": round(resident, 3),
-            "timing": "hip graph replay, one graph per %d consecutive steps" % len(reps) if graph_ms is not None else "eager launches",
+            "timing": "hip graph replay, one graph per %d consecutive steps" % n_reps if graph_ms is not None else "eager launches",
         },
         "latent_cache_GBps": round(cache_bytes / (ms * 1e-3) / 1e9, 1),
         "step_hbm_frac": round(cache_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
@@ -313,8 +320,105 @@ def main():
         },
         "cpu_baseline": cpu,
         "prefill": pre,
+        "decode_hidden": hid,
     }
     print(json.dumps(line), flush=True)
+
+
+def hidden_bench(mla, syn, dims, dev, lens, steps: int, warmup: int, replicas: int):
+    """The same batch-64 decode step started from hidden states
+    (mla_decode_hidden): the projections h -> [c^KV | k^R | c^Q] and
+    c^Q -> [q^C | q^R] in front of the step.  Step time by graph replay over
+    replicas (each with its own cache and weights); the projection kernels
+    timed with the library's events, against HBM (their weights and
+    activations are read or written once)."""
+    import numpy as np
+    import torch
+
+    d = syn.V2
+    B = len(lens)
+    tokens = int((lens + 1).sum())
+    print(f"[bench] decode from hidden states: {replicas} replicas", file=sys.stderr, flush=True)
+    reps = []
+    zero = torch.zeros(1, dtype=torch.int32, device=dev)
+    for r in range(replicas):
+        hc = syn.hidden_case(d, lens, seed=100 + r, shuffle=True)
+        base = hc.base
+        pool = torch.zeros((base.num_pages, d.page_size, d.row), dtype=d.torch_dtype, device=dev)
+        table = torch.from_numpy(base.table).to(dev)
+        for b in range(B):
+            c, kr = base.seq_rows(b)
+            n = int(lens[b])
+            mla.cache_append(dims, pool, table[b:b + 1].contiguous(), zero,
+                             c[:n].unsqueeze(0).to(dev), kr[:n].unsqueeze(0).to(dev))
+        seq_lens = torch.tensor(base.attended, dtype=torch.int32, device=dev)
+        args = [hc.h.to(dev)] + [w.to(dev) for w in hc.front] + [base.w_uk.to(dev), base.w_uv.to(dev)]
+        ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        for e in ev:
+            e.record()
+        call, out = mla.decode_hidden(dims, pool, table, seq_lens, *args, prepare=True)
+        call_t, _ = mla.decode_hidden(dims, pool, table, seq_lens, *args, out=out, timing_events=ev,
+                                      prepare=True)
+        reps.append(dict(call=call, call_t=call_t, ev=ev, keep=(pool, table, seq_lens, args, out)))
+        del hc, base
+    torch.cuda.synchronize()
+    R = len(reps)
+    for i in range(warmup):
+        reps[i % R]["call"]()
+    torch.cuda.synchronize()
+    proj = []
+    for i in range(steps):
+        r = reps[i % R]
+        r["call_t"]()
+        torch.cuda.synchronize()
+        proj.append(r["ev"][0].elapsed_time(r["ev"][1]))
+    proj_ms = float(np.mean(proj))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for r in reps:
+            r["call"]()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for r in reps:
+            r["call"]()
+    singles = []
+    for r in reps:
+        gi = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gi):
+            r["call"]()
+        singles.append(gi)
+
+    def replay(n):
+        for _ in range(n // R):
+            g.replay()
+        for i in range(n % R):
+            singles[i].replay()
+
+    replay(warmup)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    replay(steps)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    dm, dq = d.d_model, d.d_cq
+    n1 = d.d_latent + d.d_rope + dq
+    n2 = d.n_heads * (d.d_nope + d.d_rope)
+    wbytes = 2 * (n1 * dm + n2 * dq)
+    abytes = 2 * B * (dm + n1 + dq + n2)        # h in, stage-1 out, c^Q in, stage-2 out
+    gbps = (wbytes + abytes) / (proj_ms * 1e-3) / 1e9
+    return {"workload": "v2_b64_ragged from hidden states: h [64, 5120] -> c^KV, k^R, c^Q "
+                        "(W^DKV, W^KR, W^DQ) -> q^C, q^R (W^UQ, W^QR), then the decode step",
+            "value": round(tokens / (ms * 1e-3), 1), "unit": "cached tokens/s",
+            "ms_per_step": round(ms, 5), "projections_ms": round(proj_ms, 5),
+            "timing": "hip graph replay over %d replicas; projections by events, one step at a time" % R,
+            "roofline": {"kernel": "proj_gemm (+ split-K reduce)", "bound": "hbm",
+                         "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(gbps / HBM_PEAK_GBPS, 4), "algorithmic_bytes": wbytes + abytes}}
 
 
 def prefill_bench(mla, syn, dims, dev, steps: int):

@@ -145,6 +145,37 @@ mla_status mla_decode_step(const mla_dims* dims, const mla_paged_cache* cache, i
                            const void* q_nope, const void* q_rope, const void* w_uk,
                            const void* w_uv, void* out, void* workspace, size_t workspace_bytes,
                            int32_t n_workgroups, void* const* timing_events, void* stream);
+/* Bytes of device workspace mla_decode_hidden needs (0 for unsupported sizes). */
+size_t mla_decode_hidden_workspace_size(const mla_dims* dims, int32_t batch, int32_t n_workgroups,
+                                        int32_t d_model, int32_t d_q);
+
+/* One decode step that starts from each sequence's newest hidden state h_t:
+ * the projections in front of the attention ("MLA low-rank attention" tech
+ * note [three-branch computation]: (1) Query c^Q = W^DQ h, q^C = W^UQ c^Q,
+ * q^R = W^QR c^Q; (2) Key c^KV = W^DKV h, k^R = W^KR h, the latter from h and
+ * shared by all heads), then exactly mla_decode_step with c_kv_new = c^KV,
+ * k_rope_new = k^R, q_nope = q^C and q_rope = q^R.  The projections
+ * accumulate in fp32 and round their outputs to bf16 (round to nearest
+ * even), the storage dtype the step's inputs have.
+ * d_model: d (K of the first projections); d_q: d_c' (K of W^UQ and W^QR);
+ *   both positive multiples of 64.
+ * h:     [batch, d_model] (the token at position seq_lens[b] - 1)
+ * w_dkv: [d_latent, d_model]   w_kr: [d_rope, d_model]   w_dq: [d_q, d_model]
+ * w_uq:  [n_heads * d_nope, d_q]   w_qr: [n_heads * d_rope, d_q]
+ *   (out x in; head i owns rows i*d_nope .. and i*d_rope .. of W^UQ / W^QR)
+ * w_uk, w_uv, out, seq_lens, n_workgroups: as for mla_decode_step.
+ * workspace: at least mla_decode_hidden_workspace_size(...) bytes.
+ * timing_events: NULL, or two hipEvent_t recorded immediately before the
+ *   first projection and after the last one (profiling only).
+ * Only the MFMA family (V2 sizes, bf16) implements it: other sizes return
+ * MLA_ERR_UNSUPPORTED.  Other errors as for mla_decode_step.               */
+mla_status mla_decode_hidden(const mla_dims* dims, const mla_paged_cache* cache, int32_t batch,
+                             const int32_t* seq_lens, int32_t d_model, int32_t d_q, const void* h,
+                             const void* w_dkv, const void* w_kr, const void* w_dq,
+                             const void* w_uq, const void* w_qr, const void* w_uk,
+                             const void* w_uv, void* out, void* workspace, size_t workspace_bytes,
+                             int32_t n_workgroups, void* const* timing_events, void* stream);
+
 /* Bytes of device workspace mla_prefill needs. */
 size_t mla_prefill_workspace_size(const mla_dims* dims, int32_t batch, int32_t seq_len);
 

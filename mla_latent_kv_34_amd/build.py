@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmla.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "append.hip", "generic.hip", "decode_v2.hip", "prefill_v2.hip"]
+SOURCES = ["api.cpp", "append.hip", "generic.hip", "decode_v2.hip", "prefill_v2.hip", "proj.hip"]
 
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

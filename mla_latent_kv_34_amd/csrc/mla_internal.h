@@ -114,6 +114,15 @@ hipError_t launch_v2_decode(const Layer& L, const void* pool, int num_pages, con
                             const void* q_rope, const void* w_uk, const void* w_uv, void* out,
                             void* ws, int n_wg, void* const* ev, hipStream_t s,
                             const void* c_new = nullptr, const void* k_new = nullptr);
+// projections from hidden states, then the decode step (proj.hip)
+size_t v2_hidden_workspace(const Layer& L, int batch, int n_wg, int d_model, int d_q);
+hipError_t launch_v2_decode_hidden(const Layer& L, const void* pool, int num_pages,
+                                   const int32_t* table, int max_pages, int batch,
+                                   const int32_t* seq_lens, int d_model, int d_q, const void* h,
+                                   const void* w_dkv, const void* w_kr, const void* w_dq,
+                                   const void* w_uq, const void* w_qr, const void* w_uk,
+                                   const void* w_uv, void* out, void* ws, int n_wg,
+                                   void* const* ev, hipStream_t s);
 size_t v2_prefill_workspace(int batch, int seq_len);
 hipError_t launch_v2_prefill(const Layer& L, const void* pool, int num_pages, const int32_t* table,
                              int max_pages, int batch, int seq_len, const void* q_nope,

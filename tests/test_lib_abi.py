@@ -82,3 +82,23 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(mla.LibraryMissing):
         _lib.load()
+
+
+def test_decode_hidden_rejections_on_host(lib):
+    """mla_decode_hidden validates before anything is launched: the generic
+    family is unsupported, K sizes must be positive multiples of 64, and the
+    workspace size query returns 0 for sizes it does not implement."""
+    cache = _lib._Cache(0x1000, 1, 1, 0x2000)   # never dereferenced
+    args = lambda d, dm, dq: (ctypes.byref(d), ctypes.byref(cache), 1, 0x3000, dm, dq,  # noqa: E731
+                              0x4000, 0x5000, 0x6000, 0x7000, 0x8000, 0x9000, 0xa000, 0xb000, 0xc000,
+                              0xd000, 1 << 30, 0, None, None)
+    tiny = _dims(n_heads=4, d_nope=16, d_rope=8, d_latent=32, dtype=1)
+    assert lib.mla_decode_hidden(*args(tiny, 128, 64)) == mla.MLA_ERR_UNSUPPORTED
+    assert b"V2" in lib.mla_last_error()
+    v2 = _dims()
+    assert lib.mla_decode_hidden(*args(v2, 5000, 1536)) == mla.MLA_ERR_INVALID_ARG
+    assert b"d_model" in lib.mla_last_error()
+    assert lib.mla_decode_hidden(*args(v2, 5120, 0)) == mla.MLA_ERR_INVALID_ARG
+    assert b"d_q" in lib.mla_last_error()
+    assert lib.mla_decode_hidden_workspace_size(ctypes.byref(tiny), 4, 0, 128, 64) == 0
+    assert lib.mla_decode_hidden_workspace_size(ctypes.byref(v2), 4, 0, 5000, 1536) == 0
