@@ -29,7 +29,8 @@ import torch
 __all__ = [
     "Dims", "TINY", "V2", "DecodeCase", "PrefillCase", "draw", "to_storage",
     "weights", "decode_case", "prefill_case", "ragged_lengths", "page_table",
-    "CONFIGS", "front_weights", "hidden", "HiddenCase", "hidden_case",
+    "CONFIGS", "front_weights", "hidden", "HiddenCase", "hidden_case", "ChunkCase",
+    "chunk_case",
 ]
 
 
@@ -238,6 +239,60 @@ def prefill_case(dims: Dims, batch: int, seq_len: int, seed: int = 0,
     table, npages = page_table(np.full(B, T), dims.page_size, seed, shuffle)
     return PrefillCase(dims, B, T, to_storage(q_c, dims), to_storage(q_r, dims),
                        to_storage(c, dims), to_storage(kr, dims), w_uk, w_uv, table, npages)
+
+
+@dataclass
+class ChunkCase:
+    """A prompt chunk of ``chunk_len`` tokens per sequence that continues
+    sequences whose first ``start[b]`` tokens are already cached.  ``c_all`` /
+    ``k_all`` hold every token of every sequence (sequence b uses rows
+    0 .. start[b] + chunk_len - 1; the rest is padding); the chunk's own rows
+    are start[b] .. start[b] + chunk_len - 1, its queries ``q_c`` / ``q_r``."""
+    dims: Dims
+    start: np.ndarray    # [B] int64
+    chunk_len: int
+    q_c: torch.Tensor    # [B, T, n_h, d_h^C]
+    q_r: torch.Tensor    # [B, T, n_h, d_h^R], pre-RoPE
+    c_all: torch.Tensor  # [B, max(start) + T, d_c]
+    k_all: torch.Tensor  # [B, max(start) + T, d_h^R], pre-RoPE
+    w_uk: torch.Tensor
+    w_uv: torch.Tensor
+    table: np.ndarray
+    num_pages: int
+
+    @property
+    def batch(self) -> int:
+        return len(self.start)
+
+    @property
+    def context(self) -> np.ndarray:
+        return self.start + self.chunk_len
+
+    def chunk_rows(self):
+        """(c_kv, k_r) of the chunk tokens, [B, T, d_c] and [B, T, d_h^R]."""
+        idx = torch.from_numpy(self.start[:, None] + np.arange(self.chunk_len)[None, :])
+        b = torch.arange(self.batch)[:, None]
+        return self.c_all[b, idx], self.k_all[b, idx]
+
+    def seq_rows(self, b: int):
+        """(c_kv, k_r) of every token of sequence b, prefix and chunk."""
+        n = int(self.context[b])
+        return self.c_all[b, :n], self.k_all[b, :n]
+
+
+def chunk_case(dims: Dims, start, chunk_len: int, seed: int = 0,
+               shuffle: bool = True) -> ChunkCase:
+    start = np.asarray(start, dtype=np.int64)
+    B, T = len(start), int(chunk_len)
+    S = int(start.max()) + T
+    q_c = draw((B, T, dims.n_heads, dims.d_nope), seed, _T_QC)
+    q_r = draw((B, T, dims.n_heads, dims.d_rope), seed, _T_QR)
+    c = draw((B, S, dims.d_latent), seed, _T_C)
+    kr = draw((B, S, dims.d_rope), seed, _T_KR)
+    w_uk, w_uv = weights(dims, seed)
+    table, npages = page_table(start + T, dims.page_size, seed, shuffle)
+    return ChunkCase(dims, start, T, to_storage(q_c, dims), to_storage(q_r, dims),
+                     to_storage(c, dims), to_storage(kr, dims), w_uk, w_uv, table, npages)
 
 
 # The five workloads of this hot path, by name.

@@ -57,7 +57,8 @@ import numpy as np
 
 __all__ = [
     "rope_frequencies", "rotate_pairs", "rope", "front_end",
-    "expand_heads", "decode_ref", "prefill_ref", "absorbed_decode_ref",
+    "expand_heads", "decode_ref", "prefill_ref", "prefill_chunk_ref",
+    "absorbed_decode_ref",
     "bf16_bits_rne", "f32_rne", "append_expected",
     "cache_elements_per_token", "kv_cache_bytes",
 ]
@@ -236,6 +237,50 @@ def prefill_ref(q_c, q_r, c_kv, k_r, w_uk, w_uv, *, base: float, scale: float = 
     s = (np.einsum("thr,hjr->htj", qc, kc) + np.einsum("thr,jr->htj", qr, kr)) * scale
     mask = np.arange(n)[None, :] > rows[:, None]                        # [R, n]
     s = np.where(mask[None, :, :], -np.inf, s)
+    p = _softmax_rows(s)                                                # [h, R, n]
+    o = np.einsum("htj,hjr->htr", p, vc)
+    return np.swapaxes(o, 0, 1)                                         # [R, h, d_C]
+
+
+def prefill_chunk_ref(q_c, q_r, c_kv, k_r, w_uk, w_uv, *, start: int, base: float,
+                      scale: float = None, rows=None, heads=None) -> np.ndarray:
+    """Causal attention of one prompt chunk over the sequence's latent cache.
+
+    The tech note's hybrid mode [what the KV cache stores]: the cache layout is
+    the latent one in both phases, and a prompt is processed by expanding the
+    latent rows into per-head keys and values (haowenji [section 7]: prompts
+    are compute-bound and are not absorbed).  A chunk of T tokens continues a
+    sequence whose first ``start`` tokens are already cached.
+
+    c_kv [start + T, d_c] and k_r [start + T, d_h^R] (pre-RoPE) hold the whole
+    sequence, the cached prefix first; q_c [T, n_h, d_h^C], q_r [T, n_h, d_h^R]
+    (pre-RoPE) are the chunk's queries.  Chunk row t sits at position
+    start + t and attends positions 0 .. start + t (tech note (4)), with
+    q = [q^C ; RoPE(q^R, start + t)], k_j = [W^UK c_j ; RoPE(k^R_j, j)],
+    v_j = W^UV c_j.  Returns o [len(rows), len(heads), d_h^C] in fp64.
+    """
+    q_c = np.asarray(q_c, dtype=np.float64)
+    q_r = np.asarray(q_r, dtype=np.float64)
+    c_kv = np.asarray(c_kv, dtype=np.float64)
+    k_r = np.asarray(k_r, dtype=np.float64)
+    T, n_h, d_nope = q_c.shape
+    d_rope = q_r.shape[-1]
+    rows = np.arange(T) if rows is None else np.asarray(rows)
+    sel = np.arange(n_h) if heads is None else np.asarray(heads)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_nope + d_rope)
+    pos = start + rows                                                  # query positions
+    n = int(pos.max()) + 1 if len(rows) else 0                          # keys any row can see
+    wk = np.asarray(w_uk, dtype=np.float64)[sel]
+    wv = np.asarray(w_uv, dtype=np.float64)[sel]
+    kc = expand_heads(c_kv[:n], wk)                                     # [h, n, d_C]
+    vc = expand_heads(c_kv[:n], wv)
+    kr = rope(k_r[:n], np.arange(n), base)                              # [n, d_R]
+    qc = q_c[rows][:, sel]                                              # [R, h, d_C]
+    qr = rope(q_r[rows][:, sel], pos[:, None], base)                    # [R, h, d_R]
+    s = (np.einsum("thr,hjr->htj", qc, kc) + np.einsum("thr,jr->htj", qr, kr)) * scale
+    later = np.arange(n)[None, :] > pos[:, None]                        # key after the query
+    s = np.where(later[None, :, :], -np.inf, s)
     p = _softmax_rows(s)                                                # [h, R, n]
     o = np.einsum("htj,hjr->htr", p, vc)
     return np.swapaxes(o, 0, 1)                                         # [R, h, d_C]
