@@ -59,6 +59,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches only")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill measurement")
+    ap.add_argument("--no-chunk", action="store_true", help="skip the chunked-prefill measurement")
     ap.add_argument("--no-hidden", action="store_true",
                     help="skip the decode-from-hidden-states measurement")
     ap.add_argument("--prefill-steps", type=int, default=10)
@@ -270,6 +271,10 @@ def main():
     if not args.no_prefill:
         pre = prefill_bench(mla, syn, dims, dev, args.prefill_steps)
 
+    chk = None
+    if not args.no_chunk:
+        chk = chunk_bench(mla, syn, dims, dev, args.prefill_steps)
+
     hid = None
     n_reps = len(reps)
     if not args.no_hidden:
@@ -320,6 +325,7 @@ def main():
         },
         "cpu_baseline": cpu,
         "prefill": pre,
+        "prefill_chunk": chk,
         "decode_hidden": hid,
     }
     print(json.dumps(line), flush=True)
@@ -464,6 +470,64 @@ def prefill_bench(mla, syn, dims, dev, steps: int):
     tflops = flop / (kern_ms * 1e-3) / 1e12
     return {"workload": "v2_prefill_2x4k: 2 prompts x 4096 tokens, causal, cache written",
             "value": round(B * T / (ms * 1e-3), 1), "unit": "prompt tokens/s",
+            "ms_per_call": round(ms, 4), "kernels_ms": round(kern_ms, 4),
+            "roofline": {"kernel": "expand + prefill_attn", "bound": "mfma",
+                         "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "algorithmic_flop": flop}}
+
+
+def chunk_bench(mla, syn, dims, dev, steps: int):
+    """Chunked prefill: the last 512-token chunk of two 4096-token prompts,
+    3584 positions already cached (append the chunk, expand K/V for all 4096
+    positions, causal attention of the chunk's rows): chunk tokens/s and the
+    MFMA fraction of the expansion + attention kernels."""
+    import numpy as np
+    import torch
+
+    print("[bench] chunked prefill 2 x (3584 + 512)", file=sys.stderr, flush=True)
+    P, T = 3584, 512
+    case = syn.chunk_case(syn.V2, [P, P], T, seed=0)
+    B, H, d = case.batch, case.dims.n_heads, case.dims
+    ctx = P + T
+    pool = torch.zeros((case.num_pages, d.page_size, d.row), dtype=d.torch_dtype, device=dev)
+    table = torch.from_numpy(case.table).to(dev)
+    mla.cache_append(dims, pool, table, torch.zeros(B, dtype=torch.int32, device=dev),
+                     case.c_all[:, :P].contiguous().to(dev), case.k_all[:, :P].contiguous().to(dev))
+    c_new, k_new = case.chunk_rows()
+    start = torch.from_numpy(case.start.astype(np.int32)).to(dev)
+    args = [case.q_c.to(dev), case.q_r.to(dev), c_new.contiguous().to(dev), k_new.contiguous().to(dev),
+            case.w_uk.to(dev), case.w_uv.to(dev)]
+    del case
+    ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    for e in ev:
+        e.record()
+    call, out = mla.prefill_chunk(dims, pool, table, start, *args, max_context=ctx, prepare=True)
+    call_t, _ = mla.prefill_chunk(dims, pool, table, start, *args, max_context=ctx, out=out,
+                                  timing_events=ev, prepare=True)
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        call()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    kern = []
+    for _ in range(steps):
+        call_t()
+        torch.cuda.synchronize()
+        kern.append(ev[0].elapsed_time(ev[1]))
+    kern_ms = float(np.mean(kern))
+    pairs = B * H * (T * P + T * (T + 1) // 2)            # causal (query, key) pairs
+    flop = pairs * 2 * (d.d_nope + d.d_rope + d.d_nope)    # scores + weighted sum
+    flop += 2 * B * ctx * d.d_latent * 2 * H * d.d_nope    # K^C and V^C of every position
+    tflops = flop / (kern_ms * 1e-3) / 1e12
+    return {"workload": "v2_chunk_2x(3584+512): 2 sequences, 3584 cached + 512-token chunk, causal, "
+                        "chunk rows written",
+            "value": round(B * T / (ms * 1e-3), 1), "unit": "chunk tokens/s",
             "ms_per_call": round(ms, 4), "kernels_ms": round(kern_ms, 4),
             "roofline": {"kernel": "expand + prefill_attn", "bound": "mfma",
                          "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,

@@ -197,6 +197,39 @@ mla_status mla_prefill(const mla_dims* dims, const mla_paged_cache* cache, int32
                        const void* w_uv, void* out, void* workspace, size_t workspace_bytes,
                        void* const* timing_events, void* stream);
 
+/* Bytes of device workspace mla_prefill_chunk needs (0 for invalid sizes). */
+size_t mla_prefill_chunk_workspace_size(const mla_dims* dims, int32_t batch, int32_t chunk_len,
+                                        int32_t max_context);
+
+/* Chunked prefill over an existing latent cache: every sequence b continues
+ * with chunk_len prompt tokens at positions start_pos[b] .. start_pos[b] +
+ * chunk_len - 1, its earlier positions already cached (by an earlier chunk,
+ * mla_prefill or decode steps).  The cache layout is the latent one in both
+ * phases and a prompt is processed by expanding it ("MLA low-rank attention"
+ * tech note [what the KV cache stores], the hybrid mode; "From LLaMA to
+ * DeepSeek [01]" [section 7]: prompts are compute-bound and not absorbed).
+ * Steps: append the chunk's rows (as mla_cache_append with start_pos), expand
+ * K^C = W^UK c and V^C = W^UV c per head for every position 0 .. start_pos[b]
+ * + chunk_len - 1 from the latent rows in the cache, and run causal attention:
+ * chunk row t attends positions 0 .. start_pos[b] + t with q = [q^C ;
+ * RoPE(q^R, start_pos[b] + t)] and k = [K^C ; cached RoPE(k^R, j)].
+ * start_pos: device int32 [batch]; the caller guarantees 0 <= start_pos[b]
+ *   and start_pos[b] + chunk_len <= max_context (the kernels clamp start_pos[b]
+ *   into that range, so a violation gives wrong results, not a fault).
+ * max_context: host int, bound on start_pos[b] + chunk_len; sizes the
+ *   workspace (keys are expanded into it for max_context positions per
+ *   sequence); the page table needs ceil(max_context / page_size) columns.
+ * q_nope, q_rope, c_kv, k_rope, out: as for mla_prefill with seq_len =
+ *   chunk_len (the chunk's tokens only).
+ * mla_prefill(..., seq_len, ...) is this call with start_pos[b] = 0 and
+ * max_context = seq_len.  timing_events as for mla_prefill.                 */
+mla_status mla_prefill_chunk(const mla_dims* dims, const mla_paged_cache* cache, int32_t batch,
+                             const int32_t* start_pos, int32_t chunk_len, int32_t max_context,
+                             const void* q_nope, const void* q_rope, const void* c_kv,
+                             const void* k_rope, const void* w_uk, const void* w_uv, void* out,
+                             void* workspace, size_t workspace_bytes, void* const* timing_events,
+                             void* stream);
+
 /* Static name of a status code. */
 const char* mla_status_string(mla_status status);
 

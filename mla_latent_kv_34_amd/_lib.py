@@ -24,7 +24,8 @@ MLA_BF16, MLA_F32 = 0, 1
 EXPORTED = (
     "mla_cache_append", "mla_decode_workspace_size", "mla_decode", "mla_decode_step",
     "mla_decode_hidden_workspace_size", "mla_decode_hidden",
-    "mla_prefill_workspace_size", "mla_prefill", "mla_status_string", "mla_last_error",
+    "mla_prefill_workspace_size", "mla_prefill", "mla_prefill_chunk_workspace_size",
+    "mla_prefill_chunk", "mla_status_string", "mla_last_error",
 )
 
 
@@ -115,6 +116,13 @@ def load() -> ctypes.CDLL:
     lib.mla_prefill.argtypes = [ctypes.POINTER(_Dims), ctypes.POINTER(_Cache), ctypes.c_int32, ctypes.c_int32,
                                 P, P, P, P, P, P, P, P, ctypes.c_size_t, P, P]
     lib.mla_prefill.restype = ctypes.c_int
+    lib.mla_prefill_chunk_workspace_size.argtypes = [ctypes.POINTER(_Dims), ctypes.c_int32, ctypes.c_int32,
+                                                     ctypes.c_int32]
+    lib.mla_prefill_chunk_workspace_size.restype = ctypes.c_size_t
+    lib.mla_prefill_chunk.argtypes = [ctypes.POINTER(_Dims), ctypes.POINTER(_Cache), ctypes.c_int32,
+                                      ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32] + \
+        [ctypes.c_void_p] * 8 + [ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    lib.mla_prefill_chunk.restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
     lib.mla_last_error.argtypes = []
@@ -398,6 +406,57 @@ def prefill(dims: Dims, pool: torch.Tensor, page_table: torch.Tensor, q_nope: to
     args.append(evs.ptr)
     call = _Prepared(lib.mla_prefill, args, keep=(d, cache, q_nope, q_rope, c_kv, k_rope, w_uk,
                                                    w_uv, out, workspace, evs))
+    if prepare:
+        return call, out
+    call(stream)
+    return out
+
+
+def prefill_chunk_workspace_size(dims: Dims, batch: int, chunk_len: int, max_context: int) -> int:
+    d = dims._c()
+    return int(load().mla_prefill_chunk_workspace_size(ctypes.byref(d), batch, chunk_len, max_context))
+
+
+def prefill_chunk(dims: Dims, pool: torch.Tensor, page_table: torch.Tensor, start_pos: torch.Tensor,
+                  q_nope: torch.Tensor, q_rope: torch.Tensor, c_kv: torch.Tensor, k_rope: torch.Tensor,
+                  w_uk: torch.Tensor, w_uv: torch.Tensor, max_context: int,
+                  out: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None,
+                  timing_events=None, prepare: bool = False):
+    """Chunked prefill over an existing latent cache (mla_prefill_chunk): chunk
+    row t of sequence b sits at position start_pos[b] + t and attends every
+    position up to its own.  start_pos: int32 [batch] on the device;
+    max_context bounds start_pos[b] + chunk_len.  Tensors as for prefill with
+    seq_len = chunk_len; timing_events and prepare as for decode()."""
+    lib = load()
+    cache = _cache(dims, pool, page_table)
+    dev = pool.device
+    B, T = q_nope.shape[0], q_nope.shape[1]
+    H = dims.n_heads
+    _need(q_nope, "q_nope", dims.dtype, (B, T, H, dims.d_nope), dev)
+    _need(q_rope, "q_rope", dims.dtype, (B, T, H, dims.d_rope), dev)
+    _need(c_kv, "c_kv", dims.dtype, (B, T, dims.d_latent), dev)
+    _need(k_rope, "k_rope", dims.dtype, (B, T, dims.d_rope), dev)
+    _need(w_uk, "w_uk", dims.dtype, (H, dims.d_nope, dims.d_latent), dev)
+    _need(w_uv, "w_uv", dims.dtype, (H, dims.d_nope, dims.d_latent), dev)
+    _need(start_pos, "start_pos", torch.int32, (B,), dev)
+    if page_table.shape[0] < B:
+        raise ValueError("page_table has fewer rows than the batch")
+    if out is None:
+        out = torch.empty((B, T, H, dims.d_nope), dtype=dims.dtype, device=dev)
+    _need(out, "out", dims.dtype, (B, T, H, dims.d_nope), dev)
+    need = prefill_chunk_workspace_size(dims, B, T, max_context)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    d = dims._c()
+    args = [ctypes.byref(d), ctypes.byref(cache), B, _ptr(start_pos), T, int(max_context), _ptr(q_nope),
+            _ptr(q_rope), _ptr(c_kv), _ptr(k_rope), _ptr(w_uk), _ptr(w_uv), _ptr(out), _ptr(workspace),
+            wbytes]
+    evs = _events(timing_events)
+    args.append(evs.ptr)
+    call = _Prepared(lib.mla_prefill_chunk, args, keep=(d, cache, start_pos, q_nope, q_rope, c_kv,
+                                                         k_rope, w_uk, w_uv, out, workspace, evs, pool,
+                                                         page_table))
     if prepare:
         return call, out
     call(stream)

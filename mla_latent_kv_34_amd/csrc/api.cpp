@@ -325,28 +325,47 @@ mla_status mla_decode_hidden(const mla_dims* dims, const mla_paged_cache* cache,
                   "decode from hidden states launch");
 }
 
+static size_t prefill_need(const mla::Layer& L, Family fam, int batch, int chunk_len, int max_context) {
+  return fam == Family::V2 ? mla::v2_prefill_workspace(batch, chunk_len, max_context)
+                           : mla::generic_prefill_workspace(L, batch, max_context);
+}
+
 size_t mla_prefill_workspace_size(const mla_dims* dims, int32_t batch, int32_t seq_len) {
   mla::Layer L;
   Family fam;
   if (check_dims(dims, &L, &fam) != MLA_OK || batch < 1 || seq_len < 1) return 0;
-  if (fam == Family::V2) return mla::v2_prefill_workspace(batch, seq_len);
-  return mla::generic_prefill_workspace(L, batch, seq_len);
+  return prefill_need(L, fam, batch, seq_len, seq_len);
 }
 
-mla_status mla_prefill(const mla_dims* dims, const mla_paged_cache* cache, int32_t batch,
-                       int32_t seq_len, const void* q_nope, const void* q_rope, const void* c_kv,
-                       const void* k_rope, const void* w_uk, const void* w_uv, void* out,
-                       void* workspace, size_t workspace_bytes, void* const* timing_events,
-                       void* stream) {
+size_t mla_prefill_chunk_workspace_size(const mla_dims* dims, int32_t batch, int32_t chunk_len,
+                                        int32_t max_context) {
+  mla::Layer L;
+  Family fam;
+  if (check_dims(dims, &L, &fam) != MLA_OK || batch < 1 || chunk_len < 1 || max_context < chunk_len)
+    return 0;
+  return prefill_need(L, fam, batch, chunk_len, max_context);
+}
+
+// Shared body of mla_prefill (start_pos NULL, max_context = seq_len) and
+// mla_prefill_chunk.
+static mla_status prefill_common(const mla_dims* dims, const mla_paged_cache* cache, int32_t batch,
+                                 const int32_t* start_pos, int32_t chunk_len, int32_t max_context,
+                                 const void* q_nope, const void* q_rope, const void* c_kv,
+                                 const void* k_rope, const void* w_uk, const void* w_uv, void* out,
+                                 void* workspace, size_t workspace_bytes,
+                                 void* const* timing_events, void* stream, const char* ws_name) {
   mla::Layer L;
   Family fam;
   MLA_TRY(check_dims(dims, &L, &fam));
   MLA_TRY(check_cache(cache));
-  if (batch < 1 || seq_len < 1) return fail(MLA_ERR_INVALID_ARG, "batch and seq_len must be >= 1");
-  if ((long long)cache->max_pages * L.page_size < seq_len)
-    return fail(MLA_ERR_INVALID_ARG, "page_table rows are too short for seq_len tokens");
-  if ((long long)batch * seq_len * L.n_heads > 0x7fffffffLL)
-    return fail(MLA_ERR_INVALID_ARG, "batch * seq_len * n_heads too large");
+  if (batch < 1 || chunk_len < 1) return fail(MLA_ERR_INVALID_ARG, "batch and the token count must be >= 1");
+  if (max_context < chunk_len) return fail(MLA_ERR_INVALID_ARG, "max_context must be >= chunk_len");
+  if ((long long)cache->max_pages * L.page_size < max_context)
+    return fail(MLA_ERR_INVALID_ARG, "page_table rows are too short for max_context tokens");
+  if ((long long)batch * chunk_len * L.n_heads > 0x7fffffffLL ||
+      (long long)batch * max_context * L.n_heads > 0x7fffffffLL)
+    return fail(MLA_ERR_INVALID_ARG, "batch * tokens * n_heads too large");
+  if (start_pos) MLA_TRY(check_idx(start_pos, "start_pos"));
   MLA_TRY(check_ptr(q_nope, "q_nope"));
   MLA_TRY(check_ptr(q_rope, "q_rope"));
   MLA_TRY(check_ptr(c_kv, "c_kv"));
@@ -354,27 +373,50 @@ mla_status mla_prefill(const mla_dims* dims, const mla_paged_cache* cache, int32
   MLA_TRY(check_ptr(w_uk, "w_uk"));
   MLA_TRY(check_ptr(w_uv, "w_uv"));
   MLA_TRY(check_ptr(out, "out"));
-  const size_t need = fam == Family::V2 ? mla::v2_prefill_workspace(batch, seq_len)
-                                        : mla::generic_prefill_workspace(L, batch, seq_len);
+  const size_t need = prefill_need(L, fam, batch, chunk_len, max_context);
   if (need > 0 && (!workspace || workspace_bytes < need))
-    return fail(MLA_ERR_WORKSPACE, "workspace smaller than mla_prefill_workspace_size()");
+    return fail(MLA_ERR_WORKSPACE, ws_name);
   if (need > 0) MLA_TRY(check_ptr(workspace, "workspace"));
   hipStream_t s = (hipStream_t)stream;
   g_err.clear();
-  // the prompt's latent rows go into the cache first; attention reads the
-  // rotated keys back from it
+  // the chunk's latent rows go into the cache first; the expansion and the
+  // attention read every position, prefix and chunk, back from it
   MLA_TRY(launched(mla::launch_append(L, cache->pool, cache->num_pages, cache->page_table,
-                                      cache->max_pages, batch, nullptr, seq_len, c_kv, k_rope, s),
+                                      cache->max_pages, batch, start_pos, chunk_len, c_kv, k_rope, s),
                    "prefill append launch"));
   if (fam == Family::V2)
     return launched(mla::launch_v2_prefill(L, cache->pool, cache->num_pages, cache->page_table,
-                                           cache->max_pages, batch, seq_len, q_nope, q_rope, c_kv,
-                                           w_uk, w_uv, out, workspace, timing_events, s),
+                                           cache->max_pages, batch, chunk_len, start_pos,
+                                           max_context, q_nope, q_rope, w_uk, w_uv, out, workspace,
+                                           timing_events, s),
                     "prefill launch");
   return launched(mla::launch_generic_prefill(L, cache->pool, cache->num_pages, cache->page_table,
-                                              cache->max_pages, batch, seq_len, q_nope, q_rope,
-                                              c_kv, w_uk, w_uv, out, workspace, timing_events, s),
+                                              cache->max_pages, batch, chunk_len, start_pos,
+                                              max_context, q_nope, q_rope, w_uk, w_uv, out,
+                                              workspace, timing_events, s),
                   "generic prefill launch");
+}
+
+mla_status mla_prefill(const mla_dims* dims, const mla_paged_cache* cache, int32_t batch,
+                       int32_t seq_len, const void* q_nope, const void* q_rope, const void* c_kv,
+                       const void* k_rope, const void* w_uk, const void* w_uv, void* out,
+                       void* workspace, size_t workspace_bytes, void* const* timing_events,
+                       void* stream) {
+  return prefill_common(dims, cache, batch, nullptr, seq_len, seq_len, q_nope, q_rope, c_kv, k_rope,
+                        w_uk, w_uv, out, workspace, workspace_bytes, timing_events, stream,
+                        "workspace smaller than mla_prefill_workspace_size()");
+}
+
+mla_status mla_prefill_chunk(const mla_dims* dims, const mla_paged_cache* cache, int32_t batch,
+                             const int32_t* start_pos, int32_t chunk_len, int32_t max_context,
+                             const void* q_nope, const void* q_rope, const void* c_kv,
+                             const void* k_rope, const void* w_uk, const void* w_uv, void* out,
+                             void* workspace, size_t workspace_bytes, void* const* timing_events,
+                             void* stream) {
+  if (!start_pos) return fail(MLA_ERR_INVALID_ARG, "start_pos is NULL");
+  return prefill_common(dims, cache, batch, start_pos, chunk_len, max_context, q_nope, q_rope, c_kv,
+                        k_rope, w_uk, w_uv, out, workspace, workspace_bytes, timing_events, stream,
+                        "workspace smaller than mla_prefill_chunk_workspace_size()");
 }
 
 }  // extern "C"

@@ -151,15 +151,34 @@ generic_decode_kernel(const void* __restrict__ pool, int num_pages, const int32_
   }
 }
 
-// K^C / V^C expansion for prefill: kv[(b*T + t)][2][n_heads][d_nope] in fp32.
+// A prefill call processes a chunk of T tokens per sequence: chunk row t of
+// sequence b sits at position P_b + t (P_b = start_pos[b] clamped to
+// [0, ctx - T]; NULL start_pos: 0) and attends positions 0 .. P_b + t, the
+// cached prefix included.
+__device__ __forceinline__ int generic_chunk_start(const int32_t* start_pos, int b, int T,
+                                                   int ctx) {
+  return start_pos ? min(max(start_pos[b], 0), ctx - T) : 0;
+}
+
+// K^C / V^C expansion for prefill, from the latent rows in the cache:
+// kv[(b*ctx + j)][2][n_heads][d_nope] in fp32 for positions j < P_b + T.
 template <bool BF16>
 __global__ void __launch_bounds__(kThreads)
-generic_expand_kernel(const void* __restrict__ c_kv, const void* __restrict__ w_uk,
-                      const void* __restrict__ w_uv, float* __restrict__ kv, int n_heads,
-                      int d_nope, int d_latent) {
-  const long long bt = blockIdx.x;
+generic_expand_kernel(const void* __restrict__ pool, int num_pages,
+                      const int32_t* __restrict__ table, int max_pages,
+                      const int32_t* __restrict__ start_pos, int T, int ctx,
+                      const void* __restrict__ w_uk, const void* __restrict__ w_uv,
+                      float* __restrict__ kv, int n_heads, int d_nope, int d_rope, int d_latent,
+                      int page_size) {
+  const long long bt = blockIdx.x;  // b * ctx + j
+  const int b = (int)(bt / ctx), j = (int)(bt % ctx);
+  if (j >= generic_chunk_start(start_pos, b, T, ctx) + T) return;
+  // a skipped page (id outside the pool) expands to zeros; its keys score -inf
+  const int page = table[(size_t)b * max_pages + j / page_size];
+  const bool ok = page >= 0 && page < num_pages;
+  const long long r0 = ((long long)(ok ? page : 0) * page_size + j % page_size) * (d_latent + d_rope);
   __shared__ float c[1024];
-  for (int i = threadIdx.x; i < d_latent; i += kThreads) c[i] = ld<BF16>(c_kv, bt * d_latent + i);
+  for (int i = threadIdx.x; i < d_latent; i += kThreads) c[i] = ok ? ld<BF16>(pool, r0 + i) : 0.f;
   __syncthreads();
   const int per = n_heads * d_nope;
   for (int o = threadIdx.x; o < 2 * per; o += kThreads) {
@@ -176,9 +195,9 @@ __global__ void __launch_bounds__(kThreads)
 generic_prefill_attn_kernel(const void* __restrict__ pool, int num_pages,
                             const int32_t* __restrict__ table, int max_pages,
                             const void* __restrict__ q_nope, const void* __restrict__ q_rope,
-                            const float* __restrict__ kv, void* __restrict__ out, int T,
-                            int n_heads, int d_nope, int d_rope, int d_latent, int page_size,
-                            float scale, double base) {
+                            const float* __restrict__ kv, const int32_t* __restrict__ start_pos,
+                            int ctx, void* __restrict__ out, int T, int n_heads, int d_nope,
+                            int d_rope, int d_latent, int page_size, float scale, double base) {
   __shared__ float q[512];
   __shared__ float o[256];
   __shared__ float sc[kThreads];
@@ -188,18 +207,19 @@ generic_prefill_attn_kernel(const void* __restrict__ pool, int num_pages,
   const long long bt = id / n_heads;
   const int t = (int)(bt % T);
   const int b = (int)(bt / T);
+  const int pos = generic_chunk_start(start_pos, b, T, ctx) + t;
   const int row = d_latent + d_rope;
   const int per = n_heads * d_nope;
   for (int r = threadIdx.x; r < d_nope; r += kThreads) q[r] = ld<BF16>(q_nope, id * d_nope + r);
   for (int k = threadIdx.x; k < d_rope / 2; k += kThreads) {
     double ra, rb;
     rope_pair_f64(ld<BF16>(q_rope, id * d_rope + 2 * k), ld<BF16>(q_rope, id * d_rope + 2 * k + 1),
-                  (double)t, k, d_rope, base, &ra, &rb);
+                  (double)pos, k, d_rope, base, &ra, &rb);
     q[d_nope + 2 * k] = (float)ra;
     q[d_nope + 2 * k + 1] = (float)rb;
   }
   __syncthreads();
-  const long long kvb = (long long)b * T;
+  const long long kvb = (long long)b * ctx;
   auto score = [&](int j) -> float {
     const int pi = j / page_size;
     const int page = pi < max_pages ? table[(size_t)b * max_pages + pi] : -1;
@@ -213,7 +233,7 @@ generic_prefill_attn_kernel(const void* __restrict__ pool, int num_pages,
   };
   auto value = [&](int j, int r) -> float { return kv[(kvb + j) * 2 * per + per + (size_t)h * d_nope + r]; };
   float l_run;
-  attend(t + 1, d_nope, score, value, o, sc, red, &l_run);
+  attend(pos + 1, d_nope, score, value, o, sc, red, &l_run);
   __syncthreads();
   const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
   for (int r = threadIdx.x; r < d_nope; r += kThreads) st<BF16>(out, id * d_nope + r, o[r] * inv);
@@ -247,34 +267,37 @@ hipError_t launch_generic_decode(const Layer& L, const void* pool, int num_pages
   return mark(ev, 1, s);
 }
 
-size_t generic_prefill_workspace(const Layer& L, int batch, int seq_len) {
-  return align256((size_t)batch * seq_len * 2 * L.n_heads * L.d_nope * sizeof(float));
+size_t generic_prefill_workspace(const Layer& L, int batch, int max_context) {
+  return align256((size_t)batch * max_context * 2 * L.n_heads * L.d_nope * sizeof(float));
 }
 
 hipError_t launch_generic_prefill(const Layer& L, const void* pool, int num_pages,
-                                  const int32_t* table, int max_pages, int batch, int seq_len,
-                                  const void* q_nope, const void* q_rope, const void* c_kv,
-                                  const void* w_uk, const void* w_uv, void* out, void* ws,
-                                  void* const* ev, hipStream_t s) {
-  const long long bt = (long long)batch * seq_len;
-  const long long blocks = bt * L.n_heads;
-  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+                                  const int32_t* table, int max_pages, int batch, int chunk_len,
+                                  const int32_t* start_pos, int max_context, const void* q_nope,
+                                  const void* q_rope, const void* w_uk, const void* w_uv,
+                                  void* out, void* ws, void* const* ev, hipStream_t s) {
+  const int T = chunk_len, ctx = max_context;
+  const long long rows = (long long)batch * ctx;
+  const long long blocks = (long long)batch * T * L.n_heads;
+  if (blocks > 0x7fffffffLL || rows > 0x7fffffffLL) return hipErrorInvalidValue;
   float* kv = (float*)ws;
   if (L.bf16) {
-    hipLaunchKernelGGL(generic_expand_kernel<true>, dim3((unsigned)bt), dim3(kThreads), 0, s, c_kv,
-                       w_uk, w_uv, kv, L.n_heads, L.d_nope, L.d_latent);
+    hipLaunchKernelGGL(generic_expand_kernel<true>, dim3((unsigned)rows), dim3(kThreads), 0, s,
+                       pool, num_pages, table, max_pages, start_pos, T, ctx, w_uk, w_uv, kv,
+                       L.n_heads, L.d_nope, L.d_rope, L.d_latent, L.page_size);
     if (mark(ev, 0, s) != hipSuccess) return hipErrorInvalidValue;
     hipLaunchKernelGGL(generic_prefill_attn_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0,
-                       s, pool, num_pages, table, max_pages, q_nope, q_rope, kv, out, seq_len,
-                       L.n_heads, L.d_nope, L.d_rope, L.d_latent, L.page_size, L.scale,
+                       s, pool, num_pages, table, max_pages, q_nope, q_rope, kv, start_pos, ctx,
+                       out, T, L.n_heads, L.d_nope, L.d_rope, L.d_latent, L.page_size, L.scale,
                        L.rope_base);
   } else {
-    hipLaunchKernelGGL(generic_expand_kernel<false>, dim3((unsigned)bt), dim3(kThreads), 0, s, c_kv,
-                       w_uk, w_uv, kv, L.n_heads, L.d_nope, L.d_latent);
+    hipLaunchKernelGGL(generic_expand_kernel<false>, dim3((unsigned)rows), dim3(kThreads), 0, s,
+                       pool, num_pages, table, max_pages, start_pos, T, ctx, w_uk, w_uv, kv,
+                       L.n_heads, L.d_nope, L.d_rope, L.d_latent, L.page_size);
     if (mark(ev, 0, s) != hipSuccess) return hipErrorInvalidValue;
     hipLaunchKernelGGL(generic_prefill_attn_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), 0,
-                       s, pool, num_pages, table, max_pages, q_nope, q_rope, kv, out, seq_len,
-                       L.n_heads, L.d_nope, L.d_rope, L.d_latent, L.page_size, L.scale,
+                       s, pool, num_pages, table, max_pages, q_nope, q_rope, kv, start_pos, ctx,
+                       out, T, L.n_heads, L.d_nope, L.d_rope, L.d_latent, L.page_size, L.scale,
                        L.rope_base);
   }
   const hipError_t e = hipGetLastError();

@@ -97,12 +97,16 @@ hipError_t launch_generic_decode(const Layer& L, const void* pool, int num_pages
                                  const int32_t* seq_lens, const void* q_nope, const void* q_rope,
                                  const void* w_uk, const void* w_uv, void* out, void* ws,
                                  void* const* ev, hipStream_t s);
-size_t generic_prefill_workspace(const Layer& L, int batch, int seq_len);
+// Prefill of a chunk of chunk_len tokens per sequence at positions
+// start_pos[b] .. start_pos[b] + chunk_len - 1 (NULL start_pos: 0) over the
+// latent rows already in the cache (the chunk's own rows included);
+// max_context bounds start_pos[b] + chunk_len and sizes the workspace.
+size_t generic_prefill_workspace(const Layer& L, int batch, int max_context);
 hipError_t launch_generic_prefill(const Layer& L, const void* pool, int num_pages,
-                                  const int32_t* table, int max_pages, int batch, int seq_len,
-                                  const void* q_nope, const void* q_rope, const void* c_kv,
-                                  const void* w_uk, const void* w_uv, void* out, void* ws,
-                                  void* const* ev, hipStream_t s);
+                                  const int32_t* table, int max_pages, int batch, int chunk_len,
+                                  const int32_t* start_pos, int max_context, const void* q_nope,
+                                  const void* q_rope, const void* w_uk, const void* w_uv,
+                                  void* out, void* ws, void* const* ev, hipStream_t s);
 
 // MFMA family for the V2 sizes
 size_t v2_decode_workspace(int batch, int n_wg);
@@ -123,12 +127,13 @@ hipError_t launch_v2_decode_hidden(const Layer& L, const void* pool, int num_pag
                                    const void* w_uq, const void* w_qr, const void* w_uk,
                                    const void* w_uv, void* out, void* ws, int n_wg,
                                    void* const* ev, hipStream_t s);
-size_t v2_prefill_workspace(int batch, int seq_len);
+// chunked prefill as launch_generic_prefill (prefill_v2.hip)
+size_t v2_prefill_workspace(int batch, int chunk_len, int max_context);
 hipError_t launch_v2_prefill(const Layer& L, const void* pool, int num_pages, const int32_t* table,
-                             int max_pages, int batch, int seq_len, const void* q_nope,
-                             const void* q_rope, const void* c_kv, const void* w_uk,
-                             const void* w_uv, void* out, void* ws, void* const* ev,
-                             hipStream_t s);
+                             int max_pages, int batch, int chunk_len, const int32_t* start_pos,
+                             int max_context, const void* q_nope, const void* q_rope,
+                             const void* w_uk, const void* w_uv, void* out, void* ws,
+                             void* const* ev, hipStream_t s);
 
 // Record timing event ev[i] (a hipEvent_t) on s when ev is non-null.
 static inline hipError_t mark(void* const* ev, int i, hipStream_t s) {

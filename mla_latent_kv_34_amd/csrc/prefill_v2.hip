@@ -6,18 +6,25 @@
 //   K^C_i = C W^UK_i^T,  V^C_i = C W^UV_i^T                 (expand, MFMA GEMM)
 //   s_ti  = ([q^C_ti ; RoPE(q^R_ti, t)] . [K^C_ij ; RoPE(k^R_j, j)]) / sqrt(192)
 //   o_ti  = sum_{j <= t} softmax_j(s_ti) V^C_ij             (prefill_attn)
-// The rotated k^R rows are read back from the latent cache, which the bulk
-// append has written for positions 0..T-1 before these kernels run.
+// Both the latent rows C and the rotated k^R rows are read back from the
+// latent cache, which the bulk append has written before these kernels run.
 //
-// Workspace (per prompt b and head h, T rounded up to Tp = 64 * ceil(T/64)):
-//   rope  [T][32] (cos, sin) of the query rotation angles (fp64, stored fp32)
+// A call processes a chunk of T prompt tokens per sequence: chunk row t of
+// prompt b sits at position P_b + t, where the cache already holds positions
+// 0 .. P_b - 1 (the tech note [what the KV cache stores]: one latent layout,
+// expanded for prompts), and attends positions 0 .. P_b + t.  A whole prompt
+// is the chunk with P_b = 0.  Keys are expanded for every position of the
+// sequence, prefix included; ctx >= P_b + T bounds the positions.
+//
+// Workspace (per prompt b and head h, ctx rounded up to Tp = 64 * ceil(ctx/64)):
+//   rope  [b][T][32] (cos, sin) of the query rotation angles (fp64, stored fp32)
 //   K^C   [b][h][Tp][128] bf16, the 128 dims of every 16-dim group stored in
 //         the order 0-3, 8-11, 4-7, 12-15 (the k-slot order of the MFMA result
 //         layout, so the expansion writes 16-byte pieces; the query is read in
 //         the same order, which leaves every dot product unchanged)
 //   V^T   [b][h][128][Tp] bf16, keys in the same order within 16-key groups,
 //         so one 16-byte LDS read gives a lane the 8 keys its probabilities
-//         cover; rows past T hold zeros.
+//         cover; rows past P_b + T hold zeros.
 #include <type_traits>
 
 #include "mla_internal.h"
@@ -72,30 +79,40 @@ __device__ __forceinline__ void dma16(const void* src, char* lds_block) {
                                    0, 0);
 }
 
+// First position P_b of prompt b's chunk: start_pos[b] clamped to
+// [0, ctx - T] so every access stays inside the workspace (NULL: 0).
+__device__ __forceinline__ int chunk_start(const int32_t* start_pos, int b, int T, int ctx) {
+  return start_pos ? min(max(start_pos[b], 0), ctx - T) : 0;
+}
+
 // ---------------------------------------------------------------------------
-// rope_table: tab[t][k] = (cos, sin) of t * base^(-2k/64), computed in fp64
-// and stored in fp32 (the rotated query is rounded to bf16 afterwards).
+// rope_table: tab[b][t][k] = (cos, sin) of (P_b + t) * base^(-2k/64),
+// computed in fp64 and stored in fp32 (the rotated query is rounded to bf16
+// afterwards).
 // ---------------------------------------------------------------------------
-__global__ void rope_table_kernel(int T, double base, float2* __restrict__ tab) {
+__global__ void rope_table_kernel(int B, int T, const int32_t* __restrict__ start_pos, int ctx,
+                                  double base, float2* __restrict__ tab) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= T * (DR / 2)) return;
-  const int t = i / (DR / 2), k = i % (DR / 2);
+  if (i >= B * T * (DR / 2)) return;
+  const int bt = i / (DR / 2), k = i % (DR / 2);
+  const int b = bt / T, t = bt % T;
+  const int pos = chunk_start(start_pos, b, T, ctx) + t;
   const double theta = pow(base, -2.0 * (double)k / (double)DR);
-  const double ang = __dmul_rn((double)t, theta);
+  const double ang = __dmul_rn((double)pos, theta);
   double s, c;
   sincos(ang, &s, &c);
   tab[i] = make_float2((float)c, (float)s);
 }
 
 // ---------------------------------------------------------------------------
-// expand: one workgroup of 8 waves (two per SIMD) per (head h, 256-token tile
-// of prompt b).  Waves 0-3 compute K^C for tokens 64w..64w+63 of the tile as
+// expand: one workgroup of 8 waves (two per SIMD) per (head h, 256-position
+// tile of prompt b); tiles at or past P_b + T exit at once.  Waves 0-3 compute K^C for tokens 64w..64w+63 of the tile as
 // K^T = W^UK_h C^T (rows = key dims, so a lane ends with 8 key dims of one
 // token in k-slot order); waves 4-7 compute V = C W^UV_h^T for the same token
 // blocks (rows = tokens, so a lane ends with 8 tokens of one value dim).  The
 // latent dimension runs in 8 stages of 64 columns, double-buffered in LDS with
-// direct-to-LDS loads: C rows of the tile [256][64] then W^UK_h and W^UV_h
-// rows [256][64], 128 bytes per row.  Two waves per SIMD keep the MFMA pipe
+// direct-to-LDS loads: C rows of the tile [256][64] (from the cache pages)
+// then W^UK_h and W^UV_h rows [256][64], 128 bytes per row.  Two waves per SIMD keep the MFMA pipe
 // fed while the other waits for its stage.
 // ---------------------------------------------------------------------------
 constexpr int EX_TOK = 256;
@@ -106,13 +123,17 @@ constexpr int EX_DMA = EX_STAGEB / 1024 / EX_NW;  // 8 one-KiB loads per wave pe
 constexpr int EX_CU = EX_CB / 16;          // 16-byte units of C per stage
 
 __global__ void __launch_bounds__(64 * EX_NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
-expand_kernel(const uint16_t* __restrict__ c_kv, const uint16_t* __restrict__ w_uk,
-              const uint16_t* __restrict__ w_uv, int B, int T, int tp, int nt,
-              uint16_t* __restrict__ kc, uint16_t* __restrict__ vt) {
+expand_kernel(const char* __restrict__ pool, int num_pages, const int32_t* __restrict__ table,
+              int max_pages, const int32_t* __restrict__ start_pos,
+              const uint16_t* __restrict__ w_uk, const uint16_t* __restrict__ w_uv, int B, int T,
+              int ctx, int tp, int nt, uint16_t* __restrict__ kc, uint16_t* __restrict__ vt) {
   __shared__ __attribute__((aligned(1024))) char lds[2 * EX_STAGEB];
   const int ttiles = B * nt;
   const int h = blockIdx.x / ttiles, tile = blockIdx.x % ttiles;
   const int b = tile / nt, t0 = (tile % nt) * EX_TOK;
+  const int n_pos = chunk_start(start_pos, b, T, ctx) + T;  // positions of prompt b
+  if (t0 >= n_pos) return;  // uniform: no key of this tile is ever read
+  const int32_t* trow = table + (size_t)b * max_pages;
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int g = lane >> 5, n = lane & 31;
 
@@ -124,8 +145,10 @@ expand_kernel(const uint16_t* __restrict__ c_kv, const uint16_t* __restrict__ w_
     const int u = (EX_NW * m + wave) * 64 + lane;
     if (m < EX_CU / (64 * EX_NW)) {
       const int r = u >> 3, c = (u & 7) ^ swz8(u >> 3);
-      const int t = min(t0 + r, T - 1);
-      src[m] = (const char*)(c_kv + ((size_t)b * T + t) * DL) + 16 * c;
+      const int t = min(t0 + r, n_pos - 1);
+      int page = trow[t / PS];
+      if (page < 0 || page >= num_pages) page = 0;  // stay in bounds on a bad table
+      src[m] = pool + (size_t)page * TILEB + (size_t)(t % PS) * ROWB + 16 * c;
     } else {
       const int v = u - EX_CU, r = v >> 3, c = (v & 7) ^ swz8(v >> 3);
       const uint16_t* w = r < DC ? w_uk + ((size_t)h * DC + r) * DL
@@ -188,7 +211,7 @@ expand_kernel(const uint16_t* __restrict__ c_kv, const uint16_t* __restrict__ w_
             if (t >= tp) continue;
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-              v[e] = t < T ? (__bf16)agpr_read(acc[4 * i + j][8 * hh + e]) : (__bf16)0.f;
+              v[e] = t < n_pos ? (__bf16)agpr_read(acc[4 * i + j][8 * hh + e]) : (__bf16)0.f;
             *(bf16x8*)(kc + (bh * tp + t) * DC + 32 * j + 16 * hh + 8 * g) = v;
           } else {
             // value dim 32j + n; stored key positions p0 .. p0+7 of the tile
@@ -197,7 +220,7 @@ expand_kernel(const uint16_t* __restrict__ c_kv, const uint16_t* __restrict__ w_
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
               const int t = t0 + tb + 32 * i + 16 * hh + 8 * (e >> 2) + 4 * g + (e & 3);
-              v[e] = t < T ? (__bf16)agpr_read(acc[4 * i + j][8 * hh + e]) : (__bf16)0.f;
+              v[e] = t < n_pos ? (__bf16)agpr_read(acc[4 * i + j][8 * hh + e]) : (__bf16)0.f;
             }
             *(bf16x8*)(vt + (bh * DC + 32 * j + n) * tp + p0) = v;
           }
@@ -208,8 +231,8 @@ expand_kernel(const uint16_t* __restrict__ c_kv, const uint16_t* __restrict__ w_
 }
 
 // ---------------------------------------------------------------------------
-// prefill_attn: one workgroup per (prompt b, head h, 128-query block); wave v
-// owns queries 32v..32v+31 of the block.  Key tiles of 64 (one cache page)
+// prefill_attn: one workgroup per (prompt b, head h, 128-query block of the
+// chunk); wave v owns chunk rows 32v..32v+31 of the block.  Key tiles of 64 (one cache page)
 // are double-buffered in LDS as four regions of 128-byte rows, each filled by
 // direct-to-LDS loads from one source: K^C dims 0-63 and 64-127 [64 keys],
 // the rotated k^R from the cache page [64 keys], and V^T [128 dims][64 keys].
@@ -229,18 +252,21 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
 prefill_attn_kernel(const char* __restrict__ pool, int num_pages, const int32_t* __restrict__ table,
                     int max_pages, const uint16_t* __restrict__ q_nope,
                     const uint16_t* __restrict__ q_rope, const float2* __restrict__ rope_tab,
-                    const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vt, int B, int T,
-                    int tp, int nqb, float sc_log2, uint16_t* __restrict__ out) {
+                    const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vt,
+                    const int32_t* __restrict__ start_pos, int B, int T, int ctx, int tp, int nqb,
+                    float sc_log2, uint16_t* __restrict__ out) {
   __shared__ __attribute__((aligned(1024))) char lds[2 * STAGEB];
   const int L = logical_of_launched(blockIdx.x, B * H * nqb);
   const int bh = L / nqb, qb = nqb - 1 - L % nqb;  // longest query blocks first
   const int b = bh / H, h = bh % H;
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int g = lane >> 5, n = lane & 31;
-  const int q0 = qb * QB + 32 * wave;       // first query of this wave
-  const int tq = q0 + n;                    // this lane's query
-  const int lim = min(tq, T - 1);           // keys <= lim are visible to it
-  const int lim_lo = min(q0, T - 1), lim_hi = min(q0 + 31, T - 1);
+  const int P = chunk_start(start_pos, b, T, ctx);  // position of chunk row 0
+  const int q0 = qb * QB + 32 * wave;       // first chunk row of this wave
+  const int tq = q0 + n;                    // this lane's chunk row
+  const int row = min(tq, T - 1);
+  const int lim = P + row;                  // keys at positions <= lim are visible to it
+  const int lim_lo = P + min(q0, T - 1), lim_hi = P + min(q0 + 31, T - 1);
 
   // ---- query fragments: B operand of S^T = K Q^T, 8 dims per lane per
   // k-step.  Each lane builds its 96 bf16 (K^C dims in k-slot order
@@ -250,9 +276,9 @@ prefill_attn_kernel(const char* __restrict__ pool, int num_pages, const int32_t*
   bf16x8 q[12];
   {
     char* qs = lds + (wave * 64 + lane) * 192;  // 12 fragments of 16 bytes
-    const uint16_t* qc = q_nope + (((size_t)b * T + lim) * H + h) * DC;
-    const uint16_t* qr = q_rope + (((size_t)b * T + lim) * H + h) * DR;
-    const float2* cs = rope_tab + (size_t)lim * (DR / 2) + 4 * g;
+    const uint16_t* qc = q_nope + (((size_t)b * T + row) * H + h) * DC;
+    const uint16_t* qr = q_rope + (((size_t)b * T + row) * H + h) * DR;
+    const float2* cs = rope_tab + ((size_t)b * T + row) * (DR / 2) + 4 * g;
     // every load first, so the staging costs one memory round trip
     uint2 lo[8], hi[8];
     uint4 rr[4];
@@ -338,7 +364,7 @@ prefill_attn_kernel(const char* __restrict__ pool, int num_pages, const int32_t*
   for (int d = 0; d < 4; ++d) o[d] = (f32x16){};
   float m_run = -INFINITY, l_part = 0.f;
 
-  const int ntile = min(tp / PS, (qb * QB + QB - 1) / PS + 1);
+  const int ntile = (P + min(qb * QB + QB - 1, T - 1)) / PS + 1;  // <= tp / PS
   issue(0, page_of(0));
   for (int kt = 0; kt < ntile; ++kt) {
     const int pnext = kt + 1 < ntile ? page_of(kt + 1) : 0;
@@ -429,10 +455,10 @@ prefill_attn_kernel(const char* __restrict__ pool, int num_pages, const int32_t*
 struct PfLayout {
   size_t rope, kc, vt, total;
   int tp;
-  PfLayout(int B, int T) {
-    tp = (T + PS - 1) / PS * PS;
+  PfLayout(int B, int T, int ctx) {
+    tp = (ctx + PS - 1) / PS * PS;
     rope = 0;
-    kc = align256(rope + (size_t)T * (DR / 2) * sizeof(float2));
+    kc = align256(rope + (size_t)B * T * (DR / 2) * sizeof(float2));
     vt = align256(kc + (size_t)B * H * tp * DC * 2);
     total = align256(vt + (size_t)B * H * DC * tp * 2);
   }
@@ -440,36 +466,37 @@ struct PfLayout {
 
 }  // namespace v2p
 
-size_t v2_prefill_workspace(int batch, int seq_len) {
-  return v2p::PfLayout(batch, seq_len).total;
+size_t v2_prefill_workspace(int batch, int chunk_len, int max_context) {
+  return v2p::PfLayout(batch, chunk_len, max_context).total;
 }
 
 hipError_t launch_v2_prefill(const Layer& L, const void* pool, int num_pages, const int32_t* table,
-                             int max_pages, int batch, int seq_len, const void* q_nope,
-                             const void* q_rope, const void* c_kv, const void* w_uk,
-                             const void* w_uv, void* out, void* ws, void* const* ev,
-                             hipStream_t s) {
+                             int max_pages, int batch, int chunk_len, const int32_t* start_pos,
+                             int max_context, const void* q_nope, const void* q_rope,
+                             const void* w_uk, const void* w_uv, void* out, void* ws,
+                             void* const* ev, hipStream_t s) {
   using namespace v2p;
-  const int B = batch, T = seq_len;
-  const PfLayout lay(B, T);
+  const int B = batch, T = chunk_len, ctx = max_context;
+  const PfLayout lay(B, T, ctx);
   char* w = (char*)ws;
   float2* tab = (float2*)(w + lay.rope);
   uint16_t* kc = (uint16_t*)(w + lay.kc);
   uint16_t* vt = (uint16_t*)(w + lay.vt);
   hipError_t e = mark(ev, 0, s);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((T * (DR / 2) + 255) / 256)), dim3(256), 0,
-                     s, T, L.rope_base, tab);
-  const int nt = (T + EX_TOK - 1) / EX_TOK;
+  hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((B * T * (DR / 2) + 255) / 256)),
+                     dim3(256), 0, s, B, T, start_pos, ctx, L.rope_base, tab);
+  const int nt = (ctx + EX_TOK - 1) / EX_TOK;
   hipLaunchKernelGGL(expand_kernel, dim3((unsigned)(H * B * nt)), dim3(64 * EX_NW), 0, s,
-                     (const uint16_t*)c_kv, (const uint16_t*)w_uk, (const uint16_t*)w_uv, B, T,
-                     lay.tp, nt, kc, vt);
+                     (const char*)pool, num_pages, table, max_pages, start_pos,
+                     (const uint16_t*)w_uk, (const uint16_t*)w_uv, B, T, ctx, lay.tp, nt, kc, vt);
   const int nqb = (T + QB - 1) / QB;
   const float sc_log2 = L.scale * 1.4426950408889634f;
   hipLaunchKernelGGL(prefill_attn_kernel, dim3((unsigned)(B * H * nqb)), dim3(256), 0, s,
                      (const char*)pool, num_pages, table, max_pages, (const uint16_t*)q_nope,
                      (const uint16_t*)q_rope, (const float2*)tab, (const uint16_t*)kc,
-                     (const uint16_t*)vt, B, T, lay.tp, nqb, sc_log2, (uint16_t*)out);
+                     (const uint16_t*)vt, start_pos, B, T, ctx, lay.tp, nqb, sc_log2,
+                     (uint16_t*)out);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   return mark(ev, 1, s);

@@ -102,3 +102,30 @@ def test_decode_hidden_rejections_on_host(lib):
     assert b"d_q" in lib.mla_last_error()
     assert lib.mla_decode_hidden_workspace_size(ctypes.byref(tiny), 4, 0, 128, 64) == 0
     assert lib.mla_decode_hidden_workspace_size(ctypes.byref(v2), 4, 0, 5000, 1536) == 0
+
+
+def test_prefill_chunk_rejections_on_host(lib):
+    """mla_prefill_chunk validates before anything is launched: start_pos is
+    required, max_context must cover the chunk and fit the page table, and the
+    workspace must cover max_context positions per sequence."""
+    d = _dims(n_heads=4, d_nope=16, d_rope=8, d_latent=32, dtype=1)
+    cache = _lib._Cache(0x1000, 4, 2, 0x2000)   # 2 pages of 64 positions per sequence
+    def call(start, T, ctx, ws_bytes=1 << 30):
+        return lib.mla_prefill_chunk(ctypes.byref(d), ctypes.byref(cache), 1, start, T, ctx, 0x4000, 0x5000,
+                                     0x6000, 0x7000, 0x8000, 0x9000, 0xa000, 0xb000, ws_bytes, None, None)
+    assert call(None, 8, 64) == mla.MLA_ERR_INVALID_ARG and b"start_pos" in lib.mla_last_error()
+    assert call(0x3000, 8, 7) == mla.MLA_ERR_INVALID_ARG and b"max_context" in lib.mla_last_error()
+    assert call(0x3000, 8, 129) == mla.MLA_ERR_INVALID_ARG and b"page_table" in lib.mla_last_error()
+    assert call(0x3002, 8, 64) == mla.MLA_ERR_INVALID_ARG and b"aligned" in lib.mla_last_error()
+    need = lib.mla_prefill_chunk_workspace_size(ctypes.byref(d), 1, 8, 100)
+    assert need == 100 * 2 * 4 * 16 * 4                  # fp32 K^C and V^C for 100 positions
+    assert call(0x3000, 8, 100, need - 1) == mla.MLA_ERR_WORKSPACE
+    assert lib.mla_prefill_chunk_workspace_size(ctypes.byref(d), 1, 8, 7) == 0
+    # a whole prompt is the chunk at start 0 with max_context = its length
+    assert lib.mla_prefill_workspace_size(ctypes.byref(d), 3, 50) == \
+        lib.mla_prefill_chunk_workspace_size(ctypes.byref(d), 3, 50, 50)
+    v2 = _dims()
+    assert lib.mla_prefill_workspace_size(ctypes.byref(v2), 2, 4096) == \
+        lib.mla_prefill_chunk_workspace_size(ctypes.byref(v2), 2, 4096, 4096)
+    assert lib.mla_prefill_chunk_workspace_size(ctypes.byref(v2), 2, 512, 4096) > \
+        lib.mla_prefill_chunk_workspace_size(ctypes.byref(v2), 2, 512, 512)
