@@ -29,7 +29,7 @@ import torch
 __all__ = [
     "Dims", "TINY", "V2", "DecodeCase", "PrefillCase", "draw", "to_storage",
     "weights", "decode_case", "prefill_case", "ragged_lengths", "page_table",
-    "CONFIGS", "front_weights", "hidden", "HiddenCase", "hidden_case", "ChunkCase",
+    "CONFIGS", "front_weights", "out_weight", "hidden", "HiddenCase", "hidden_case", "ChunkCase",
     "chunk_case",
 ]
 
@@ -67,6 +67,7 @@ V2 = Dims(n_heads=128, d_nope=128, d_rope=64, d_latent=512, d_cq=1536, d_model=5
 # tensor ids of the per-tensor random streams
 _T_QC, _T_QR, _T_C, _T_KR, _T_WUK, _T_WUV, _T_LENS, _T_PERM = range(1, 9)
 _T_H, _T_WDKV, _T_WKR, _T_WDQ, _T_WUQ, _T_WQR = range(9, 15)
+_T_WO = 15
 
 
 def draw(shape, seed: int, tensor_id: int, std: float = 1.0) -> np.ndarray:
@@ -101,6 +102,12 @@ def front_weights(dims: Dims, seed: int = 0):
               (_T_WDQ, (dq, d), d), (_T_WUQ, (dims.n_heads * dims.d_nope, dq), dq),
               (_T_WQR, (dims.n_heads * dims.d_rope, dq), dq))
     return tuple(to_storage(draw(shp, seed, tid, 1.0 / np.sqrt(fan)), dims) for tid, shp, fan in shapes)
+
+
+def out_weight(dims: Dims, seed: int = 0) -> torch.Tensor:
+    """W^O [d, n_h d_h^C] (out x in), N(0, 1/fan_in) (storage tensor)."""
+    fan = dims.n_heads * dims.d_nope
+    return to_storage(draw((dims.d_model, fan), seed, _T_WO, 1.0 / np.sqrt(fan)), dims)
 
 
 def hidden(batch: int, dims: Dims, seed: int = 0) -> torch.Tensor:

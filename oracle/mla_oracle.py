@@ -56,7 +56,7 @@ import math
 import numpy as np
 
 __all__ = [
-    "rope_frequencies", "rotate_pairs", "rope", "front_end",
+    "rope_frequencies", "rotate_pairs", "rope", "front_end", "output_proj",
     "expand_heads", "decode_ref", "prefill_ref", "prefill_chunk_ref",
     "absorbed_decode_ref",
     "bf16_bits_rne", "f32_rne", "append_expected",
@@ -135,6 +135,18 @@ def front_end(h, w_dkv, w_kr, w_dq, w_uq, w_qr, *, n_heads: int):
     k_r = h @ f(w_kr).T                                                  # [..., d_R]
     lead = h.shape[:-1]
     return (c_kv, k_r, q_c.reshape(lead + (n_heads, -1)), q_r.reshape(lead + (n_heads, -1)))
+
+
+def output_proj(o, w_o):
+    """The projection after the attention (tech note [(4) attention and output]):
+    u = W^O [o_1; ...; o_{n_h}], the heads' outputs concatenated head-major.
+
+    o: [..., n_h, d_h^C]; w_o: [d, n_h d_h^C] (out x in; column i*d_h^C + r
+    takes head i's element r).  Returns u [..., d] in fp64.
+    """
+    o = np.asarray(o, dtype=np.float64)
+    flat = o.reshape(o.shape[:-2] + (-1,))                               # [..., n_h d_C]
+    return flat @ np.asarray(w_o, dtype=np.float64).T
 
 
 # ----------------------------------------------------------------------------
