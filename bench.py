@@ -365,52 +365,69 @@ def hidden_bench(mla, syn, dims, dev, lens, steps: int, warmup: int, replicas: i
         call, out = mla.decode_hidden(dims, pool, table, seq_lens, *args, prepare=True)
         call_t, _ = mla.decode_hidden(dims, pool, table, seq_lens, *args, out=out, timing_events=ev,
                                       prepare=True)
-        reps.append(dict(call=call, call_t=call_t, ev=ev, keep=(pool, table, seq_lens, args, out)))
+        w_o = syn.out_weight(d, 100 + r).to(dev)
+        ev_l = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        for e in ev_l:
+            e.record()
+        ws = torch.empty(mla.decode_hidden_workspace_size(dims, B, d.d_model, d.d_cq), dtype=torch.uint8,
+                         device=dev)
+        call_l, u = mla.decode_layer(dims, pool, table, seq_lens, *args, w_o, workspace=ws, prepare=True)
+        call_lt, _ = mla.decode_layer(dims, pool, table, seq_lens, *args, w_o, u=u, workspace=ws,
+                                      timing_events=ev_l, prepare=True)
+        reps.append(dict(call=call, call_t=call_t, ev=ev, call_l=call_l, call_lt=call_lt, ev_l=ev_l,
+                         keep=(pool, table, seq_lens, args, out, w_o, ws, u)))
         del hc, base
     torch.cuda.synchronize()
     R = len(reps)
-    for i in range(warmup):
-        reps[i % R]["call"]()
-    torch.cuda.synchronize()
-    proj = []
-    for i in range(steps):
-        r = reps[i % R]
-        r["call_t"]()
+
+    def measure(kc, kt, ke):
+        """(mean event-bracketed ms, step ms by graph replay) of one call kind."""
+        for i in range(warmup):
+            reps[i % R][kc]()
         torch.cuda.synchronize()
-        proj.append(r["ev"][0].elapsed_time(r["ev"][1]))
-    proj_ms = float(np.mean(proj))
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
+        evms = []
+        for i in range(steps):
+            r = reps[i % R]
+            r[kt]()
+            torch.cuda.synchronize()
+            evms.append(r[ke][0].elapsed_time(r[ke][1]))
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            for r in reps:
+                r[kc]()
+        torch.cuda.current_stream().wait_stream(st)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for r in reps:
+                r[kc]()
+        singles = []
         for r in reps:
-            r["call"]()
-    torch.cuda.current_stream().wait_stream(s)
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for r in reps:
-            r["call"]()
-    singles = []
-    for r in reps:
-        gi = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(gi):
-            r["call"]()
-        singles.append(gi)
+            gi = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gi):
+                r[kc]()
+            singles.append(gi)
 
-    def replay(n):
-        for _ in range(n // R):
-            g.replay()
-        for i in range(n % R):
-            singles[i].replay()
+        def replay(n):
+            for _ in range(n // R):
+                g.replay()
+            for i in range(n % R):
+                singles[i].replay()
 
-    replay(warmup)
-    torch.cuda.synchronize()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record()
-    replay(steps)
-    t1.record()
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / steps
+        replay(warmup)
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        replay(steps)
+        t1.record()
+        torch.cuda.synchronize()
+        return float(np.mean(evms)), t0.elapsed_time(t1) / steps
+
+    proj_ms, ms = measure("call", "call_t", "ev")
+    wo_ms, layer_ms = measure("call_l", "call_lt", "ev_l")
+    wo_bytes = 2 * (d.d_model * d.n_heads * d.d_nope + B * (d.n_heads * d.d_nope + d.d_model))
+    wo_gbps = wo_bytes / (wo_ms * 1e-3) / 1e9
     dm, dq = d.d_model, d.d_cq
     n1 = d.d_latent + d.d_rope + dq
     n2 = d.n_heads * (d.d_nope + d.d_rope)
@@ -424,7 +441,15 @@ def hidden_bench(mla, syn, dims, dev, lens, steps: int, warmup: int, replicas: i
             "timing": "hip graph replay over %d replicas; projections by events, one step at a time" % R,
             "roofline": {"kernel": "proj_gemm (+ split-K reduce)", "bound": "hbm",
                          "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": round(gbps / HBM_PEAK_GBPS, 4), "algorithmic_bytes": wbytes + abytes}}
+                         "frac": round(gbps / HBM_PEAK_GBPS, 4), "algorithmic_bytes": wbytes + abytes},
+            "layer": {"workload": "the same step through W^O: u [64, 5120] = W^O [o_1..o_128] "
+                                  "(mla_decode_layer)",
+                      "value": round(tokens / (layer_ms * 1e-3), 1), "unit": "cached tokens/s",
+                      "ms_per_step": round(layer_ms, 5), "w_o_ms": round(wo_ms, 5),
+                      "roofline": {"kernel": "proj_gemm W^O (+ split-K reduce)", "bound": "hbm",
+                                   "achieved": round(wo_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                   "frac": round(wo_gbps / HBM_PEAK_GBPS, 4),
+                                   "algorithmic_bytes": wo_bytes}}}
 
 
 def prefill_bench(mla, syn, dims, dev, steps: int):

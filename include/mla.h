@@ -176,6 +176,28 @@ mla_status mla_decode_hidden(const mla_dims* dims, const mla_paged_cache* cache,
                              const void* w_uv, void* out, void* workspace, size_t workspace_bytes,
                              int32_t n_workgroups, void* const* timing_events, void* stream);
 
+/* The whole attention layer of one decode step, from each sequence's newest
+ * hidden state h_t to the layer output u_t: exactly mla_decode_hidden, then
+ * u = W^O [o_1; ...; o_{n_heads}] ("MLA low-rank attention" tech note [(4)
+ * attention and output]: the heads' outputs concatenated head-major and
+ * mapped back to d_model), accumulated in fp32 and rounded to bf16 (round to
+ * nearest even).
+ * w_o: [d_model, n_heads * d_nope] (out x in; column i*d_nope + r takes head
+ *   i's element r).   u: [batch, d_model].
+ * workspace: at least mla_decode_hidden_workspace_size(...) bytes (the same
+ *   layout, which holds the heads' outputs o between the two steps).
+ * timing_events: NULL, or two hipEvent_t recorded immediately before and
+ *   after the W^O projection (profiling only).
+ * Every other argument and error as for mla_decode_hidden (MLA_ERR_UNSUPPORTED
+ * outside the V2 sizes).                                                    */
+mla_status mla_decode_layer(const mla_dims* dims, const mla_paged_cache* cache, int32_t batch,
+                            const int32_t* seq_lens, int32_t d_model, int32_t d_q, const void* h,
+                            const void* w_dkv, const void* w_kr, const void* w_dq,
+                            const void* w_uq, const void* w_qr, const void* w_uk,
+                            const void* w_uv, const void* w_o, void* u, void* workspace,
+                            size_t workspace_bytes, int32_t n_workgroups,
+                            void* const* timing_events, void* stream);
+
 /* Bytes of device workspace mla_prefill needs. */
 size_t mla_prefill_workspace_size(const mla_dims* dims, int32_t batch, int32_t seq_len);
 

@@ -24,7 +24,7 @@ MLA_BF16, MLA_F32 = 0, 1
 EXPORTED = (
     "mla_cache_append", "mla_decode_workspace_size", "mla_decode", "mla_decode_step",
     "mla_decode_hidden_workspace_size", "mla_decode_hidden",
-    "mla_prefill_workspace_size", "mla_prefill", "mla_prefill_chunk_workspace_size",
+    "mla_decode_layer", "mla_prefill_workspace_size", "mla_prefill", "mla_prefill_chunk_workspace_size",
     "mla_prefill_chunk", "mla_status_string", "mla_last_error",
 )
 
@@ -111,6 +111,10 @@ def load() -> ctypes.CDLL:
                                       ctypes.c_int32, ctypes.c_int32, P, P, P, P, P, P, P, P, P, P,
                                       ctypes.c_size_t, ctypes.c_int32, P, P]
     lib.mla_decode_hidden.restype = ctypes.c_int
+    lib.mla_decode_layer.argtypes = [ctypes.POINTER(_Dims), ctypes.POINTER(_Cache), ctypes.c_int32, P,
+                                     ctypes.c_int32, ctypes.c_int32, P, P, P, P, P, P, P, P, P, P, P,
+                                     ctypes.c_size_t, ctypes.c_int32, P, P]
+    lib.mla_decode_layer.restype = ctypes.c_int
     lib.mla_prefill_workspace_size.argtypes = [ctypes.POINTER(_Dims), ctypes.c_int32, ctypes.c_int32]
     lib.mla_prefill_workspace_size.restype = ctypes.c_size_t
     lib.mla_prefill.argtypes = [ctypes.POINTER(_Dims), ctypes.POINTER(_Cache), ctypes.c_int32, ctypes.c_int32,
@@ -365,6 +369,57 @@ def decode_hidden(dims: Dims, pool: torch.Tensor, page_table: torch.Tensor, seq_
         return call, out
     call(stream)
     return out
+
+
+def decode_layer(dims: Dims, pool: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor,
+                 h: torch.Tensor, w_dkv: torch.Tensor, w_kr: torch.Tensor, w_dq: torch.Tensor,
+                 w_uq: torch.Tensor, w_qr: torch.Tensor, w_uk: torch.Tensor, w_uv: torch.Tensor,
+                 w_o: torch.Tensor, u: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                 n_workgroups: int = 0, stream=None, timing_events=None, prepare: bool = False):
+    """The attention layer of a decode step from the newest hidden states to
+    the layer output (mla_decode_layer): decode_hidden, then u = W^O o with
+    w_o [d_model, n_heads * d_nope].  Returns u [batch, d_model]; timing_events
+    bracket the W^O projection."""
+    lib = load()
+    cache = _cache(dims, pool, page_table)
+    dev = pool.device
+    if h.dim() != 2:
+        raise ValueError("h must be [batch, d_model]")
+    B, d_model = h.shape
+    d_q = w_dq.shape[0] if w_dq.dim() == 2 else -1
+    H = dims.n_heads
+    _need(h, "h", dims.dtype, (B, d_model), dev)
+    _need(w_dkv, "w_dkv", dims.dtype, (dims.d_latent, d_model), dev)
+    _need(w_kr, "w_kr", dims.dtype, (dims.d_rope, d_model), dev)
+    _need(w_dq, "w_dq", dims.dtype, (d_q, d_model), dev)
+    _need(w_uq, "w_uq", dims.dtype, (H * dims.d_nope, d_q), dev)
+    _need(w_qr, "w_qr", dims.dtype, (H * dims.d_rope, d_q), dev)
+    _need(w_uk, "w_uk", dims.dtype, (H, dims.d_nope, dims.d_latent), dev)
+    _need(w_uv, "w_uv", dims.dtype, (H, dims.d_nope, dims.d_latent), dev)
+    _need(w_o, "w_o", dims.dtype, (d_model, H * dims.d_nope), dev)
+    _need(seq_lens, "seq_lens", torch.int32, (B,), dev)
+    if page_table.shape[0] < B:
+        raise ValueError("page_table has fewer rows than the batch")
+    if u is None:
+        u = torch.empty((B, d_model), dtype=dims.dtype, device=dev)
+    _need(u, "u", dims.dtype, (B, d_model), dev)
+    need = decode_hidden_workspace_size(dims, B, d_model, d_q, n_workgroups)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    d = dims._c()
+    args = [ctypes.byref(d), ctypes.byref(cache), B, _ptr(seq_lens), d_model, d_q, _ptr(h),
+            _ptr(w_dkv), _ptr(w_kr), _ptr(w_dq), _ptr(w_uq), _ptr(w_qr), _ptr(w_uk), _ptr(w_uv),
+            _ptr(w_o), _ptr(u), _ptr(workspace), wbytes, n_workgroups]
+    evs = _events(timing_events)
+    args.append(evs.ptr)
+    call = _Prepared(lib.mla_decode_layer, args, keep=(d, cache, seq_lens, h, w_dkv, w_kr, w_dq, w_uq,
+                                                        w_qr, w_uk, w_uv, w_o, u, workspace, evs, pool,
+                                                        page_table))
+    if prepare:
+        return call, u
+    call(stream)
+    return u
 
 
 def prefill_workspace_size(dims: Dims, batch: int, seq_len: int) -> int:

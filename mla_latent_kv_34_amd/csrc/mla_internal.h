@@ -127,6 +127,14 @@ hipError_t launch_v2_decode_hidden(const Layer& L, const void* pool, int num_pag
                                    const void* w_uq, const void* w_qr, const void* w_uk,
                                    const void* w_uv, void* out, void* ws, int n_wg,
                                    void* const* ev, hipStream_t s);
+// mla_decode_hidden, then u = W^O o (proj.hip); same workspace size
+hipError_t launch_v2_decode_layer(const Layer& L, const void* pool, int num_pages,
+                                  const int32_t* table, int max_pages, int batch,
+                                  const int32_t* seq_lens, int d_model, int d_q, const void* h,
+                                  const void* w_dkv, const void* w_kr, const void* w_dq,
+                                  const void* w_uq, const void* w_qr, const void* w_uk,
+                                  const void* w_uv, const void* w_o, void* u, void* ws, int n_wg,
+                                  void* const* ev, hipStream_t s);
 // chunked prefill as launch_generic_prefill (prefill_v2.hip)
 size_t v2_prefill_workspace(int batch, int chunk_len, int max_context);
 hipError_t launch_v2_prefill(const Layer& L, const void* pool, int num_pages, const int32_t* table,

@@ -18,6 +18,8 @@
 // for k-step s), which makes the four k-steps of a step read whole 128-byte
 // lines; x is read in the same order.
 // ---------------------------------------------------------------------------
+#include <algorithm>
+
 #include "mla_internal.h"
 
 namespace mla {
@@ -136,7 +138,7 @@ int choose_split(int n_total, int K) {
 }
 
 struct HiddenLayout {
-  size_t c_kv, k_r, c_q, q_nope, q_rope, part, decode, total;
+  size_t c_kv, k_r, c_q, q_nope, q_rope, o, part, decode, total;
   HiddenLayout(const Layer& L, int batch, int n_wg, int d_model, int d_q) {
     auto al = [](size_t v) { return (v + 255) & ~(size_t)255; };
     const size_t B = (size_t)batch;
@@ -145,11 +147,13 @@ struct HiddenLayout {
     c_q = al(k_r + B * L.d_rope * 2);
     q_nope = al(c_q + B * d_q * 2);
     q_rope = al(q_nope + B * L.n_heads * L.d_nope * 2);
-    part = al(q_rope + B * L.n_heads * L.d_rope * 2);
+    o = al(q_rope + B * L.n_heads * L.d_rope * 2);
+    part = al(o + B * L.n_heads * L.d_nope * 2);
     const int n1 = L.d_latent + L.d_rope + d_q, n2 = L.n_heads * (L.d_nope + L.d_rope);
     const size_t p1 = (size_t)choose_split(n1, d_model) * n1 * B * 4;
     const size_t p2 = (size_t)choose_split(n2, d_q) * n2 * B * 4;
-    decode = al(part + (p1 > p2 ? p1 : p2));
+    const size_t p3 = (size_t)choose_split(d_model, L.n_heads * L.d_nope) * d_model * B * 4;
+    decode = al(part + std::max(p1, std::max(p2, p3)));
     total = decode + v2_decode_workspace(batch, n_wg);
   }
 };
@@ -210,6 +214,36 @@ hipError_t launch_v2_decode_hidden(const Layer& L, const void* pool, int num_pag
   // (3) the decode step: append [c^KV ; RoPE(k^R)] at seq_lens[b] - 1, then attend
   return launch_v2_decode(L, pool, num_pages, table, max_pages, batch, seq_lens, q_nope, q_rope,
                           w_uk, w_uv, out, w + lay.decode, n_wg, nullptr, s, c_kv, k_r);
+}
+
+// The whole attention layer of a decode step: mla_decode_hidden into the
+// workspace, then u = W^O [o_1; ...; o_nh] ("MLA low-rank attention" tech note
+// [(4) attention and output]) as one more projection stage (K = n_h d_h^C).
+hipError_t launch_v2_decode_layer(const Layer& L, const void* pool, int num_pages,
+                                  const int32_t* table, int max_pages, int batch,
+                                  const int32_t* seq_lens, int d_model, int d_q, const void* h,
+                                  const void* w_dkv, const void* w_kr, const void* w_dq,
+                                  const void* w_uq, const void* w_qr, const void* w_uk,
+                                  const void* w_uv, const void* w_o, void* u, void* ws, int n_wg,
+                                  void* const* ev, hipStream_t s) {
+  using namespace pj;
+  const HiddenLayout lay(L, batch, n_wg, d_model, d_q);
+  char* w = (char*)ws;
+  uint16_t* o = (uint16_t*)(w + lay.o);
+  hipError_t e = launch_v2_decode_hidden(L, pool, num_pages, table, max_pages, batch, seq_lens,
+                                         d_model, d_q, h, w_dkv, w_kr, w_dq, w_uq, w_qr, w_uk,
+                                         w_uv, o, ws, n_wg, nullptr, s);
+  if (e != hipSuccess) return e;
+  if (ev && ev[0] && (e = hipEventRecord((hipEvent_t)ev[0], s)) != hipSuccess) return e;
+  Segs s3{};
+  s3.s[0] = Seg{(const uint16_t*)w_o, (uint16_t*)u, d_model};
+  s3.count = 1;
+  s3.n_total = d_model;
+  if ((e = launch_stage(o, batch, L.n_heads * L.d_nope, s3, (float*)(w + lay.part), s)) !=
+      hipSuccess)
+    return e;
+  if (ev && ev[1] && (e = hipEventRecord((hipEvent_t)ev[1], s)) != hipSuccess) return e;
+  return hipSuccess;
 }
 
 }  // namespace mla

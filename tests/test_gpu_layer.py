@@ -1,0 +1,78 @@
+"""GPU parity of the whole attention layer of a decode step (mla_decode_layer:
+the projections from h, the decode step, then u = W^O over the heads'
+outputs) against the fp64 oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import mla_latent_kv_34_amd as mla
+import mla_synth as syn
+from oracle import decode_ref, front_end, output_proj
+
+pytestmark = pytest.mark.gpu
+
+from gpu_common import DEV, assert_close, canary_pool, f64, fill_cache, lib_dims  # noqa: E402
+
+
+def _run(hc: syn.HiddenCase, w_o: torch.Tensor, seq_lens=None):
+    base = hc.base
+    dims = lib_dims(base.dims)
+    pool = canary_pool(base.dims, base.num_pages)
+    table = torch.from_numpy(base.table).to(DEV)
+    fill_cache(base, dims, pool, table)
+    if seq_lens is None:
+        seq_lens = base.attended
+    sl = torch.tensor(np.asarray(seq_lens), dtype=torch.int32, device=DEV)
+    u = mla.decode_layer(dims, pool, table, sl, hc.h.to(DEV), *[w.to(DEV) for w in hc.front],
+                         base.w_uk.to(DEV), base.w_uv.to(DEV), w_o.to(DEV))
+    torch.cuda.synchronize()
+    return u
+
+
+def _oracle(hc: syn.HiddenCase, w_o: torch.Tensor, b: int):
+    """fp64: projections of h_b, decode over the cached rows plus the new row
+    (every head), then W^O."""
+    base = hc.base
+    f = [w.double().numpy() for w in hc.front]
+    c_new, k_new, q_c, q_r = front_end(hc.h[b].double().numpy(), *f, n_heads=base.dims.n_heads)
+    c_rows, k_rows = base.seq_rows(b)
+    n = int(base.cached[b])
+    c_all = np.vstack([c_rows[:n].double().numpy(), c_new[None]])
+    k_all = np.vstack([k_rows[:n].double().numpy(), k_new[None]])
+    o = decode_ref(q_c, q_r, c_all, k_all, base.w_uk.double().numpy(), base.w_uv.double().numpy(),
+                   base=base.dims.rope_base)
+    return output_proj(o, w_o.double().numpy())
+
+
+@pytest.mark.parametrize("cached,shuffle", [([1, 63, 64, 65, 300], True), ([0, 700, 5], False)])
+def test_decode_layer_small(cached, shuffle):
+    print(f"case decode_layer {cached}", flush=True)
+    hc = syn.hidden_case(syn.V2, cached, seed=41, shuffle=shuffle)
+    w_o = syn.out_weight(syn.V2, 41)
+    u = _run(hc, w_o)
+    for b in range(hc.base.batch):
+        assert_close(f64(u[b]), _oracle(hc, w_o, b), f"u of seq {b} (cached {hc.base.cached[b]})")
+
+
+def test_decode_layer_zero_length_sequence():
+    """A sequence with seq_lens 0 attends nothing: o = 0, so u = 0."""
+    print("case decode_layer zero length", flush=True)
+    hc = syn.hidden_case(syn.V2, [40, 3], seed=42, shuffle=True)
+    w_o = syn.out_weight(syn.V2, 42)
+    u = _run(hc, w_o, seq_lens=[int(hc.base.attended[0]), 0])
+    assert (u[1] == 0).all()
+    assert_close(f64(u[0]), _oracle(hc, w_o, 0), "u of seq 0")
+
+
+def test_decode_layer_b64_ragged_full_size_sampled():
+    """Batch 64, cached lengths uniform in [1024, 8192], shuffled pages: u of
+    sampled sequences (every head enters u) against the oracle."""
+    print("case decode_layer v2_b64_ragged", flush=True)
+    lens = syn.ragged_lengths(64, 1024, 8192, seed=0)
+    hc = syn.hidden_case(syn.V2, lens, seed=0, shuffle=True)
+    w_o = syn.out_weight(syn.V2, 0)
+    u = _run(hc, w_o)
+    assert torch.isfinite(u.float()).all()
+    rng = np.random.default_rng(14)
+    for b in rng.choice(64, size=3, replace=False):
+        assert_close(f64(u[b]), _oracle(hc, w_o, int(b)), f"u of seq {b} (cached {hc.base.cached[b]})")
