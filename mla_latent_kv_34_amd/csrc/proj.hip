@@ -7,16 +7,21 @@
 //
 // Each projection is y = x W^T with x [M, K] bf16, W [N, K] bf16 (out x in),
 // fp32 accumulation and a bf16 (round-to-nearest-even) result.  For a decode
-// batch M is small and N K large, so the launch streams the weights once:
-// one wave owns 32 weight rows and every row of x, and the weights of one
-// projection stage (same K) are laid end to end so they share one launch.
+// batch M is small and N K large: the launch streams the weights once and is
+// bound by HBM.  The weights of one projection stage (same K) are laid end to
+// end so they share one launch.
 //
-// MFMA mapping: C^T[n][m] = sum_k W[n][k] x[m][k] with v_mfma_f32_32x32x16_bf16,
-// A = 32 weight rows, B = x^T for 32 rows of x.  The dot products do not depend
-// on the order of k, so each lane reads 64 contiguous bytes of its weight row
-// per 64-wide K step (k-slot j of the MFMA's 16 k-slots is k0 + 32g + 8s + j'
-// for k-step s), which makes the four k-steps of a step read whole 128-byte
-// lines; x is read in the same order.
+// proj_gemm_kernel: a workgroup of 2 WR / 32 waves owns WR weight rows and
+// 64 rows of x per pass.  Both stream through a DEPTH-deep LDS ring of 64-wide
+// K steps (stage = WR weight rows + 64 x rows, 128 bytes each) filled by
+// direct-to-LDS loads, so DEPTH - 1 stages per workgroup are in flight while
+// one is consumed, and each x tile is read once per workgroup.
+// Wave w computes the 32 x 32 block (weight rows 32(w/2).., x rows 32(w%2)..)
+// with v_mfma_f32_32x32x16_bf16, A = weight rows, B = x rows.  The dot
+// products do not depend on the order of k, so lane (g, n) takes bytes
+// 64g + 16s .. +15 of its row for k-step s (4 per stage); the 16-byte chunks
+// of a row are swizzled in LDS (chunk c at c ^ swz(row)) so the 16 lanes of a
+// read phase hit distinct banks.
 // ---------------------------------------------------------------------------
 #include <algorithm>
 
@@ -25,15 +30,34 @@
 namespace mla {
 namespace pj {
 
-constexpr int RW = 32;   // weight rows per wave (one MFMA block)
-constexpr int KC = 64;   // K per step (4 MFMA k-steps of 16)
-constexpr int MB = 64;   // rows of x per pass (two MFMA blocks)
+#ifndef PJ_WR
+#define PJ_WR 64
+#endif
+#ifndef PJ_DEPTH
+#define PJ_DEPTH 4
+#endif
+#ifndef PJ_MIN_WG
+#define PJ_MIN_WG 256
+#endif
+constexpr int WR = PJ_WR;              // weight rows per workgroup
+constexpr int KC = 64;                 // K per stage
+constexpr int MB = 64;                 // rows of x per pass
+constexpr int NW = 2 * WR / 32;        // waves per workgroup
+constexpr int ROWB = KC * 2;           // 128 bytes per row per stage
+constexpr int STB = (WR + MB) * ROWB;  // bytes per stage
+constexpr int DEPTH = PJ_DEPTH;        // stages in the LDS ring
+constexpr int DMA_W = STB / 1024 / NW; // one-KiB loads per wave per stage
+constexpr int DMA_WT = WR * ROWB / 1024 / NW;  // of which weight rows
+constexpr int XOFF = WR * ROWB;        // x rows follow the weight rows in a stage
 constexpr int MAXSEG = 3;
+constexpr int kWeightPolicy = 2;       // weights are read once: non-temporal
+static_assert(STB % (1024 * NW) == 0 && (WR * ROWB) % (1024 * NW) == 0, "whole loads per wave");
+static_assert(DEPTH >= 2 && DEPTH * STB <= 160 * 1024, "LDS ring size");
 
 struct Seg {
   const uint16_t* w;  // [rows, K]
   uint16_t* out;      // [M, rows]
-  int rows;           // a multiple of RW
+  int rows;           // a multiple of 32
 };
 struct Segs {
   Seg s[MAXSEG];
@@ -41,58 +65,165 @@ struct Segs {
   int n_total;  // sum of rows
 };
 
-// Grid: (n_total / RW) * ksplit one-wave workgroups; workgroup ib takes row
-// block ib % nrb and K slice ib / nrb.  ksplit == 1 writes bf16 into the
-// segment outputs; ksplit > 1 writes fp32 partials part[split][row][m] that
-// proj_reduce_kernel sums.
-__global__ void __launch_bounds__(64)
-proj_gemm_kernel(const uint16_t* __restrict__ x, int M, int K, Segs segs, int ksplit,
-                 float* __restrict__ part) {
-  const int lane = threadIdx.x, g = lane >> 5, n = lane & 31;
-  const int nrb = segs.n_total / RW;
-  const int rb = (int)blockIdx.x % nrb, split = (int)blockIdx.x / nrb;
-  const int r0 = rb * RW;
-  int si = 0, base = 0;
-  while (si + 1 < segs.count && r0 >= base + segs.s[si].rows) {
-    base += segs.s[si].rows;
+// Segment of global weight row r (< n_total) and the first row of that segment.
+__device__ __forceinline__ int seg_of(const Segs& segs, int r, int* base) {
+  int si = 0, b = 0;
+  while (si + 1 < segs.count && r >= b + segs.s[si].rows) {
+    b += segs.s[si].rows;
     ++si;
   }
-  const Seg sg = segs.s[si];
-  const uint16_t* wrow = sg.w + (size_t)(r0 - base + n) * K + 32 * g;
-  const int kper = K / ksplit, k0 = split * kper, k1 = k0 + kper;
+  *base = b;
+  return si;
+}
+
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+
+__device__ __forceinline__ void raw_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// One stage of one wave: 8 LDS reads (A and B fragments of 4 k-steps) and 4
+// accumulating MFMAs.  Every read is waited for inside the block before the
+// MFMA that uses it.
+__device__ __forceinline__ void stage_mfma(f32x16& acc, const uint32_t (&a)[4],
+                                           const uint32_t (&b)[4]) {
+  u32x4 t0, t1, t2, t3, t4, t5, t6, t7;
+  asm volatile(
+      "ds_read_b128 %[t0], %[a0]\n\t"
+      "ds_read_b128 %[t1], %[b0]\n\t"
+      "ds_read_b128 %[t2], %[a1]\n\t"
+      "ds_read_b128 %[t3], %[b1]\n\t"
+      "ds_read_b128 %[t4], %[a2]\n\t"
+      "ds_read_b128 %[t5], %[b2]\n\t"
+      "ds_read_b128 %[t6], %[a3]\n\t"
+      "ds_read_b128 %[t7], %[b3]\n\t"
+      "s_waitcnt lgkmcnt(6)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[acc], %[t0], %[t1], %[acc]\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[acc], %[t2], %[t3], %[acc]\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[acc], %[t4], %[t5], %[acc]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[acc], %[t6], %[t7], %[acc]\n\t"
+      : [acc] "+a"(acc), [t0] "=&v"(t0), [t1] "=&v"(t1), [t2] "=&v"(t2), [t3] "=&v"(t3),
+        [t4] "=&v"(t4), [t5] "=&v"(t5), [t6] "=&v"(t6), [t7] "=&v"(t7)
+      : [a0] "v"(a[0]), [a1] "v"(a[1]), [a2] "v"(a[2]), [a3] "v"(a[3]), [b0] "v"(b[0]),
+        [b1] "v"(b[1]), [b2] "v"(b[2]), [b3] "v"(b[3]));
+}
+
+// Grid: ceil(n_total / WR) * ksplit workgroups; workgroup ib takes row block
+// ib % nrb and K slice ib / nrb.  Rows at or past n_total (the last block of a
+// stage whose size is not a multiple of WR) are loaded from row n_total - 1
+// and not stored.  ksplit == 1 writes bf16 into the segment outputs;
+// ksplit > 1 writes fp32 partials part[split][m][row] that proj_reduce_kernel
+// sums.
+__global__ void __launch_bounds__(64 * NW)
+proj_gemm_kernel(const uint16_t* __restrict__ x, int M, int K, Segs segs, int ksplit,
+                 float* __restrict__ part) {
+  __shared__ __attribute__((aligned(1024))) char lds[DEPTH * STB];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, n = lane & 31;
+  const int nrb = (segs.n_total + WR - 1) / WR;
+  const int rb = (int)blockIdx.x % nrb, split = (int)blockIdx.x / nrb;
+  const int r0 = rb * WR;
+  const int kper = K / ksplit, k0 = split * kper, nst = kper / KC;
+
+  // direct-to-LDS plan: load j of wave w fills the 1 KiB block q = NW j + w
+  // of a stage, rows 8q .. 8q + 7 (loads j < DMA_WT: weight rows, the rest:
+  // x rows); lane l stores its 16 bytes at chunk l % 8 of row 8q + l / 8,
+  // i.e. source chunk (l % 8) ^ swz(row).
+  const char* wsrc[DMA_WT];
+#pragma unroll
+  for (int j = 0; j < DMA_WT; ++j) {
+    const int row = 8 * (NW * j + wave) + (lane >> 3);
+    const int gr = min(r0 + row, segs.n_total - 1);
+    int base;
+    const int si = seg_of(segs, gr, &base);
+    wsrc[j] = (const char*)(segs.s[si].w + (size_t)(gr - base) * K) + (size_t)k0 * 2 +
+              16 * ((lane & 7) ^ swz(row));
+  }
+  int xrow_of[DMA_W - DMA_WT];
+#pragma unroll
+  for (int j = DMA_WT; j < DMA_W; ++j) xrow_of[j - DMA_WT] = 8 * (NW * j + wave) + (lane >> 3) - WR;
+
+  // LDS read addresses of this wave's fragments (ring slot 0)
+  const int wrow = 32 * (wave >> 1) + n, xrow = 32 * (wave & 1) + n;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)lds);
+  uint32_t aa[4], bb[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    aa[s] = lds0 + (uint32_t)(wrow * ROWB + 16 * ((4 * g + s) ^ swz(wrow)));
+    bb[s] = lds0 + (uint32_t)(XOFF + xrow * ROWB + 16 * ((4 * g + s) ^ swz(xrow)));
+  }
 
   for (int m0 = 0; m0 < M; m0 += MB) {
-    const int ma = m0 + n, mb = m0 + RW + n;
-    const bool va = ma < M, vb = mb < M;
-    const uint16_t* xa = x + (size_t)min(ma, M - 1) * K + 32 * g;
-    const uint16_t* xb = x + (size_t)min(mb, M - 1) * K + 32 * g;
-    f32x16 acc0 = {}, acc1 = {};
-#pragma unroll 2
-    for (int k = k0; k < k1; k += KC) {
-      bf16x8 a[4], b0[4], b1[4];
+    const char* xsrc[DMA_W - DMA_WT];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        a[s] = *(const bf16x8*)(wrow + k + 8 * s);
-        b0[s] = *(const bf16x8*)(xa + k + 8 * s);
-        b1[s] = *(const bf16x8*)(xb + k + 8 * s);
-      }
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        if (!va) b0[s] = (bf16x8){};
-        if (!vb) b1[s] = (bf16x8){};
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s], b0[s], acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s], b1[s], acc1, 0, 0, 0);
-      }
+    for (int j = 0; j < DMA_W - DMA_WT; ++j) {
+      const int r = xrow_of[j];
+      xsrc[j] = (const char*)(x + (size_t)min(m0 + r, M - 1) * K) + (size_t)k0 * 2 +
+                16 * ((lane & 7) ^ swz(r));
     }
-    // accumulator element i of a lane: weight row 8(i / 4) + 4g + (i % 4) of
-    // the block, x row (column) n of the block
+    auto issue = [&](int st) {
+      char* buf = lds + (st % DEPTH) * STB + wave * 1024;
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      const int m = m0 + RW * blk + n;
-      if (m >= M) continue;
-      const f32x16& acc = blk ? acc1 : acc0;
+      for (int j = 0; j < DMA_WT; ++j)
+        __builtin_amdgcn_global_load_lds(wsrc[j] + (size_t)st * ROWB,
+                                         (__attribute__((address_space(3))) void*)(buf + NW * j * 1024),
+                                         16, 0, kWeightPolicy);
+#pragma unroll
+      for (int j = DMA_WT; j < DMA_W; ++j)
+        __builtin_amdgcn_global_load_lds(xsrc[j - DMA_WT] + (size_t)st * ROWB,
+                                         (__attribute__((address_space(3))) void*)(buf + NW * j * 1024),
+                                         16, 0, 0);
+    };
+    f32x16 acc = {};
+    const int pre = min(DEPTH - 1, nst);
+    for (int st = 0; st < pre; ++st) issue(st);
+    for (int st = 0; st < nst; ++st) {
+      // wait for this wave's loads of stage st: the later stages it has issued
+      // (at most DEPTH - 2) may stay in flight
+      const int after = min(DEPTH - 2, nst - 1 - st);
+      if constexpr (DEPTH >= 5) {
+        if (after >= 3) { wait_vmcnt<3 * DMA_W>(); goto waited; }
+      }
+      if constexpr (DEPTH >= 4) {
+        if (after == 2) { wait_vmcnt<2 * DMA_W>(); goto waited; }
+      }
+      if constexpr (DEPTH >= 3) {
+        if (after == 1) { wait_vmcnt<DMA_W>(); goto waited; }
+      }
+      wait_vmcnt<0>();
+    waited:
+      raw_barrier();  // stage st is in LDS; every wave is done with stage st - 1
+      if (st + DEPTH - 1 < nst) issue(st + DEPTH - 1);
+      const uint32_t off = (uint32_t)((st % DEPTH) * STB);
+      uint32_t a[4], b[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        a[s] = aa[s] + off;
+        b[s] = bb[s] + off;
+      }
+      stage_mfma(acc, a, b);
+    }
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");  // MFMA results before VALU reads
+    // accumulator element i of a lane: weight row 8(i / 4) + 4g + (i % 4) of
+    // the wave's block, x row n of the block
+    const int m = m0 + xrow;
+    const int grow = r0 + 32 * (wave >> 1);  // first global row of the wave's block
+    if (m < M && grow < segs.n_total) {
       if (ksplit == 1) {
-        uint16_t* dst = sg.out + (size_t)m * sg.rows + (r0 - base) + 4 * g;
+        int base;
+        const Seg sg = segs.s[seg_of(segs, grow, &base)];
+        uint16_t* dst = sg.out + (size_t)m * sg.rows + (grow - base) + 4 * g;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           ushort4 v;
@@ -103,37 +234,50 @@ proj_gemm_kernel(const uint16_t* __restrict__ x, int M, int K, Segs segs, int ks
           *(ushort4*)(dst + 8 * q) = v;
         }
       } else {
-        float* dst = part + ((size_t)split * segs.n_total + r0 + 4 * g) * M + m;
+        float* dst = part + ((size_t)split * M + m) * segs.n_total + grow + 4 * g;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) dst[(size_t)(8 * (i >> 2) + (i & 3)) * M] = acc[i];
+        for (int q = 0; q < 4; ++q)
+          *(float4*)(dst + 8 * q) = make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
       }
     }
+    raw_barrier();  // every wave is done with the ring before the next pass refills it
   }
 }
 
-// out[m][row] = bf16(sum over splits of part[split][row][m]); thread e takes
-// row e / M, x row e % M (consecutive threads read consecutive partials).
+// out[m][row .. row + 3] = bf16(sum over splits of part[split][m][row .. row + 3]);
+// consecutive threads take consecutive 4-row groups of one x row, so both the
+// partial reads and the output writes are contiguous.
 __global__ void __launch_bounds__(256)
 proj_reduce_kernel(const float* __restrict__ part, int M, int ksplit, Segs segs) {
+  const int q4 = segs.n_total / 4;
   const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (e >= (long long)segs.n_total * M) return;
-  const int row = (int)(e / M), m = (int)(e % M);
-  float acc = 0.f;
-  for (int s = 0; s < ksplit; ++s) acc += part[((size_t)s * segs.n_total + row) * M + m];
-  int si = 0, base = 0;
-  while (si + 1 < segs.count && row >= base + segs.s[si].rows) {
-    base += segs.s[si].rows;
-    ++si;
+  if (e >= (long long)q4 * M) return;
+  const int m = (int)(e / q4), row = 4 * (int)(e % q4);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s = 0; s < ksplit; ++s) {
+    const float4 v = *(const float4*)(part + ((size_t)s * M + m) * segs.n_total + row);
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
   }
-  segs.s[si].out[(size_t)m * segs.s[si].rows + (row - base)] = bf16_bits_rne_f32(acc);
+  int base;
+  const Seg sg = segs.s[seg_of(segs, row, &base)];
+  ushort4 o;
+  o.x = bf16_bits_rne_f32(acc.x);
+  o.y = bf16_bits_rne_f32(acc.y);
+  o.z = bf16_bits_rne_f32(acc.z);
+  o.w = bf16_bits_rne_f32(acc.w);
+  *(ushort4*)(sg.out + (size_t)m * sg.rows + (row - base)) = o;
 }
 
-// K slices per launch: enough one-wave workgroups (>= 512) to keep the whole
-// chip's memory queues busy; a power of two dividing K / KC.
+// K slices per launch: at least PJ_MIN_WG workgroups, a power of two
+// dividing K / KC.
+constexpr int kMinWorkgroups = PJ_MIN_WG;
 int choose_split(int n_total, int K) {
-  const int tiles = n_total / RW;
+  const int tiles = (n_total + WR - 1) / WR;
   int s = 1;
-  while (tiles * s < 512 && (K / KC) % (2 * s) == 0) s *= 2;
+  while (tiles * s < kMinWorkgroups && (K / KC) % (2 * s) == 0) s *= 2;
   return s;
 }
 
@@ -161,10 +305,10 @@ struct HiddenLayout {
 hipError_t launch_stage(const uint16_t* x, int M, int K, const Segs& segs, float* part,
                         hipStream_t s) {
   const int ks = choose_split(segs.n_total, K);
-  hipLaunchKernelGGL(proj_gemm_kernel, dim3((unsigned)(segs.n_total / RW * ks)), dim3(64), 0, s, x,
-                     M, K, segs, ks, part);
+  hipLaunchKernelGGL(proj_gemm_kernel, dim3((unsigned)((segs.n_total + WR - 1) / WR * ks)),
+                     dim3(64 * NW), 0, s, x, M, K, segs, ks, part);
   if (ks > 1) {
-    const long long n = (long long)segs.n_total * M;
+    const long long n = (long long)segs.n_total / 4 * M;
     hipLaunchKernelGGL(proj_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                        (const float*)part, M, ks, segs);
   }
