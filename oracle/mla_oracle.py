@@ -56,7 +56,7 @@ import math
 import numpy as np
 
 __all__ = [
-    "rope_frequencies", "rotate_pairs", "rope", "front_end", "output_proj",
+    "rope_frequencies", "rotate_pairs", "rope", "front_end", "output_proj", "merge_query_weights",
     "expand_heads", "decode_ref", "prefill_ref", "prefill_chunk_ref",
     "absorbed_decode_ref",
     "bf16_bits_rne", "f32_rne", "append_expected",
@@ -147,6 +147,21 @@ def output_proj(o, w_o):
     o = np.asarray(o, dtype=np.float64)
     flat = o.reshape(o.shape[:-2] + (-1,))                               # [..., n_h d_C]
     return flat @ np.asarray(w_o, dtype=np.float64).T
+
+
+def merge_query_weights(w_uq, w_uk, *, n_heads: int) -> np.ndarray:
+    """The fixed product of the query up-projection and the key absorption
+    ("From LLaMA to DeepSeek [01]" [section 6]: both are fixed matrices, so
+    they can be multiplied once in advance): W^UQK_i = W^UK_i^T W^UQ_i.
+
+    w_uq: [n_h d_h^C, d_c'] (out x in, head-major rows); w_uk: [n_h, d_h^C, d_c].
+    Returns [n_h, d_c, d_c'] in fp64, so that q_lat_i = W^UQK_i c^Q.
+    """
+    w_uq = np.asarray(w_uq, dtype=np.float64)
+    w_uk = np.asarray(w_uk, dtype=np.float64)
+    d_nope = w_uk.shape[1]
+    uq = w_uq.reshape(n_heads, d_nope, -1)                              # [h, d_C, d_c']
+    return np.matmul(np.swapaxes(w_uk, 1, 2), uq)                       # [h, d_c, d_c']
 
 
 # ----------------------------------------------------------------------------
