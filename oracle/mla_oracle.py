@@ -56,7 +56,7 @@ import math
 import numpy as np
 
 __all__ = [
-    "rope_frequencies", "rotate_pairs", "rope", "front_end", "output_proj", "merge_query_weights",
+    "rope_frequencies", "rotate_pairs", "rope", "front_end", "output_proj", "merge_query_weights", "merge_output_weights",
     "expand_heads", "decode_ref", "prefill_ref", "prefill_chunk_ref",
     "absorbed_decode_ref",
     "bf16_bits_rne", "f32_rne", "append_expected",
@@ -162,6 +162,23 @@ def merge_query_weights(w_uq, w_uk, *, n_heads: int) -> np.ndarray:
     d_nope = w_uk.shape[1]
     uq = w_uq.reshape(n_heads, d_nope, -1)                              # [h, d_C, d_c']
     return np.matmul(np.swapaxes(w_uk, 1, 2), uq)                       # [h, d_c, d_c']
+
+
+def merge_output_weights(w_o, w_uv) -> np.ndarray:
+    """The value side of the absorption carried into the output projection
+    ("From LLaMA to DeepSeek [01]" [section 6]: the V side works like the K
+    side, and fixed matrices can be multiplied in advance):
+    W^OV = [W^O_1 W^UV_1, ..., W^O_nh W^UV_nh], where W^O_i is the block of
+    W^O's columns that takes head i, so u = W^OV [o_lat_1; ...; o_lat_nh].
+
+    w_o: [d, n_h d_h^C] (out x in); w_uv: [n_h, d_h^C, d_c].
+    Returns [d, n_h d_c] in fp64.
+    """
+    w_o = np.asarray(w_o, dtype=np.float64)
+    w_uv = np.asarray(w_uv, dtype=np.float64)
+    n_h, d_nope, d_c = w_uv.shape
+    blocks = [w_o[:, i * d_nope:(i + 1) * d_nope] @ w_uv[i] for i in range(n_h)]
+    return np.concatenate(blocks, axis=1)
 
 
 # ----------------------------------------------------------------------------

@@ -59,3 +59,39 @@ def test_associativity_and_decode():
     np.testing.assert_allclose(absorbed_decode_ref(q_c, q_r, c_all, k_all, w_uk, w_uv, base=d.rope_base),
                                decode_ref(q_c, q_r, c_all, k_all, w_uk, w_uv, base=d.rope_base),
                                rtol=1e-11, atol=1e-12)
+
+
+def test_output_merge_selection_weights():
+    """W^O picks head elements, W^UV_i places latent slots: the merged weight
+    maps latent slot c of head i to output j exactly when W^O's column for
+    (i, r) feeds j and W^UV_i row r reads slot c."""
+    from oracle import merge_output_weights
+    n_h, d_nope, d_c, d = 2, 3, 4, 5
+    w_o = np.zeros((d, n_h * d_nope))
+    w_uv = np.zeros((n_h, d_nope, d_c))
+    w_o[0, 0 * d_nope + 2] = 1.0          # u_0 <- head 0, element 2
+    w_o[3, 1 * d_nope + 0] = 1.0          # u_3 <- head 1, element 0
+    w_uv[0, 2, 1] = 1.0                   # head 0 element 2 <- latent 1
+    w_uv[1, 0, 3] = 1.0                   # head 1 element 0 <- latent 3
+    m = merge_output_weights(w_o, w_uv)
+    want = np.zeros((d, n_h * d_c))
+    want[0, 0 * d_c + 1] = 1.0
+    want[3, 1 * d_c + 3] = 1.0
+    np.testing.assert_array_equal(m, want)
+
+
+def test_output_merge_plain_loops_and_associativity():
+    from oracle import merge_output_weights, output_proj
+    rng = np.random.default_rng(7)
+    n_h, d_nope, d_c, d = 3, 4, 5, 6
+    w_o = rng.standard_normal((d, n_h * d_nope))
+    w_uv = rng.standard_normal((n_h, d_nope, d_c))
+    m = merge_output_weights(w_o, w_uv)
+    for j in range(d):
+        for i in range(n_h):
+            for c in range(d_c):
+                acc = sum(w_o[j, i * d_nope + r] * w_uv[i, r, c] for r in range(d_nope))
+                assert abs(m[j, i * d_c + c] - acc) <= 1e-12 * (1 + abs(acc))
+    o_lat = rng.standard_normal((n_h, d_c))
+    o = np.einsum("hrc,hc->hr", w_uv, o_lat)
+    np.testing.assert_allclose(m @ o_lat.reshape(-1), output_proj(o, w_o), rtol=1e-12, atol=1e-12)
