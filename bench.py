@@ -374,8 +374,29 @@ def hidden_bench(mla, syn, dims, dev, lens, steps: int, warmup: int, replicas: i
         call_l, u = mla.decode_layer(dims, pool, table, seq_lens, *args, w_o, workspace=ws, prepare=True)
         call_lt, _ = mla.decode_layer(dims, pool, table, seq_lens, *args, w_o, u=u, workspace=ws,
                                       timing_events=ev_l, prepare=True)
+        w_uqk = mla.merge_query_weights(dims, args[4], args[6])
+
+        def layer_merged(w_o, ws):
+            w_ov = mla.merge_output_weights(dims, w_o, args[7])
+            ev_v = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for e in ev_v:
+                e.record()
+            largs = args[:7] + [w_ov]                             # ..., W^UQ, W^QR, W^UK, W^OV
+            c_v, u_v = mla.decode_layer_merged(dims, pool, table, seq_lens, *largs, workspace=ws, prepare=True)
+            c_vt, _ = mla.decode_layer_merged(dims, pool, table, seq_lens, *largs, u=u_v, workspace=ws,
+                                              timing_events=ev_v, prepare=True)
+            return dict(call_v=c_v, call_vt=c_vt, ev_v=ev_v, keep_v=(w_ov, u_v))
+        margs = args[:4] + [w_uqk, args[5], args[7]]             # h, W^DKV, W^KR, W^DQ, W^UQK, W^QR, W^UV
+        ev_m = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        for e in ev_m:
+            e.record()
+        call_m, out_m = mla.decode_hidden_merged(dims, pool, table, seq_lens, *margs, workspace=ws,
+                                                 prepare=True)
+        call_mt, _ = mla.decode_hidden_merged(dims, pool, table, seq_lens, *margs, out=out_m, workspace=ws,
+                                              timing_events=ev_m, prepare=True)
         reps.append(dict(call=call, call_t=call_t, ev=ev, call_l=call_l, call_lt=call_lt, ev_l=ev_l,
-                         keep=(pool, table, seq_lens, args, out, w_o, ws, u)))
+                         call_m=call_m, call_mt=call_mt, ev_m=ev_m, **layer_merged(w_o, ws),
+                         keep=(pool, table, seq_lens, args, out, w_o, ws, u, w_uqk, out_m)))
         del hc, base
     torch.cuda.synchronize()
     R = len(reps)
@@ -426,6 +447,9 @@ def hidden_bench(mla, syn, dims, dev, lens, steps: int, warmup: int, replicas: i
 
     proj_ms, ms = measure("call", "call_t", "ev")
     wo_ms, layer_ms = measure("call_l", "call_lt", "ev_l")
+    pm_ms, merged_ms = measure("call_m", "call_mt", "ev_m")
+    wov_ms, layer_v_ms = measure("call_v", "call_vt", "ev_v")
+    wov_bytes = 2 * (d.d_model * d.n_heads * d.d_latent + B * (d.n_heads * d.d_latent + d.d_model))
     wo_bytes = 2 * (d.d_model * d.n_heads * d.d_nope + B * (d.n_heads * d.d_nope + d.d_model))
     wo_gbps = wo_bytes / (wo_ms * 1e-3) / 1e9
     dm, dq = d.d_model, d.d_cq
@@ -434,6 +458,8 @@ def hidden_bench(mla, syn, dims, dev, lens, steps: int, warmup: int, replicas: i
     wbytes = 2 * (n1 * dm + n2 * dq)
     abytes = 2 * B * (dm + n1 + dq + n2)        # h in, stage-1 out, c^Q in, stage-2 out
     gbps = (wbytes + abytes) / (proj_ms * 1e-3) / 1e9
+    n2m = d.n_heads * (d.d_latent + d.d_rope)
+    mbytes = 2 * (n1 * dm + n2m * dq) + 2 * B * (dm + n1 + dq + n2m)
     return {"workload": "v2_b64_ragged from hidden states: h [64, 5120] -> c^KV, k^R, c^Q "
                         "(W^DKV, W^KR, W^DQ) -> q^C, q^R (W^UQ, W^QR), then the decode step",
             "value": round(tokens / (ms * 1e-3), 1), "unit": "cached tokens/s",
@@ -442,6 +468,12 @@ def hidden_bench(mla, syn, dims, dev, lens, steps: int, warmup: int, replicas: i
             "roofline": {"kernel": "proj_gemm (+ split-K reduce)", "bound": "hbm",
                          "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                          "frac": round(gbps / HBM_PEAK_GBPS, 4), "algorithmic_bytes": wbytes + abytes},
+            "merged": {"workload": "the same step with the pre-merged query weight W^UK_i^T W^UQ_i "
+                                   "(mla_decode_hidden_merged): c^Q -> [q_lat | q^R] in place of c^Q -> q^C",
+                       "value": round(tokens / (merged_ms * 1e-3), 1), "unit": "cached tokens/s",
+                       "ms_per_step": round(merged_ms, 5), "projections_ms": round(pm_ms, 5),
+                       "projection_bytes": mbytes,
+                       "projections_GBps": round(mbytes / (pm_ms * 1e-3) / 1e9, 1)},
             "layer": {"workload": "the same step through W^O: u [64, 5120] = W^O [o_1..o_128] "
                                   "(mla_decode_layer)",
                       "value": round(tokens / (layer_ms * 1e-3), 1), "unit": "cached tokens/s",
@@ -449,7 +481,13 @@ def hidden_bench(mla, syn, dims, dev, lens, steps: int, warmup: int, replicas: i
                       "roofline": {"kernel": "proj_gemm W^O (+ split-K reduce)", "bound": "hbm",
                                    "achieved": round(wo_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                                    "frac": round(wo_gbps / HBM_PEAK_GBPS, 4),
-                                   "algorithmic_bytes": wo_bytes}}}
+                                   "algorithmic_bytes": wo_bytes}},
+            "layer_merged": {"workload": "the layer with W^UV merged into W^O per head (mla_decode_layer_merged): "
+                                         "u = W^OV [o_lat_1..o_lat_128]",
+                             "value": round(tokens / (layer_v_ms * 1e-3), 1), "unit": "cached tokens/s",
+                             "ms_per_step": round(layer_v_ms, 5), "w_ov_ms": round(wov_ms, 5),
+                             "w_ov_bytes": wov_bytes,
+                             "w_ov_GBps": round(wov_bytes / (wov_ms * 1e-3) / 1e9, 1)}}
 
 
 def prefill_bench(mla, syn, dims, dev, steps: int):

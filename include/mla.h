@@ -198,6 +198,67 @@ mla_status mla_decode_layer(const mla_dims* dims, const mla_paged_cache* cache, 
                             size_t workspace_bytes, int32_t n_workgroups,
                             void* const* timing_events, void* stream);
 
+/* Pre-merge the fixed query up-projection with the key absorption ("From
+ * LLaMA to DeepSeek [01]" [section 6]: both matrices are fixed, so their
+ * product can be formed once in advance): W^UQK_i = W^UK_i^T W^UQ_i, so that
+ * the absorbed content query is q_lat_i = W^UQK_i c^Q.  A one-time weight
+ * preparation for mla_decode_hidden_merged, not part of a step.
+ * w_uq: [n_heads * d_nope, d_q]   w_uk: [n_heads, d_nope, d_latent]
+ * w_uqk (output, caller-allocated): [n_heads, d_latent, d_q], fp32 sums
+ *   rounded to bf16 (round to nearest even).
+ * d_q: a positive multiple of 64.  V2 sizes only (MLA_ERR_UNSUPPORTED
+ * otherwise).                                                              */
+mla_status mla_merge_query_weights(const mla_dims* dims, int32_t d_q, const void* w_uq,
+                                  const void* w_uk, void* w_uqk, void* stream);
+
+/* mla_decode_hidden with the pre-merged query weight: c^Q = W^DQ h as there,
+ * then q_lat_i = W^UQK_i c^Q and q^R = W^QR c^Q in one projection stage, and
+ * the decode step with q_lat in place of W^UK_i^T q^C_i.  The same result as
+ * mla_decode_hidden up to rounding (q^C is never formed).  It reads
+ * n_heads * d_latent * d_q weights for the query instead of n_heads * d_nope
+ * * (d_q + d_latent): 4x the bytes of W^UQ plus W^UK at the V2 sizes, so at
+ * decode batch sizes, which are bound by reading weights, it is slower.
+ * w_uqk: from mla_merge_query_weights.  No w_uq, w_uk.  Every other argument,
+ * the workspace size (mla_decode_hidden_workspace_size) and the errors as for
+ * mla_decode_hidden.                                                        */
+mla_status mla_decode_hidden_merged(const mla_dims* dims, const mla_paged_cache* cache,
+                                    int32_t batch, const int32_t* seq_lens, int32_t d_model,
+                                    int32_t d_q, const void* h, const void* w_dkv, const void* w_kr,
+                                    const void* w_dq, const void* w_uqk, const void* w_qr,
+                                    const void* w_uv, void* out, void* workspace,
+                                    size_t workspace_bytes, int32_t n_workgroups,
+                                    void* const* timing_events, void* stream);
+
+/* Merge W^UV into W^O per head ("From LLaMA to DeepSeek [01]" [section 6]:
+ * the value side is absorbed like the key side, and fixed matrices can be
+ * multiplied in advance): W^OV = [W^O_1 W^UV_1, ..., W^O_nh W^UV_nh], where
+ * W^O_i holds the d_nope columns of W^O that take head i.  A one-time weight
+ * preparation for mla_decode_layer_merged.
+ * w_o: [d_model, n_heads * d_nope]   w_uv: [n_heads, d_nope, d_latent]
+ * w_ov (output, caller-allocated): [d_model, n_heads * d_latent], fp32 sums
+ *   rounded to bf16 (round to nearest even).
+ * d_model: a positive multiple of 64.  V2 sizes only.                       */
+mla_status mla_merge_output_weights(const mla_dims* dims, int32_t d_model, const void* w_o,
+                                   const void* w_uv, void* w_ov, void* stream);
+
+/* mla_decode_layer with W^UV merged into W^O: the projections and the decode
+ * as mla_decode_hidden, except that the decode ends at the normalised latent
+ * outputs o_lat_i (rounded to bf16), then u = W^OV [o_lat_1; ...; o_lat_nh].
+ * The same u as mla_decode_layer up to rounding.  W^OV holds n_heads *
+ * d_latent * d_model weights against (n_heads * d_nope) * (d_latent +
+ * d_model) for W^UV plus W^O: 3.6x the bytes at the V2 sizes, so at decode
+ * batch sizes, which are bound by reading weights, it is slower.
+ * w_ov: from mla_merge_output_weights; no w_uv, w_o.  Every other argument,
+ * the workspace size (mla_decode_hidden_workspace_size) and the errors as for
+ * mla_decode_layer (timing_events bracket the W^OV projection).              */
+mla_status mla_decode_layer_merged(const mla_dims* dims, const mla_paged_cache* cache, int32_t batch,
+                                   const int32_t* seq_lens, int32_t d_model, int32_t d_q,
+                                   const void* h, const void* w_dkv, const void* w_kr,
+                                   const void* w_dq, const void* w_uq, const void* w_qr,
+                                   const void* w_uk, const void* w_ov, void* u, void* workspace,
+                                   size_t workspace_bytes, int32_t n_workgroups,
+                                   void* const* timing_events, void* stream);
+
 /* Bytes of device workspace mla_prefill needs. */
 size_t mla_prefill_workspace_size(const mla_dims* dims, int32_t batch, int32_t seq_len);
 

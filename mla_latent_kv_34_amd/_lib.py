@@ -24,7 +24,9 @@ MLA_BF16, MLA_F32 = 0, 1
 EXPORTED = (
     "mla_cache_append", "mla_decode_workspace_size", "mla_decode", "mla_decode_step",
     "mla_decode_hidden_workspace_size", "mla_decode_hidden",
-    "mla_decode_layer", "mla_prefill_workspace_size", "mla_prefill", "mla_prefill_chunk_workspace_size",
+    "mla_decode_layer", "mla_merge_query_weights", "mla_decode_hidden_merged",
+    "mla_merge_output_weights", "mla_decode_layer_merged",
+    "mla_prefill_workspace_size", "mla_prefill", "mla_prefill_chunk_workspace_size",
     "mla_prefill_chunk", "mla_status_string", "mla_last_error",
 )
 
@@ -115,6 +117,18 @@ def load() -> ctypes.CDLL:
                                      ctypes.c_int32, ctypes.c_int32, P, P, P, P, P, P, P, P, P, P, P,
                                      ctypes.c_size_t, ctypes.c_int32, P, P]
     lib.mla_decode_layer.restype = ctypes.c_int
+    lib.mla_merge_query_weights.argtypes = [ctypes.POINTER(_Dims), ctypes.c_int32, P, P, P, P]
+    lib.mla_merge_query_weights.restype = ctypes.c_int
+    lib.mla_decode_hidden_merged.argtypes = [ctypes.POINTER(_Dims), ctypes.POINTER(_Cache), ctypes.c_int32, P,
+                                             ctypes.c_int32, ctypes.c_int32, P, P, P, P, P, P, P, P, P,
+                                             ctypes.c_size_t, ctypes.c_int32, P, P]
+    lib.mla_decode_hidden_merged.restype = ctypes.c_int
+    lib.mla_merge_output_weights.argtypes = [ctypes.POINTER(_Dims), ctypes.c_int32, P, P, P, P]
+    lib.mla_merge_output_weights.restype = ctypes.c_int
+    lib.mla_decode_layer_merged.argtypes = [ctypes.POINTER(_Dims), ctypes.POINTER(_Cache), ctypes.c_int32, P,
+                                            ctypes.c_int32, ctypes.c_int32, P, P, P, P, P, P, P, P, P, P,
+                                            ctypes.c_size_t, ctypes.c_int32, P, P]
+    lib.mla_decode_layer_merged.restype = ctypes.c_int
     lib.mla_prefill_workspace_size.argtypes = [ctypes.POINTER(_Dims), ctypes.c_int32, ctypes.c_int32]
     lib.mla_prefill_workspace_size.restype = ctypes.c_size_t
     lib.mla_prefill.argtypes = [ctypes.POINTER(_Dims), ctypes.POINTER(_Cache), ctypes.c_int32, ctypes.c_int32,
@@ -416,6 +430,147 @@ def decode_layer(dims: Dims, pool: torch.Tensor, page_table: torch.Tensor, seq_l
     call = _Prepared(lib.mla_decode_layer, args, keep=(d, cache, seq_lens, h, w_dkv, w_kr, w_dq, w_uq,
                                                         w_qr, w_uk, w_uv, w_o, u, workspace, evs, pool,
                                                         page_table))
+    if prepare:
+        return call, u
+    call(stream)
+    return u
+
+
+def merge_query_weights(dims: Dims, w_uq: torch.Tensor, w_uk: torch.Tensor,
+                        w_uqk: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """W^UQK_i = W^UK_i^T W^UQ_i (mla_merge_query_weights): w_uq [n_heads *
+    d_nope, d_q], w_uk [n_heads, d_nope, d_latent]; returns [n_heads,
+    d_latent, d_q]."""
+    lib = load()
+    H = dims.n_heads
+    if w_uq.dim() != 2:
+        raise ValueError("w_uq must be [n_heads * d_nope, d_q]")
+    d_q = w_uq.shape[1]
+    dev = w_uq.device
+    _need(w_uq, "w_uq", dims.dtype, (H * dims.d_nope, d_q), dev)
+    _need(w_uk, "w_uk", dims.dtype, (H, dims.d_nope, dims.d_latent), dev)
+    if w_uqk is None:
+        w_uqk = torch.empty((H, dims.d_latent, d_q), dtype=dims.dtype, device=dev)
+    _need(w_uqk, "w_uqk", dims.dtype, (H, dims.d_latent, d_q), dev)
+    d = dims._c()
+    _check(lib.mla_merge_query_weights(ctypes.byref(d), d_q, _ptr(w_uq), _ptr(w_uk), _ptr(w_uqk),
+                                       _stream(stream)))
+    return w_uqk
+
+
+def decode_hidden_merged(dims: Dims, pool: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor,
+                         h: torch.Tensor, w_dkv: torch.Tensor, w_kr: torch.Tensor, w_dq: torch.Tensor,
+                         w_uqk: torch.Tensor, w_qr: torch.Tensor, w_uv: torch.Tensor,
+                         out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                         n_workgroups: int = 0, stream=None, timing_events=None, prepare: bool = False):
+    """decode_hidden with the pre-merged query weight (mla_decode_hidden_merged):
+    w_uqk [n_heads, d_latent, d_q] from merge_query_weights replaces w_uq and
+    w_uk.  Returns out [batch, n_heads, d_nope]."""
+    lib = load()
+    cache = _cache(dims, pool, page_table)
+    dev = pool.device
+    if h.dim() != 2:
+        raise ValueError("h must be [batch, d_model]")
+    B, d_model = h.shape
+    d_q = w_dq.shape[0] if w_dq.dim() == 2 else -1
+    H = dims.n_heads
+    _need(h, "h", dims.dtype, (B, d_model), dev)
+    _need(w_dkv, "w_dkv", dims.dtype, (dims.d_latent, d_model), dev)
+    _need(w_kr, "w_kr", dims.dtype, (dims.d_rope, d_model), dev)
+    _need(w_dq, "w_dq", dims.dtype, (d_q, d_model), dev)
+    _need(w_uqk, "w_uqk", dims.dtype, (H, dims.d_latent, d_q), dev)
+    _need(w_qr, "w_qr", dims.dtype, (H * dims.d_rope, d_q), dev)
+    _need(w_uv, "w_uv", dims.dtype, (H, dims.d_nope, dims.d_latent), dev)
+    _need(seq_lens, "seq_lens", torch.int32, (B,), dev)
+    if page_table.shape[0] < B:
+        raise ValueError("page_table has fewer rows than the batch")
+    if out is None:
+        out = torch.empty((B, H, dims.d_nope), dtype=dims.dtype, device=dev)
+    _need(out, "out", dims.dtype, (B, H, dims.d_nope), dev)
+    need = decode_hidden_workspace_size(dims, B, d_model, d_q, n_workgroups)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    d = dims._c()
+    args = [ctypes.byref(d), ctypes.byref(cache), B, _ptr(seq_lens), d_model, d_q, _ptr(h),
+            _ptr(w_dkv), _ptr(w_kr), _ptr(w_dq), _ptr(w_uqk), _ptr(w_qr), _ptr(w_uv),
+            _ptr(out), _ptr(workspace), wbytes, n_workgroups]
+    evs = _events(timing_events)
+    args.append(evs.ptr)
+    call = _Prepared(lib.mla_decode_hidden_merged, args, keep=(d, cache, seq_lens, h, w_dkv, w_kr, w_dq,
+                                                                w_uqk, w_qr, w_uv, out, workspace, evs,
+                                                                pool, page_table))
+    if prepare:
+        return call, out
+    call(stream)
+    return out
+
+
+def merge_output_weights(dims: Dims, w_o: torch.Tensor, w_uv: torch.Tensor,
+                         w_ov: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """W^OV = [W^O_i W^UV_i]_i (mla_merge_output_weights): w_o [d_model,
+    n_heads * d_nope], w_uv [n_heads, d_nope, d_latent]; returns [d_model,
+    n_heads * d_latent]."""
+    lib = load()
+    H = dims.n_heads
+    if w_o.dim() != 2:
+        raise ValueError("w_o must be [d_model, n_heads * d_nope]")
+    d_model = w_o.shape[0]
+    dev = w_o.device
+    _need(w_o, "w_o", dims.dtype, (d_model, H * dims.d_nope), dev)
+    _need(w_uv, "w_uv", dims.dtype, (H, dims.d_nope, dims.d_latent), dev)
+    if w_ov is None:
+        w_ov = torch.empty((d_model, H * dims.d_latent), dtype=dims.dtype, device=dev)
+    _need(w_ov, "w_ov", dims.dtype, (d_model, H * dims.d_latent), dev)
+    d = dims._c()
+    _check(lib.mla_merge_output_weights(ctypes.byref(d), d_model, _ptr(w_o), _ptr(w_uv), _ptr(w_ov),
+                                        _stream(stream)))
+    return w_ov
+
+
+def decode_layer_merged(dims: Dims, pool: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor,
+                        h: torch.Tensor, w_dkv: torch.Tensor, w_kr: torch.Tensor, w_dq: torch.Tensor,
+                        w_uq: torch.Tensor, w_qr: torch.Tensor, w_uk: torch.Tensor, w_ov: torch.Tensor,
+                        u: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                        n_workgroups: int = 0, stream=None, timing_events=None, prepare: bool = False):
+    """decode_layer with W^UV merged into W^O (mla_decode_layer_merged): w_ov
+    [d_model, n_heads * d_latent] from merge_output_weights replaces w_uv and
+    w_o.  Returns u [batch, d_model]; timing_events bracket the W^OV stage."""
+    lib = load()
+    cache = _cache(dims, pool, page_table)
+    dev = pool.device
+    if h.dim() != 2:
+        raise ValueError("h must be [batch, d_model]")
+    B, d_model = h.shape
+    d_q = w_dq.shape[0] if w_dq.dim() == 2 else -1
+    H = dims.n_heads
+    _need(h, "h", dims.dtype, (B, d_model), dev)
+    _need(w_dkv, "w_dkv", dims.dtype, (dims.d_latent, d_model), dev)
+    _need(w_kr, "w_kr", dims.dtype, (dims.d_rope, d_model), dev)
+    _need(w_dq, "w_dq", dims.dtype, (d_q, d_model), dev)
+    _need(w_uq, "w_uq", dims.dtype, (H * dims.d_nope, d_q), dev)
+    _need(w_qr, "w_qr", dims.dtype, (H * dims.d_rope, d_q), dev)
+    _need(w_uk, "w_uk", dims.dtype, (H, dims.d_nope, dims.d_latent), dev)
+    _need(w_ov, "w_ov", dims.dtype, (d_model, H * dims.d_latent), dev)
+    _need(seq_lens, "seq_lens", torch.int32, (B,), dev)
+    if page_table.shape[0] < B:
+        raise ValueError("page_table has fewer rows than the batch")
+    if u is None:
+        u = torch.empty((B, d_model), dtype=dims.dtype, device=dev)
+    _need(u, "u", dims.dtype, (B, d_model), dev)
+    need = decode_hidden_workspace_size(dims, B, d_model, d_q, n_workgroups)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    d = dims._c()
+    args = [ctypes.byref(d), ctypes.byref(cache), B, _ptr(seq_lens), d_model, d_q, _ptr(h),
+            _ptr(w_dkv), _ptr(w_kr), _ptr(w_dq), _ptr(w_uq), _ptr(w_qr), _ptr(w_uk), _ptr(w_ov),
+            _ptr(u), _ptr(workspace), wbytes, n_workgroups]
+    evs = _events(timing_events)
+    args.append(evs.ptr)
+    call = _Prepared(lib.mla_decode_layer_merged, args, keep=(d, cache, seq_lens, h, w_dkv, w_kr, w_dq,
+                                                               w_uq, w_qr, w_uk, w_ov, u, workspace, evs,
+                                                               pool, page_table))
     if prepare:
         return call, u
     call(stream)

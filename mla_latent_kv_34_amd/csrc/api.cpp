@@ -366,6 +366,115 @@ mla_status mla_decode_layer(const mla_dims* dims, const mla_paged_cache* cache, 
                   "decode layer launch");
 }
 
+mla_status mla_merge_query_weights(const mla_dims* dims, int32_t d_q, const void* w_uq,
+                                  const void* w_uk, void* w_uqk, void* stream) {
+  mla::Layer L;
+  Family fam;
+  MLA_TRY(check_dims(dims, &L, &fam));
+  MLA_TRY(check_front(fam, 64, d_q));
+  MLA_TRY(check_ptr(w_uq, "w_uq"));
+  MLA_TRY(check_ptr(w_uk, "w_uk"));
+  MLA_TRY(check_ptr(w_uqk, "w_uqk"));
+  g_err.clear();
+  return launched(mla::launch_v2_merge_query(L, d_q, w_uq, w_uk, w_uqk, (hipStream_t)stream),
+                  "query weight merge launch");
+}
+
+mla_status mla_decode_hidden_merged(const mla_dims* dims, const mla_paged_cache* cache,
+                                    int32_t batch, const int32_t* seq_lens, int32_t d_model,
+                                    int32_t d_q, const void* h, const void* w_dkv, const void* w_kr,
+                                    const void* w_dq, const void* w_uqk, const void* w_qr,
+                                    const void* w_uv, void* out, void* workspace,
+                                    size_t workspace_bytes, int32_t n_workgroups,
+                                    void* const* timing_events, void* stream) {
+  mla::Layer L;
+  Family fam;
+  MLA_TRY(check_dims(dims, &L, &fam));
+  MLA_TRY(check_cache(cache));
+  MLA_TRY(check_front(fam, d_model, d_q));
+  if (batch < 1) return fail(MLA_ERR_INVALID_ARG, "batch must be >= 1");
+  if ((long long)batch * L.n_heads > 0x7fffffffLL) return fail(MLA_ERR_INVALID_ARG, "batch too large");
+  MLA_TRY(check_idx(seq_lens, "seq_lens"));
+  MLA_TRY(check_ptr(h, "h"));
+  MLA_TRY(check_ptr(w_dkv, "w_dkv"));
+  MLA_TRY(check_ptr(w_kr, "w_kr"));
+  MLA_TRY(check_ptr(w_dq, "w_dq"));
+  MLA_TRY(check_ptr(w_uqk, "w_uqk"));
+  MLA_TRY(check_ptr(w_qr, "w_qr"));
+  MLA_TRY(check_ptr(w_uv, "w_uv"));
+  MLA_TRY(check_ptr(out, "out"));
+  if (n_workgroups < 0 || n_workgroups > 65536)
+    return fail(MLA_ERR_INVALID_ARG, "n_workgroups must be in [0, 65536]");
+  int wg = 0;
+  if (resolve_wg(n_workgroups, &wg) != 0) return fail(MLA_ERR_HIP, "cannot query the device");
+  const size_t need = mla::v2_hidden_workspace(L, batch, wg, d_model, d_q);
+  if (!workspace || workspace_bytes < need)
+    return fail(MLA_ERR_WORKSPACE, "workspace smaller than mla_decode_hidden_workspace_size()");
+  MLA_TRY(check_ptr(workspace, "workspace"));
+  g_err.clear();
+  return launched(mla::launch_v2_decode_hidden_merged(L, cache->pool, cache->num_pages,
+                                                      cache->page_table, cache->max_pages, batch,
+                                                      seq_lens, d_model, d_q, h, w_dkv, w_kr, w_dq,
+                                                      w_uqk, w_qr, w_uv, out, workspace, wg,
+                                                      timing_events, (hipStream_t)stream),
+                  "merged decode from hidden states launch");
+}
+
+mla_status mla_merge_output_weights(const mla_dims* dims, int32_t d_model, const void* w_o,
+                                   const void* w_uv, void* w_ov, void* stream) {
+  mla::Layer L;
+  Family fam;
+  MLA_TRY(check_dims(dims, &L, &fam));
+  MLA_TRY(check_front(fam, d_model, 64));
+  MLA_TRY(check_ptr(w_o, "w_o"));
+  MLA_TRY(check_ptr(w_uv, "w_uv"));
+  MLA_TRY(check_ptr(w_ov, "w_ov"));
+  g_err.clear();
+  return launched(mla::launch_v2_merge_output(L, d_model, w_o, w_uv, w_ov, (hipStream_t)stream),
+                  "output weight merge launch");
+}
+
+mla_status mla_decode_layer_merged(const mla_dims* dims, const mla_paged_cache* cache, int32_t batch,
+                                   const int32_t* seq_lens, int32_t d_model, int32_t d_q,
+                                   const void* h, const void* w_dkv, const void* w_kr,
+                                   const void* w_dq, const void* w_uq, const void* w_qr,
+                                   const void* w_uk, const void* w_ov, void* u, void* workspace,
+                                   size_t workspace_bytes, int32_t n_workgroups,
+                                   void* const* timing_events, void* stream) {
+  mla::Layer L;
+  Family fam;
+  MLA_TRY(check_dims(dims, &L, &fam));
+  MLA_TRY(check_cache(cache));
+  MLA_TRY(check_front(fam, d_model, d_q));
+  if (batch < 1) return fail(MLA_ERR_INVALID_ARG, "batch must be >= 1");
+  if ((long long)batch * L.n_heads > 0x7fffffffLL) return fail(MLA_ERR_INVALID_ARG, "batch too large");
+  MLA_TRY(check_idx(seq_lens, "seq_lens"));
+  MLA_TRY(check_ptr(h, "h"));
+  MLA_TRY(check_ptr(w_dkv, "w_dkv"));
+  MLA_TRY(check_ptr(w_kr, "w_kr"));
+  MLA_TRY(check_ptr(w_dq, "w_dq"));
+  MLA_TRY(check_ptr(w_uq, "w_uq"));
+  MLA_TRY(check_ptr(w_qr, "w_qr"));
+  MLA_TRY(check_ptr(w_uk, "w_uk"));
+  MLA_TRY(check_ptr(w_ov, "w_ov"));
+  MLA_TRY(check_ptr(u, "u"));
+  if (n_workgroups < 0 || n_workgroups > 65536)
+    return fail(MLA_ERR_INVALID_ARG, "n_workgroups must be in [0, 65536]");
+  int wg = 0;
+  if (resolve_wg(n_workgroups, &wg) != 0) return fail(MLA_ERR_HIP, "cannot query the device");
+  const size_t need = mla::v2_hidden_workspace(L, batch, wg, d_model, d_q);
+  if (!workspace || workspace_bytes < need)
+    return fail(MLA_ERR_WORKSPACE, "workspace smaller than mla_decode_hidden_workspace_size()");
+  MLA_TRY(check_ptr(workspace, "workspace"));
+  g_err.clear();
+  return launched(mla::launch_v2_decode_layer_merged(L, cache->pool, cache->num_pages,
+                                                     cache->page_table, cache->max_pages, batch,
+                                                     seq_lens, d_model, d_q, h, w_dkv, w_kr, w_dq,
+                                                     w_uq, w_qr, w_uk, w_ov, u, workspace, wg,
+                                                     timing_events, (hipStream_t)stream),
+                  "merged decode layer launch");
+}
+
 static size_t prefill_need(const mla::Layer& L, Family fam, int batch, int chunk_len, int max_context) {
   return fam == Family::V2 ? mla::v2_prefill_workspace(batch, chunk_len, max_context)
                            : mla::generic_prefill_workspace(L, batch, max_context);

@@ -262,7 +262,9 @@ struct RopeThetas {
 
 // ---------------------------------------------------------------------------
 // q_absorb: q_abs[b, i, 0:512] = W^UK_i^T q^C_{b,i}, q_abs[b, i, 512:576] =
-// RoPE(q^R_{b,i}, seq_len_b - 1).  One workgroup per (head, 128-column chunk),
+// RoPE(q^R_{b,i}, seq_len_b - 1).  With q_lat given ([B, H, 512], the first
+// part already absorbed, e.g. by a pre-merged W^UK_i^T W^UQ_i) that part is
+// copied into the fragment layout instead.  One workgroup per (head, 128-column chunk),
 // after workgroup 0, which builds the split plan (plan_block).
 // D^T[c][b] = sum_r W[r][c] q[b][r] with W^T read from LDS by transpose reads.
 // ---------------------------------------------------------------------------
@@ -272,7 +274,8 @@ q_absorb_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __restrict_
                 RopeThetas rope, uint16_t* __restrict__ q_abs, int W, int32_t* __restrict__ plan,
                 long long* __restrict__ plan_u, int4* __restrict__ plan_wg, uint16_t* __restrict__ pool, int num_pages,
                 const int32_t* __restrict__ table, int max_pages, const uint16_t* __restrict__ c_new,
-                const uint16_t* __restrict__ k_new, double rope_base) {
+                const uint16_t* __restrict__ k_new, double rope_base,
+                const uint16_t* __restrict__ q_lat) {
   // workgroup 0 builds the split plan; it is dispatched first, so it runs
   // beside the absorption workgroups instead of after them
   // W^UK_h[:, c0:c0+128] as two [128 rows r][64 cols] halves, swizzled
@@ -341,11 +344,11 @@ q_absorb_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __restrict_
     }
   };
   rope_loads(i0_first);
-  if (wave < 4 * nblk) load_q(wave, bq);
+  if (!q_lat && wave < 4 * nblk) load_q(wave, bq);
   // W^UK_h[:, c0:c0+128] straight into LDS as two [128 rows r][64 cols]
   // halves with 16-byte chunk c of row r at chunk c ^ swz_w(r): 16-byte unit
   // U = (4m + wave) * 64 + lane of the tile is written by load m of the wave
-  {
+  if (!q_lat) {
     const int wv = __builtin_amdgcn_readfirstlane(wave);
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
@@ -387,6 +390,16 @@ q_absorb_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __restrict_
   for (int i0 = i0_first + 2 * 4 * 256; i0 < B * PER; i0 += 2 * 4 * 256) {
     rope_loads(i0);
     rope_round(i0);
+  }
+  if (q_lat) {
+    // the latent part given: 4 consecutive dims are contiguous in the
+    // fragment layout
+    for (int i = tid; i < B * 32; i += 256) {
+      const int b = i >> 5, c = c0 + 4 * (i & 31);
+      *(ushort4*)(q_abs + qfrag_index(b, h, c)) =
+          *(const ushort4*)(q_lat + ((size_t)b * H + h) * DL + c);
+    }
+    return;
   }
   // the tile copies (the oldest loads of this thread) are complete
   __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
@@ -818,6 +831,9 @@ decode_splitkv_kernel(const char* __restrict__ pool, int num_pages, const int32_
 //  2. out_absorb (waves 0-3): out[b, h, r] = sum_c W^UV[h, r, c] o_lat[b, c]
 //     as O^T = W^UV_h o_lat^T; wave v owns rows 32v..32v+31, its W^UV
 //     fragments are loaded before step 1 so their latency hides behind it.
+// With olat_out given, step 1 also writes o_lat (the bf16 hi part, i.e.
+// o_lat rounded to nearest even) to olat_out[b, h, :] and step 2 is skipped:
+// the caller applies W^UV merged into W^O.
 // LDS rows are 1 KiB (512 bf16); chunk c of row b sits at chunk c ^ (b & 15),
 // so a 16-lane read of one chunk of 16 rows hits 16 distinct bank groups.
 // ---------------------------------------------------------------------------
@@ -827,7 +843,7 @@ constexpr int CO_NT = 512;
 __global__ void __launch_bounds__(CO_NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 combine_out_kernel(const int32_t* __restrict__ plan, int B, const float* __restrict__ part_ml,
                    const uint16_t* __restrict__ part_o, const uint16_t* __restrict__ w_uv,
-                   uint16_t* __restrict__ out) {
+                   uint16_t* __restrict__ out, uint16_t* __restrict__ olat_out) {
   // the bf16 hi / lo rows of o_lat; before they are written, the same bytes
   // hold the per-group partials of a block with fewer than CO_NB sequences
   __shared__ __attribute__((aligned(16))) char lds[2 * CO_NB * DL * 2];
@@ -846,7 +862,7 @@ combine_out_kernel(const int32_t* __restrict__ plan, int B, const float* __restr
 
   // W^UV_h rows 32 * wave + n: the A operand of every k-step (waves 0-3)
   bf16x8 wf[DL / 16];
-  if (wave < 4) {
+  if (wave < 4 && !olat_out) {
     const uint16_t* wr = w_uv + ((size_t)h * DC + 32 * wave + n) * DL + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < DL / 16; ++ks) wf[ks] = *(const bf16x8*)(wr + 16 * ks);
@@ -965,6 +981,8 @@ combine_out_kernel(const int32_t* __restrict__ plan, int B, const float* __restr
           const int byte = i * (DL * 2) + (((c >> 3) ^ (i & 15)) << 4) + (c & 7) * 2;
           *(uint2*)(ohi + byte) = make_uint2(hi2[0], hi2[1]);
           *(uint2*)(olo + byte) = make_uint2(lo2[0], lo2[1]);
+          if (olat_out)
+            *(uint2*)(olat_out + ((size_t)b * H + h) * DL + c) = make_uint2(hi2[0], hi2[1]);
         }
       }
     }
@@ -978,7 +996,7 @@ combine_out_kernel(const int32_t* __restrict__ plan, int B, const float* __restr
     }
   }
   __syncthreads();
-  if (wave >= 4) return;
+  if (wave >= 4 || olat_out) return;
   // ---- 2. O^T[r][b] = sum_c W[r][c] o_lat[b][c]
   f32x16 acc = {};
 #pragma unroll
@@ -1012,7 +1030,7 @@ hipError_t launch_v2_decode(const Layer& L, const void* pool, int num_pages, con
                             int max_pages, int batch, const int32_t* seq_lens, const void* q_nope,
                             const void* q_rope, const void* w_uk, const void* w_uv, void* out,
                             void* ws, int n_wg, void* const* ev, hipStream_t s, const void* c_new,
-                            const void* k_new) {
+                            const void* k_new, const void* q_lat, void* olat_out) {
   using namespace v2;
   const WsLayout lay(batch, n_wg);
   char* base = (char*)ws;
@@ -1031,7 +1049,8 @@ hipError_t launch_v2_decode(const Layer& L, const void* pool, int num_pages, con
   hipLaunchKernelGGL(q_absorb_kernel, dim3(H * 4 + 1 + app_blocks), dim3(256), 0, s,
                      (const uint16_t*)q_nope, (const uint16_t*)q_rope, (const uint16_t*)w_uk,
                      seq_lens, batch, th, q_abs, n_wg, plan, plan_u, plan_wg, (uint16_t*)pool, num_pages,
-                     table, max_pages, (const uint16_t*)c_new, (const uint16_t*)k_new, L.rope_base);
+                     table, max_pages, (const uint16_t*)c_new, (const uint16_t*)k_new, L.rope_base,
+                     (const uint16_t*)q_lat);
   hipError_t e = mark(ev, 0, s);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_splitkv_kernel, dim3(n_wg), dim3(256), 0, s, (const char*)pool,
@@ -1040,7 +1059,8 @@ hipError_t launch_v2_decode(const Layer& L, const void* pool, int num_pages, con
   e = mark(ev, 1, s);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(combine_out_kernel, dim3(H * ((batch + CO_NB - 1) / CO_NB)), dim3(CO_NT), 0, s,
-                     plan, batch, part_ml, part_o, (const uint16_t*)w_uv, (uint16_t*)out);
+                     plan, batch, part_ml, part_o, (const uint16_t*)w_uv, (uint16_t*)out,
+                     (uint16_t*)olat_out);
   return hipGetLastError();
 }
 

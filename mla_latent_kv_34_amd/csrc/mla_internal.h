@@ -113,11 +113,38 @@ size_t v2_decode_workspace(int batch, int n_wg);
 // c_new / k_new: NULL, or the token at position seq_lens[b] - 1 of every
 // sequence ([batch, d_latent], [batch, d_rope]), appended to the cache by the
 // first kernel of the decode (before any cache read).
+// q_lat: NULL, or the absorbed content queries W^UK_i^T q^C_i already formed
+// ([batch, n_heads, d_latent]); q_nope and w_uk are then not read.
+// olat_out: NULL, or [batch, n_heads, d_latent] that receives the normalised
+// latent outputs o_lat (bf16) in place of out = W^UV o_lat (w_uv, out unused).
 hipError_t launch_v2_decode(const Layer& L, const void* pool, int num_pages, const int32_t* table,
                             int max_pages, int batch, const int32_t* seq_lens, const void* q_nope,
                             const void* q_rope, const void* w_uk, const void* w_uv, void* out,
                             void* ws, int n_wg, void* const* ev, hipStream_t s,
-                            const void* c_new = nullptr, const void* k_new = nullptr);
+                            const void* c_new = nullptr, const void* k_new = nullptr,
+                            const void* q_lat = nullptr, void* olat_out = nullptr);
+// W^OV = [W^O_i W^UV_i]_i ([d_model, n_heads * d_latent], fp32 sums, bf16 RNE) (proj.hip)
+hipError_t launch_v2_merge_output(const Layer& L, int d_model, const void* w_o, const void* w_uv,
+                                  void* w_ov, hipStream_t s);
+// mla_decode_hidden up to o_lat, then u = W^OV [o_lat_1; ...; o_lat_nh]
+hipError_t launch_v2_decode_layer_merged(const Layer& L, const void* pool, int num_pages,
+                                         const int32_t* table, int max_pages, int batch,
+                                         const int32_t* seq_lens, int d_model, int d_q,
+                                         const void* h, const void* w_dkv, const void* w_kr,
+                                         const void* w_dq, const void* w_uq, const void* w_qr,
+                                         const void* w_uk, const void* w_ov, void* u, void* ws,
+                                         int n_wg, void* const* ev, hipStream_t s);
+// W^UQK_i = W^UK_i^T W^UQ_i ([n_heads, d_latent, d_q], fp32 sums, bf16 RNE) (proj.hip)
+hipError_t launch_v2_merge_query(const Layer& L, int d_q, const void* w_uq, const void* w_uk,
+                                 void* w_uqk, hipStream_t s);
+// mla_decode_hidden with the merged query weight in place of W^UQ and W^UK
+hipError_t launch_v2_decode_hidden_merged(const Layer& L, const void* pool, int num_pages,
+                                          const int32_t* table, int max_pages, int batch,
+                                          const int32_t* seq_lens, int d_model, int d_q,
+                                          const void* h, const void* w_dkv, const void* w_kr,
+                                          const void* w_dq, const void* w_uqk, const void* w_qr,
+                                          const void* w_uv, void* out, void* ws, int n_wg,
+                                          void* const* ev, hipStream_t s);
 // projections from hidden states, then the decode step (proj.hip)
 size_t v2_hidden_workspace(const Layer& L, int batch, int n_wg, int d_model, int d_q);
 hipError_t launch_v2_decode_hidden(const Layer& L, const void* pool, int num_pages,

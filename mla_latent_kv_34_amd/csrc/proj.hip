@@ -281,8 +281,14 @@ int choose_split(int n_total, int K) {
   return s;
 }
 
+// fp32 partial bytes of one projection stage (0 when it is not split)
+size_t part_bytes(int n_total, int K, int batch) {
+  const int ks = choose_split(n_total, K);
+  return ks > 1 ? (size_t)ks * n_total * batch * 4 : 0;
+}
+
 struct HiddenLayout {
-  size_t c_kv, k_r, c_q, q_nope, q_rope, o, part, decode, total;
+  size_t c_kv, k_r, c_q, q_nope, q_rope, o, q_lat, part, decode, total;
   HiddenLayout(const Layer& L, int batch, int n_wg, int d_model, int d_q) {
     auto al = [](size_t v) { return (v + 255) & ~(size_t)255; };
     const size_t B = (size_t)batch;
@@ -292,12 +298,15 @@ struct HiddenLayout {
     q_nope = al(c_q + B * d_q * 2);
     q_rope = al(q_nope + B * L.n_heads * L.d_nope * 2);
     o = al(q_rope + B * L.n_heads * L.d_rope * 2);
-    part = al(o + B * L.n_heads * L.d_nope * 2);
+    q_lat = al(o + B * L.n_heads * L.d_nope * 2);
+    part = al(q_lat + B * L.n_heads * L.d_latent * 2);
     const int n1 = L.d_latent + L.d_rope + d_q, n2 = L.n_heads * (L.d_nope + L.d_rope);
-    const size_t p1 = (size_t)choose_split(n1, d_model) * n1 * B * 4;
-    const size_t p2 = (size_t)choose_split(n2, d_q) * n2 * B * 4;
-    const size_t p3 = (size_t)choose_split(d_model, L.n_heads * L.d_nope) * d_model * B * 4;
-    decode = al(part + std::max(p1, std::max(p2, p3)));
+    const int n2m = L.n_heads * (L.d_latent + L.d_rope);
+    const size_t p = std::max(
+        std::max(std::max(part_bytes(n1, d_model, batch), part_bytes(n2, d_q, batch)),
+                 std::max(part_bytes(d_model, L.n_heads * L.d_nope, batch), part_bytes(n2m, d_q, batch))),
+        part_bytes(d_model, L.n_heads * L.d_latent, batch));
+    decode = al(part + p);
     total = decode + v2_decode_workspace(batch, n_wg);
   }
 };
@@ -315,7 +324,177 @@ hipError_t launch_stage(const uint16_t* x, int M, int K, const Segs& segs, float
   return hipGetLastError();
 }
 
+// (1) h -> [c^KV | k^R | c^Q] (W^DKV, W^KR, W^DQ laid end to end)
+hipError_t launch_key_stage(const Layer& L, int batch, int d_model, int d_q, const void* h,
+                            const void* w_dkv, const void* w_kr, const void* w_dq, uint16_t* c_kv,
+                            uint16_t* k_r, uint16_t* c_q, float* part, hipStream_t s) {
+  Segs s1{};
+  s1.s[0] = Seg{(const uint16_t*)w_dkv, c_kv, L.d_latent};
+  s1.s[1] = Seg{(const uint16_t*)w_kr, k_r, L.d_rope};
+  s1.s[2] = Seg{(const uint16_t*)w_dq, c_q, d_q};
+  s1.count = 3;
+  s1.n_total = L.d_latent + L.d_rope + d_q;
+  return launch_stage((const uint16_t*)h, batch, d_model, s1, part, s);
+}
+
+// w_uqk[h][c][j] = sum_r w_uk[h][r][c] w_uq[h d_nope + r][j] in fp32, rounded
+// to bf16.  A one-time weight preparation, not part of a step: one block per
+// (head, 16 latent columns) keeps that W^UK slice in LDS and sweeps j with
+// coalesced reads of W^UQ and writes of the result.
+__global__ void __launch_bounds__(256)
+merge_query_kernel(const uint16_t* __restrict__ w_uq, const uint16_t* __restrict__ w_uk,
+                   int d_nope, int d_lat, int d_q, uint16_t* __restrict__ w_uqk) {
+  __shared__ float wk[128][16];
+  const int per = d_lat / 16;
+  const int h = (int)blockIdx.x / per, c0 = ((int)blockIdx.x % per) * 16;
+  for (int i = threadIdx.x; i < d_nope * 16; i += 256) {
+    const int r = i >> 4, c = i & 15;
+    wk[r][c] = bf16_bits_to_f32(w_uk[((size_t)h * d_nope + r) * d_lat + c0 + c]);
+  }
+  __syncthreads();
+  for (int j = threadIdx.x; j < d_q; j += 256) {
+    float acc[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) acc[c] = 0.f;
+    for (int r = 0; r < d_nope; ++r) {
+      const float u = bf16_bits_to_f32(w_uq[((size_t)h * d_nope + r) * d_q + j]);
+#pragma unroll
+      for (int c = 0; c < 16; ++c) acc[c] = __builtin_fmaf(wk[r][c], u, acc[c]);
+    }
+#pragma unroll
+    for (int c = 0; c < 16; ++c)
+      w_uqk[((size_t)h * d_lat + c0 + c) * d_q + j] = bf16_bits_rne_f32(acc[c]);
+  }
+}
+
+// w_ov[j][h d_lat + c] = sum_r w_o[j][h d_nope + r] w_uv[h][r][c] in fp32,
+// rounded to bf16.  A one-time weight preparation: one block per (head, 16
+// output rows) keeps those W^O entries in LDS and sweeps c with coalesced
+// reads of W^UV and writes of the result.
+__global__ void __launch_bounds__(256)
+merge_output_kernel(const uint16_t* __restrict__ w_o, const uint16_t* __restrict__ w_uv,
+                    int n_heads, int d_nope, int d_lat, uint16_t* __restrict__ w_ov) {
+  __shared__ float wo[16][128];
+  const int nh_dn = n_heads * d_nope;
+  const int h = (int)blockIdx.x % n_heads, j0 = ((int)blockIdx.x / n_heads) * 16;
+  for (int i = threadIdx.x; i < 16 * d_nope; i += 256) {
+    const int jj = i / d_nope, r = i % d_nope;
+    wo[jj][r] = bf16_bits_to_f32(w_o[(size_t)(j0 + jj) * nh_dn + (size_t)h * d_nope + r]);
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < d_lat; c += 256) {
+    float acc[16];
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) acc[jj] = 0.f;
+    for (int r = 0; r < d_nope; ++r) {
+      const float v = bf16_bits_to_f32(w_uv[((size_t)h * d_nope + r) * d_lat + c]);
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) acc[jj] = __builtin_fmaf(wo[jj][r], v, acc[jj]);
+    }
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj)
+      w_ov[(size_t)(j0 + jj) * n_heads * d_lat + (size_t)h * d_lat + c] = bf16_bits_rne_f32(acc[jj]);
+  }
+}
+
 }  // namespace pj
+
+hipError_t launch_v2_merge_output(const Layer& L, int d_model, const void* w_o, const void* w_uv,
+                                  void* w_ov, hipStream_t s) {
+  if (L.d_nope > 128 || d_model % 16) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(pj::merge_output_kernel, dim3((unsigned)(L.n_heads * (d_model / 16))), dim3(256),
+                     0, s, (const uint16_t*)w_o, (const uint16_t*)w_uv, L.n_heads, L.d_nope,
+                     L.d_latent, (uint16_t*)w_ov);
+  return hipGetLastError();
+}
+
+// The attention layer of a decode step with W^UV merged into W^O: the
+// projections and the decode as mla_decode_hidden, except that the decode
+// stops at the normalised latent outputs o_lat, then u = W^OV o_lat as one
+// projection stage with K = n_h d_c.
+hipError_t launch_v2_decode_layer_merged(const Layer& L, const void* pool, int num_pages,
+                                         const int32_t* table, int max_pages, int batch,
+                                         const int32_t* seq_lens, int d_model, int d_q,
+                                         const void* h, const void* w_dkv, const void* w_kr,
+                                         const void* w_dq, const void* w_uq, const void* w_qr,
+                                         const void* w_uk, const void* w_ov, void* u, void* ws,
+                                         int n_wg, void* const* ev, hipStream_t s) {
+  using namespace pj;
+  const HiddenLayout lay(L, batch, n_wg, d_model, d_q);
+  char* w = (char*)ws;
+  uint16_t* c_kv = (uint16_t*)(w + lay.c_kv);
+  uint16_t* k_r = (uint16_t*)(w + lay.k_r);
+  uint16_t* c_q = (uint16_t*)(w + lay.c_q);
+  uint16_t* q_nope = (uint16_t*)(w + lay.q_nope);
+  uint16_t* q_rope = (uint16_t*)(w + lay.q_rope);
+  uint16_t* o_lat = (uint16_t*)(w + lay.q_lat);
+  float* part = (float*)(w + lay.part);
+  hipError_t e = launch_key_stage(L, batch, d_model, d_q, h, w_dkv, w_kr, w_dq, c_kv, k_r, c_q, part, s);
+  if (e != hipSuccess) return e;
+  Segs s2{};
+  s2.s[0] = Seg{(const uint16_t*)w_uq, q_nope, L.n_heads * L.d_nope};
+  s2.s[1] = Seg{(const uint16_t*)w_qr, q_rope, L.n_heads * L.d_rope};
+  s2.count = 2;
+  s2.n_total = L.n_heads * (L.d_nope + L.d_rope);
+  if ((e = launch_stage(c_q, batch, d_q, s2, part, s)) != hipSuccess) return e;
+  if ((e = launch_v2_decode(L, pool, num_pages, table, max_pages, batch, seq_lens, q_nope, q_rope, w_uk,
+                            nullptr, nullptr, w + lay.decode, n_wg, nullptr, s, c_kv, k_r, nullptr,
+                            o_lat)) != hipSuccess)
+    return e;
+  if (ev && ev[0] && (e = hipEventRecord((hipEvent_t)ev[0], s)) != hipSuccess) return e;
+  Segs s3{};
+  s3.s[0] = Seg{(const uint16_t*)w_ov, (uint16_t*)u, d_model};
+  s3.count = 1;
+  s3.n_total = d_model;
+  if ((e = launch_stage(o_lat, batch, L.n_heads * L.d_latent, s3, part, s)) != hipSuccess) return e;
+  if (ev && ev[1] && (e = hipEventRecord((hipEvent_t)ev[1], s)) != hipSuccess) return e;
+  return hipSuccess;
+}
+
+hipError_t launch_v2_merge_query(const Layer& L, int d_q, const void* w_uq, const void* w_uk,
+                                 void* w_uqk, hipStream_t s) {
+  if (L.d_nope > 128 || L.d_latent % 16) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(pj::merge_query_kernel, dim3((unsigned)(L.n_heads * (L.d_latent / 16))),
+                     dim3(256), 0, s, (const uint16_t*)w_uq, (const uint16_t*)w_uk, L.d_nope,
+                     L.d_latent, d_q, (uint16_t*)w_uqk);
+  return hipGetLastError();
+}
+
+// The decode step from hidden states with the pre-merged query weight: stage
+// (1) as mla_decode_hidden, stage (2) c^Q -> [q_lat | q^R] with W^UQK and W^QR
+// laid end to end (q_lat_i = W^UQK_i c^Q is the absorbed content query), then
+// the decode with q_lat in place of q^C and W^UK.
+hipError_t launch_v2_decode_hidden_merged(const Layer& L, const void* pool, int num_pages,
+                                          const int32_t* table, int max_pages, int batch,
+                                          const int32_t* seq_lens, int d_model, int d_q,
+                                          const void* h, const void* w_dkv, const void* w_kr,
+                                          const void* w_dq, const void* w_uqk, const void* w_qr,
+                                          const void* w_uv, void* out, void* ws, int n_wg,
+                                          void* const* ev, hipStream_t s) {
+  using namespace pj;
+  const HiddenLayout lay(L, batch, n_wg, d_model, d_q);
+  char* w = (char*)ws;
+  uint16_t* c_kv = (uint16_t*)(w + lay.c_kv);
+  uint16_t* k_r = (uint16_t*)(w + lay.k_r);
+  uint16_t* c_q = (uint16_t*)(w + lay.c_q);
+  uint16_t* q_lat = (uint16_t*)(w + lay.q_lat);
+  uint16_t* q_rope = (uint16_t*)(w + lay.q_rope);
+  float* part = (float*)(w + lay.part);
+  hipError_t e = hipSuccess;
+  if (ev && ev[0] && (e = hipEventRecord((hipEvent_t)ev[0], s)) != hipSuccess) return e;
+  if ((e = launch_key_stage(L, batch, d_model, d_q, h, w_dkv, w_kr, w_dq, c_kv, k_r, c_q, part, s)) !=
+      hipSuccess)
+    return e;
+  Segs s2{};
+  s2.s[0] = Seg{(const uint16_t*)w_uqk, q_lat, L.n_heads * L.d_latent};
+  s2.s[1] = Seg{(const uint16_t*)w_qr, q_rope, L.n_heads * L.d_rope};
+  s2.count = 2;
+  s2.n_total = L.n_heads * (L.d_latent + L.d_rope);
+  if ((e = launch_stage(c_q, batch, d_q, s2, part, s)) != hipSuccess) return e;
+  if (ev && ev[1] && (e = hipEventRecord((hipEvent_t)ev[1], s)) != hipSuccess) return e;
+  return launch_v2_decode(L, pool, num_pages, table, max_pages, batch, seq_lens, nullptr, q_rope,
+                          nullptr, w_uv, out, w + lay.decode, n_wg, nullptr, s, c_kv, k_r, q_lat);
+}
 
 size_t v2_hidden_workspace(const Layer& L, int batch, int n_wg, int d_model, int d_q) {
   return pj::HiddenLayout(L, batch, n_wg, d_model, d_q).total;
@@ -339,14 +518,9 @@ hipError_t launch_v2_decode_hidden(const Layer& L, const void* pool, int num_pag
   float* part = (float*)(w + lay.part);
   hipError_t e = hipSuccess;
   if (ev && ev[0] && (e = hipEventRecord((hipEvent_t)ev[0], s)) != hipSuccess) return e;
-  // (1) h -> [c^KV | k^R | c^Q]
-  Segs s1{};
-  s1.s[0] = Seg{(const uint16_t*)w_dkv, c_kv, L.d_latent};
-  s1.s[1] = Seg{(const uint16_t*)w_kr, k_r, L.d_rope};
-  s1.s[2] = Seg{(const uint16_t*)w_dq, c_q, d_q};
-  s1.count = 3;
-  s1.n_total = L.d_latent + L.d_rope + d_q;
-  if ((e = launch_stage((const uint16_t*)h, batch, d_model, s1, part, s)) != hipSuccess) return e;
+  if ((e = launch_key_stage(L, batch, d_model, d_q, h, w_dkv, w_kr, w_dq, c_kv, k_r, c_q, part, s)) !=
+      hipSuccess)
+    return e;
   // (2) c^Q -> [q^C | q^R]
   Segs s2{};
   s2.s[0] = Seg{(const uint16_t*)w_uq, q_nope, L.n_heads * L.d_nope};
