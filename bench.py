@@ -210,6 +210,7 @@ def main():
         r = reps[i % len(reps)]
         torch.cuda.synchronize()
         kern_ms.append(r["ev"][0].elapsed_time(r["ev"][1]))
+    kern_pct = [round(float(v), 5) for v in np.percentile(kern_ms, [10, 50, 90])]
     kern_ms = float(np.mean(kern_ms))
 
     # ---- graph replay of the same steps
@@ -319,6 +320,7 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
             "kernel_ms": round(kern_ms, 5),
+            "kernel_ms_p10_p50_p90": kern_pct,
             "algorithmic_bytes": cache_bytes,
             "mfma": {"achieved": round(kern_tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(kern_tflops / MFMA_BF16_PEAK_TFLOPS, 4)},
