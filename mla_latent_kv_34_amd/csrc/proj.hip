@@ -1,9 +1,14 @@
-// The projections in front of the decode for the DeepSeek-V2 sizes on gfx950
-// ("MLA low-rank attention" tech note [three-branch computation]):
+// The dense projections around the decode for the DeepSeek-V2 sizes on gfx950.
+// In front ("MLA low-rank attention" tech note [three-branch computation]):
 //   (1) Query: c^Q = W^DQ h, q^C = W^UQ c^Q and q^R = W^QR c^Q (split by heads);
 //   (2) Key:   c^KV = W^DKV h and k^R = W^KR h (from h, shared by all heads).
 // q^R and k^R are rotated later (the decode's first kernel rotates q^R at the
 // query position and writes the new cache row [c^KV ; RoPE(k^R, pos)]).
+// After it ([(4) attention and output]): u = W^O [o_1; ...; o_nh].
+// Pre-merged forms ("From LLaMA to DeepSeek [01]" [section 6]: fixed matrices
+// multiplied in advance): q_lat_i = (W^UK_i^T W^UQ_i) c^Q in place of (1)'s
+// q^C and the decode's absorption, and u = [W^O_i W^UV_i]_i o_lat in place of
+// the decode's W^UV and W^O.
 //
 // Each projection is y = x W^T with x [M, K] bf16, W [N, K] bf16 (out x in),
 // fp32 accumulation and a bf16 (round-to-nearest-even) result.  For a decode
