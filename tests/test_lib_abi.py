@@ -129,3 +129,40 @@ def test_prefill_chunk_rejections_on_host(lib):
         lib.mla_prefill_chunk_workspace_size(ctypes.byref(v2), 2, 4096, 4096)
     assert lib.mla_prefill_chunk_workspace_size(ctypes.byref(v2), 2, 512, 4096) > \
         lib.mla_prefill_chunk_workspace_size(ctypes.byref(v2), 2, 512, 512)
+
+
+def test_layer_and_merge_rejections_on_host(lib):
+    """The layer, merged-weight and merge entry points validate on the host:
+    the generic family is unsupported, K sizes must be multiples of 64, and a
+    NULL weight is named in the error."""
+    cache = _lib._Cache(0x1000, 1, 1, 0x2000)   # never dereferenced
+    tiny = _dims(n_heads=4, d_nope=16, d_rope=8, d_latent=32, dtype=1)
+    v2 = _dims()
+    P = [0x4000 + 0x1000 * i for i in range(12)]
+
+    # pointer arguments in order: h, W^DKV, W^KR, W^DQ, W^UQ, W^QR, W^UK, then
+    # W^UV, W^O (mla_decode_layer) or W^OV (mla_decode_layer_merged), then u, workspace
+    def layer(fn, n_ptr, d, dm, dq, nulled=None):
+        ptrs = list(P[:n_ptr])
+        if nulled is not None:
+            ptrs[nulled] = None
+        return fn(ctypes.byref(d), ctypes.byref(cache), 1, 0x3000, dm, dq, *ptrs, 1 << 30, 0, None, None)
+
+    for fn, n_ptr, name in ((lib.mla_decode_layer, 11, b"w_o"), (lib.mla_decode_layer_merged, 10, b"w_ov")):
+        assert len(fn.argtypes) == 6 + n_ptr + 4
+        assert layer(fn, n_ptr, tiny, 128, 64) == mla.MLA_ERR_UNSUPPORTED
+        assert layer(fn, n_ptr, v2, 5000, 1536) == mla.MLA_ERR_INVALID_ARG
+        assert b"d_model" in lib.mla_last_error()
+        assert layer(fn, n_ptr, v2, 5120, 1536, nulled=n_ptr - 3) == mla.MLA_ERR_INVALID_ARG
+        assert name + b" is NULL" in lib.mla_last_error(), lib.mla_last_error()
+    assert len(lib.mla_decode_hidden_merged.argtypes) == 6 + 9 + 4
+    hm = lambda d, dm, dq: lib.mla_decode_hidden_merged(  # noqa: E731
+        ctypes.byref(d), ctypes.byref(cache), 1, 0x3000, dm, dq, *P[:9], 1 << 30, 0, None, None)
+    assert hm(tiny, 128, 64) == mla.MLA_ERR_UNSUPPORTED
+    assert hm(v2, 5120, 100) == mla.MLA_ERR_INVALID_ARG and b"d_q" in lib.mla_last_error()
+    assert lib.mla_merge_query_weights(ctypes.byref(tiny), 64, P[0], P[1], P[2], None) == mla.MLA_ERR_UNSUPPORTED
+    assert lib.mla_merge_query_weights(ctypes.byref(v2), 1536, P[0], None, P[2], None) == mla.MLA_ERR_INVALID_ARG
+    assert b"w_uk" in lib.mla_last_error()
+    assert lib.mla_merge_output_weights(ctypes.byref(v2), 5000, P[0], P[1], P[2], None) == mla.MLA_ERR_INVALID_ARG
+    assert lib.mla_merge_output_weights(ctypes.byref(v2), 5120, P[0], P[1], None, None) == mla.MLA_ERR_INVALID_ARG
+    assert b"w_ov" in lib.mla_last_error()
