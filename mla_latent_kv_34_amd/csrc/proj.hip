@@ -276,13 +276,16 @@ proj_reduce_kernel(const float* __restrict__ part, int M, int ksplit, Segs segs)
   *(ushort4*)(sg.out + (size_t)m * sg.rows + (row - base)) = o;
 }
 
-// K slices per launch: at least PJ_MIN_WG workgroups, a power of two
+// K slices per launch: at least PJ_MIN_WG workgroups (twice that for long K,
+// where the fp32 partials stay small next to the weights), a power of two
 // dividing K / KC.
 constexpr int kMinWorkgroups = PJ_MIN_WG;
+constexpr int kLongK = 8192;
 int choose_split(int n_total, int K) {
   const int tiles = (n_total + WR - 1) / WR;
+  const int target = K >= kLongK ? 2 * kMinWorkgroups : kMinWorkgroups;
   int s = 1;
-  while (tiles * s < kMinWorkgroups && (K / KC) % (2 * s) == 0) s *= 2;
+  while (tiles * s < target && (K / KC) % (2 * s) == 0) s *= 2;
   return s;
 }
 
