@@ -11,7 +11,7 @@ from oracle import decode_ref, front_end, output_proj
 
 pytestmark = pytest.mark.gpu
 
-from gpu_common import DEV, assert_close, canary_pool, f64, fill_cache, lib_dims  # noqa: E402
+from gpu_common import DEV, assert_close, bf16_round, canary_pool, f64, fill_cache, lib_dims  # noqa: E402
 
 
 def _run(hc: syn.HiddenCase, w_o: torch.Tensor, seq_lens=None):
@@ -34,7 +34,8 @@ def _oracle(hc: syn.HiddenCase, w_o: torch.Tensor, b: int):
     (every head), then W^O."""
     base = hc.base
     f = [w.double().numpy() for w in hc.front]
-    c_new, k_new, q_c, q_r = front_end(hc.h[b].double().numpy(), *f, n_heads=base.dims.n_heads)
+    c_new, k_new, q_c, q_r = (bf16_round(t) for t in
+                              front_end(hc.h[b].double().numpy(), *f, n_heads=base.dims.n_heads))
     c_rows, k_rows = base.seq_rows(b)
     n = int(base.cached[b])
     c_all = np.vstack([c_rows[:n].double().numpy(), c_new[None]])
