@@ -158,7 +158,7 @@ size_t mla_decode_hidden_workspace_size(const mla_dims* dims, int32_t batch, int
  * accumulate in fp32 and round their outputs to bf16 (round to nearest
  * even), the storage dtype the step's inputs have.
  * d_model: d (K of the first projections); d_q: d_c' (K of W^UQ and W^QR);
- *   both positive multiples of 64.
+ *   in [1, 2^20], and multiples of 64 for the V2 sizes.
  * h:     [batch, d_model] (the token at position seq_lens[b] - 1)
  * w_dkv: [d_latent, d_model]   w_kr: [d_rope, d_model]   w_dq: [d_q, d_model]
  * w_uq:  [n_heads * d_nope, d_q]   w_qr: [n_heads * d_rope, d_q]
@@ -167,8 +167,11 @@ size_t mla_decode_hidden_workspace_size(const mla_dims* dims, int32_t batch, int
  * workspace: at least mla_decode_hidden_workspace_size(...) bytes.
  * timing_events: NULL, or two hipEvent_t recorded immediately before the
  *   first projection and after the last one (profiling only).
- * Only the MFMA family (V2 sizes, bf16) implements it: other sizes return
- * MLA_ERR_UNSUPPORTED.  Other errors as for mla_decode_step.               */
+ * Both kernel families implement it: the MFMA family streams the weights
+ * through LDS; the generic family (small layers, either dtype) runs plain
+ * fp32-accumulating projections and stores the projected tensors in the
+ * layer's dtype.  Errors as for mla_decode_step; the generic family also
+ * needs batch <= 65535.                                                     */
 mla_status mla_decode_hidden(const mla_dims* dims, const mla_paged_cache* cache, int32_t batch,
                              const int32_t* seq_lens, int32_t d_model, int32_t d_q, const void* h,
                              const void* w_dkv, const void* w_kr, const void* w_dq,
@@ -188,8 +191,8 @@ mla_status mla_decode_hidden(const mla_dims* dims, const mla_paged_cache* cache,
  *   layout, which holds the heads' outputs o between the two steps).
  * timing_events: NULL, or two hipEvent_t recorded immediately before and
  *   after the W^O projection (profiling only).
- * Every other argument and error as for mla_decode_hidden (MLA_ERR_UNSUPPORTED
- * outside the V2 sizes).                                                    */
+ * Every other argument and error as for mla_decode_hidden (both kernel
+ * families).                                                                */
 mla_status mla_decode_layer(const mla_dims* dims, const mla_paged_cache* cache, int32_t batch,
                             const int32_t* seq_lens, int32_t d_model, int32_t d_q, const void* h,
                             const void* w_dkv, const void* w_kr, const void* w_dq,

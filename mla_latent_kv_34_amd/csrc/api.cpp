@@ -261,17 +261,44 @@ mla_status mla_decode_step(const mla_dims* dims, const mla_paged_cache* cache, i
 }
 
 namespace {
-// sizes of the projections in front of the decode: V2 family only; the K of
-// both projection stages must be a multiple of 64 (one 64-wide step per
-// weight line pass) and below 2^20
-mla_status check_front(Family fam, int32_t d_model, int32_t d_q) {
-  if (fam != Family::V2)
-    return fail(MLA_ERR_UNSUPPORTED, "decode from hidden states is implemented for the V2 sizes only");
-  if (d_model < 64 || d_model % 64 != 0 || d_model > (1 << 20))
-    return fail(MLA_ERR_INVALID_ARG, "d_model must be a positive multiple of 64 (at most 2^20)");
-  if (d_q < 64 || d_q % 64 != 0 || d_q > (1 << 20))
-    return fail(MLA_ERR_INVALID_ARG, "d_q must be a positive multiple of 64 (at most 2^20)");
+// sizes of the projections around the decode.  The V2 family streams K in
+// 64-wide steps, so both K sizes must be multiples of 64 there; the generic
+// family takes any positive size (and none of the pre-merged forms, which
+// v2_only marks).  Both at most 2^20.
+mla_status check_front(Family fam, int32_t d_model, int32_t d_q, bool v2_only = false) {
+  if (fam != Family::V2 && v2_only)
+    return fail(MLA_ERR_UNSUPPORTED, "the pre-merged weight forms are implemented for the V2 sizes only");
+  const int step = fam == Family::V2 ? 64 : 1;
+  if (d_model < step || d_model % step != 0 || d_model > (1 << 20))
+    return fail(MLA_ERR_INVALID_ARG, fam == Family::V2
+                                         ? "d_model must be a positive multiple of 64 (at most 2^20)"
+                                         : "d_model must be in [1, 2^20]");
+  if (d_q < step || d_q % step != 0 || d_q > (1 << 20))
+    return fail(MLA_ERR_INVALID_ARG, fam == Family::V2
+                                         ? "d_q must be a positive multiple of 64 (at most 2^20)"
+                                         : "d_q must be in [1, 2^20]");
   return MLA_OK;
+}
+// Decode from hidden states (w_o NULL) or the layer through W^O for the
+// generic family, after the caller's argument checks.
+mla_status generic_hidden(const mla::Layer& L, const mla_paged_cache* cache, int32_t batch,
+                          const int32_t* seq_lens, int32_t d_model, int32_t d_q, const void* h,
+                          const void* w_dkv, const void* w_kr, const void* w_dq, const void* w_uq,
+                          const void* w_qr, const void* w_uk, const void* w_uv, const void* w_o,
+                          void* out, void* workspace, size_t workspace_bytes,
+                          void* const* timing_events, void* stream) {
+  if (batch > 65535) return fail(MLA_ERR_INVALID_ARG, "batch must be at most 65535 for these sizes");
+  const size_t need = mla::generic_hidden_workspace(L, batch, d_q);
+  if (!workspace || workspace_bytes < need)
+    return fail(MLA_ERR_WORKSPACE, "workspace smaller than mla_decode_hidden_workspace_size()");
+  MLA_TRY(check_ptr(workspace, "workspace"));
+  g_err.clear();
+  return launched(mla::launch_generic_decode_hidden(L, cache->pool, cache->num_pages,
+                                                    cache->page_table, cache->max_pages, batch,
+                                                    seq_lens, d_model, d_q, h, w_dkv, w_kr, w_dq,
+                                                    w_uq, w_qr, w_uk, w_uv, w_o, out, workspace,
+                                                    timing_events, (hipStream_t)stream),
+                  "generic decode from hidden states launch");
 }
 }  // namespace
 
@@ -281,6 +308,7 @@ size_t mla_decode_hidden_workspace_size(const mla_dims* dims, int32_t batch, int
   Family fam;
   if (check_dims(dims, &L, &fam) != MLA_OK || batch < 1) return 0;
   if (check_front(fam, d_model, d_q) != MLA_OK) return 0;
+  if (fam == Family::Generic) return mla::generic_hidden_workspace(L, batch, d_q);
   int wg = 0;
   if (resolve_wg(n_workgroups, &wg) != 0) return 0;
   return mla::v2_hidden_workspace(L, batch, wg, d_model, d_q);
@@ -311,6 +339,9 @@ mla_status mla_decode_hidden(const mla_dims* dims, const mla_paged_cache* cache,
   MLA_TRY(check_ptr(out, "out"));
   if (n_workgroups < 0 || n_workgroups > 65536)
     return fail(MLA_ERR_INVALID_ARG, "n_workgroups must be in [0, 65536]");
+  if (fam == Family::Generic)
+    return generic_hidden(L, cache, batch, seq_lens, d_model, d_q, h, w_dkv, w_kr, w_dq, w_uq, w_qr,
+                          w_uk, w_uv, nullptr, out, workspace, workspace_bytes, timing_events, stream);
   int wg = 0;
   if (resolve_wg(n_workgroups, &wg) != 0) return fail(MLA_ERR_HIP, "cannot query the device");
   const size_t need = mla::v2_hidden_workspace(L, batch, wg, d_model, d_q);
@@ -352,6 +383,9 @@ mla_status mla_decode_layer(const mla_dims* dims, const mla_paged_cache* cache, 
   MLA_TRY(check_ptr(u, "u"));
   if (n_workgroups < 0 || n_workgroups > 65536)
     return fail(MLA_ERR_INVALID_ARG, "n_workgroups must be in [0, 65536]");
+  if (fam == Family::Generic)
+    return generic_hidden(L, cache, batch, seq_lens, d_model, d_q, h, w_dkv, w_kr, w_dq, w_uq, w_qr,
+                          w_uk, w_uv, w_o, u, workspace, workspace_bytes, timing_events, stream);
   int wg = 0;
   if (resolve_wg(n_workgroups, &wg) != 0) return fail(MLA_ERR_HIP, "cannot query the device");
   const size_t need = mla::v2_hidden_workspace(L, batch, wg, d_model, d_q);
@@ -371,7 +405,7 @@ mla_status mla_merge_query_weights(const mla_dims* dims, int32_t d_q, const void
   mla::Layer L;
   Family fam;
   MLA_TRY(check_dims(dims, &L, &fam));
-  MLA_TRY(check_front(fam, 64, d_q));
+  MLA_TRY(check_front(fam, 64, d_q, true));
   MLA_TRY(check_ptr(w_uq, "w_uq"));
   MLA_TRY(check_ptr(w_uk, "w_uk"));
   MLA_TRY(check_ptr(w_uqk, "w_uqk"));
@@ -391,7 +425,7 @@ mla_status mla_decode_hidden_merged(const mla_dims* dims, const mla_paged_cache*
   Family fam;
   MLA_TRY(check_dims(dims, &L, &fam));
   MLA_TRY(check_cache(cache));
-  MLA_TRY(check_front(fam, d_model, d_q));
+  MLA_TRY(check_front(fam, d_model, d_q, true));
   if (batch < 1) return fail(MLA_ERR_INVALID_ARG, "batch must be >= 1");
   if ((long long)batch * L.n_heads > 0x7fffffffLL) return fail(MLA_ERR_INVALID_ARG, "batch too large");
   MLA_TRY(check_idx(seq_lens, "seq_lens"));
@@ -425,7 +459,7 @@ mla_status mla_merge_output_weights(const mla_dims* dims, int32_t d_model, const
   mla::Layer L;
   Family fam;
   MLA_TRY(check_dims(dims, &L, &fam));
-  MLA_TRY(check_front(fam, d_model, 64));
+  MLA_TRY(check_front(fam, d_model, 64, true));
   MLA_TRY(check_ptr(w_o, "w_o"));
   MLA_TRY(check_ptr(w_uv, "w_uv"));
   MLA_TRY(check_ptr(w_ov, "w_ov"));
@@ -445,7 +479,7 @@ mla_status mla_decode_layer_merged(const mla_dims* dims, const mla_paged_cache* 
   Family fam;
   MLA_TRY(check_dims(dims, &L, &fam));
   MLA_TRY(check_cache(cache));
-  MLA_TRY(check_front(fam, d_model, d_q));
+  MLA_TRY(check_front(fam, d_model, d_q, true));
   if (batch < 1) return fail(MLA_ERR_INVALID_ARG, "batch must be >= 1");
   if ((long long)batch * L.n_heads > 0x7fffffffLL) return fail(MLA_ERR_INVALID_ARG, "batch too large");
   MLA_TRY(check_idx(seq_lens, "seq_lens"));

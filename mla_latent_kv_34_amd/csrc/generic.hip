@@ -239,6 +239,28 @@ generic_prefill_attn_kernel(const void* __restrict__ pool, int num_pages,
   for (int r = threadIdx.x; r < d_nope; r += kThreads) st<BF16>(out, id * d_nope + r, o[r] * inv);
 }
 
+// y[m][n] = sum_k x[m][k] w[n][k] (w out x in), fp32 accumulation, stored in
+// the layer's dtype: the dense projections around the decode for small
+// layers.  Block (n block of 256, m); one thread per output.
+template <bool BF16>
+__global__ void __launch_bounds__(kThreads)
+generic_proj_kernel(const void* __restrict__ x, int K, const void* __restrict__ w, int N,
+                    void* __restrict__ y) {
+  const int n = (int)blockIdx.x * kThreads + threadIdx.x;
+  const long long m = blockIdx.y;
+  if (n >= N) return;
+  float acc = 0.f;
+  for (int k = 0; k < K; ++k) acc += ld<BF16>(x, m * K + k) * ld<BF16>(w, (size_t)n * K + k);
+  st<BF16>(y, (size_t)m * N + n, acc);
+}
+
+template <bool BF16>
+hipError_t proj(const void* x, int M, int K, const void* w, int N, void* y, hipStream_t s) {
+  hipLaunchKernelGGL(generic_proj_kernel<BF16>, dim3((unsigned)((N + kThreads - 1) / kThreads), (unsigned)M),
+                     dim3(kThreads), 0, s, x, K, w, N, y);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 size_t generic_decode_workspace(const Layer&, int) { return 0; }
@@ -305,4 +327,80 @@ hipError_t launch_generic_prefill(const Layer& L, const void* pool, int num_page
   return mark(ev, 1, s);
 }
 
+
+// Decode from hidden states and the layer through W^O for small layers: the
+// projections of the tech note's three branches as plain GEMMs into the
+// workspace (c^KV, k^R, c^Q, q^C, q^R, then o), the new row appended at
+// position seq_lens[b] - 1, the generic decode, and for the layer u = W^O o.
+namespace {
+struct GenHidden {
+  size_t c_kv, k_r, c_q, q_nope, q_rope, o, total;
+  GenHidden(const Layer& L, int batch, int d_q) {
+    const size_t B = (size_t)batch, e = L.bf16 ? 2 : 4;
+    c_kv = 0;
+    k_r = align256(c_kv + B * L.d_latent * e);
+    c_q = align256(k_r + B * L.d_rope * e);
+    q_nope = align256(c_q + B * d_q * e);
+    q_rope = align256(q_nope + B * L.n_heads * L.d_nope * e);
+    o = align256(q_rope + B * L.n_heads * L.d_rope * e);
+    total = align256(o + B * L.n_heads * L.d_nope * e);
+  }
+};
+
+template <bool BF16>
+hipError_t generic_hidden_impl(const Layer& L, const void* pool, int num_pages, const int32_t* table,
+                               int max_pages, int batch, const int32_t* seq_lens, int d_model,
+                               int d_q, const void* h, const void* w_dkv, const void* w_kr,
+                               const void* w_dq, const void* w_uq, const void* w_qr,
+                               const void* w_uk, const void* w_uv, const void* w_o, void* out,
+                               void* ws, void* const* ev, hipStream_t s) {
+  const GenHidden lay(L, batch, d_q);
+  char* w = (char*)ws;
+  void* c_kv = w + lay.c_kv;
+  void* k_r = w + lay.k_r;
+  void* c_q = w + lay.c_q;
+  void* q_nope = w + lay.q_nope;
+  void* q_rope = w + lay.q_rope;
+  void* o = w_o ? (void*)(w + lay.o) : out;
+  const int H = L.n_heads;
+  hipError_t e = w_o ? hipSuccess : mark(ev, 0, s);
+  if (e != hipSuccess) return e;
+  if ((e = proj<BF16>(h, batch, d_model, w_dkv, L.d_latent, c_kv, s)) != hipSuccess) return e;
+  if ((e = proj<BF16>(h, batch, d_model, w_kr, L.d_rope, k_r, s)) != hipSuccess) return e;
+  if ((e = proj<BF16>(h, batch, d_model, w_dq, d_q, c_q, s)) != hipSuccess) return e;
+  if ((e = proj<BF16>(c_q, batch, d_q, w_uq, H * L.d_nope, q_nope, s)) != hipSuccess) return e;
+  if ((e = proj<BF16>(c_q, batch, d_q, w_qr, H * L.d_rope, q_rope, s)) != hipSuccess) return e;
+  if (!w_o && (e = mark(ev, 1, s)) != hipSuccess) return e;
+  if ((e = launch_append(L, const_cast<void*>(pool), num_pages, table, max_pages, batch, seq_lens, 1,
+                         c_kv, k_r, s, -1)) != hipSuccess)
+    return e;
+  if ((e = launch_generic_decode(L, pool, num_pages, table, max_pages, batch, seq_lens, q_nope, q_rope,
+                                 w_uk, w_uv, o, nullptr, nullptr, s)) != hipSuccess)
+    return e;
+  if (!w_o) return hipSuccess;
+  if ((e = mark(ev, 0, s)) != hipSuccess) return e;
+  if ((e = proj<BF16>(o, batch, H * L.d_nope, w_o, d_model, out, s)) != hipSuccess) return e;
+  return mark(ev, 1, s);
+}
+}  // namespace
+
+size_t generic_hidden_workspace(const Layer& L, int batch, int d_q) {
+  return GenHidden(L, batch, d_q).total;
+}
+
+hipError_t launch_generic_decode_hidden(const Layer& L, const void* pool, int num_pages,
+                                        const int32_t* table, int max_pages, int batch,
+                                        const int32_t* seq_lens, int d_model, int d_q,
+                                        const void* h, const void* w_dkv, const void* w_kr,
+                                        const void* w_dq, const void* w_uq, const void* w_qr,
+                                        const void* w_uk, const void* w_uv, const void* w_o,
+                                        void* out, void* ws, void* const* ev, hipStream_t s) {
+  if (batch > 65535) return hipErrorInvalidValue;  // grid y of the projections
+  return L.bf16 ? generic_hidden_impl<true>(L, pool, num_pages, table, max_pages, batch, seq_lens,
+                                            d_model, d_q, h, w_dkv, w_kr, w_dq, w_uq, w_qr, w_uk,
+                                            w_uv, w_o, out, ws, ev, s)
+                : generic_hidden_impl<false>(L, pool, num_pages, table, max_pages, batch, seq_lens,
+                                             d_model, d_q, h, w_dkv, w_kr, w_dq, w_uq, w_qr, w_uk,
+                                             w_uv, w_o, out, ws, ev, s);
+}
 }  // namespace mla

@@ -108,6 +108,17 @@ hipError_t launch_generic_prefill(const Layer& L, const void* pool, int num_page
                                   const void* q_rope, const void* w_uk, const void* w_uv,
                                   void* out, void* ws, void* const* ev, hipStream_t s);
 
+// decode from hidden states (w_o NULL: out = o, events around the
+// projections) or the layer through W^O (out = u, events around W^O)
+size_t generic_hidden_workspace(const Layer& L, int batch, int d_q);
+hipError_t launch_generic_decode_hidden(const Layer& L, const void* pool, int num_pages,
+                                        const int32_t* table, int max_pages, int batch,
+                                        const int32_t* seq_lens, int d_model, int d_q,
+                                        const void* h, const void* w_dkv, const void* w_kr,
+                                        const void* w_dq, const void* w_uq, const void* w_qr,
+                                        const void* w_uk, const void* w_uv, const void* w_o,
+                                        void* out, void* ws, void* const* ev, hipStream_t s);
+
 // MFMA family for the V2 sizes
 size_t v2_decode_workspace(int batch, int n_wg);
 // c_new / k_new: NULL, or the token at position seq_lens[b] - 1 of every

@@ -92,8 +92,11 @@ def assert_close(got: np.ndarray, ref: np.ndarray, what: str = "", max_bar: floa
     return max_rel, mean_rel
 
 
-def bf16_round(x) -> np.ndarray:
-    """fp64 values rounded to bf16 (nearest even) and back to fp64: the storage
-    type in which the path hands projected tensors to the attention rows."""
-    from oracle import bf16_bits_rne
+def store_round(x, dtype: str = "bf16") -> np.ndarray:
+    """fp64 values rounded (nearest even) to the layer's storage type and back
+    to fp64: the type in which the path hands projected tensors to the
+    attention rows."""
+    from oracle import bf16_bits_rne, f32_rne
+    if dtype == "f32":
+        return np.asarray(f32_rne(x), dtype=np.float64)
     return (bf16_bits_rne(x).astype(np.uint32) << 16).view(np.float32).astype(np.float64)

@@ -12,7 +12,7 @@ from oracle import append_expected, decode_ref, front_end
 
 pytestmark = pytest.mark.gpu
 
-from gpu_common import DEV, assert_close, bf16_round, canary_pool, f64, fill_cache, lib_dims, pool_bits  # noqa: E402
+from gpu_common import DEV, assert_close, store_round, canary_pool, f64, fill_cache, lib_dims, pool_bits  # noqa: E402
 
 
 def _run(hc: syn.HiddenCase, n_workgroups=0):
@@ -34,7 +34,7 @@ def _oracle(hc: syn.HiddenCase, b: int, heads=None):
     projected new row (query at the new token's position)."""
     base = hc.base
     f = [w.double().numpy() for w in hc.front]
-    c_new, k_new, q_c, q_r = (bf16_round(t) for t in
+    c_new, k_new, q_c, q_r = (store_round(t, base.dims.dtype) for t in
                               front_end(hc.h[b].double().numpy(), *f, n_heads=base.dims.n_heads))
     c_rows, k_rows = base.seq_rows(b)
     n = int(base.cached[b])
@@ -128,3 +128,14 @@ def test_decode_hidden_b64_ragged_full_size_sampled():
         ref, c_new, k_new = _oracle(hc, int(b), heads=heads)
         assert_close(f64(out[b])[heads], ref, f"seq {b} (cached {hc.base.cached[b]})")
         _check_new_row(hc, bits, int(b), c_new, k_new)
+
+
+def test_decode_hidden_tiny_fp32():
+    """The generic family (tiny fp32 layer, d 128, d_c' 48): projections as
+    plain GEMMs, the new row appended, the generic decode."""
+    print("case decode_hidden tiny fp32", flush=True)
+    hc = syn.hidden_case(syn.TINY, [64, 0, 130], seed=24, shuffle=True)
+    pool, out = _run(hc)
+    for b in range(hc.base.batch):
+        ref, _, _ = _oracle(hc, b)
+        assert_close(f64(out[b]), ref, f"tiny seq {b} (cached {hc.base.cached[b]})")

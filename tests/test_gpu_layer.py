@@ -11,7 +11,7 @@ from oracle import decode_ref, front_end, output_proj
 
 pytestmark = pytest.mark.gpu
 
-from gpu_common import DEV, assert_close, bf16_round, canary_pool, f64, fill_cache, lib_dims  # noqa: E402
+from gpu_common import DEV, assert_close, store_round, canary_pool, f64, fill_cache, lib_dims  # noqa: E402
 
 
 def _run(hc: syn.HiddenCase, w_o: torch.Tensor, seq_lens=None):
@@ -34,7 +34,7 @@ def _oracle(hc: syn.HiddenCase, w_o: torch.Tensor, b: int):
     (every head), then W^O."""
     base = hc.base
     f = [w.double().numpy() for w in hc.front]
-    c_new, k_new, q_c, q_r = (bf16_round(t) for t in
+    c_new, k_new, q_c, q_r = (store_round(t, base.dims.dtype) for t in
                               front_end(hc.h[b].double().numpy(), *f, n_heads=base.dims.n_heads))
     c_rows, k_rows = base.seq_rows(b)
     n = int(base.cached[b])
@@ -77,3 +77,14 @@ def test_decode_layer_b64_ragged_full_size_sampled():
     rng = np.random.default_rng(14)
     for b in rng.choice(64, size=3, replace=False):
         assert_close(f64(u[b]), _oracle(hc, w_o, int(b)), f"u of seq {b} (cached {hc.base.cached[b]})")
+
+
+def test_decode_layer_tiny_fp32():
+    """The generic family (tiny fp32 layer): u = W^O o after the projections
+    and the generic decode."""
+    print("case decode_layer tiny fp32", flush=True)
+    hc = syn.hidden_case(syn.TINY, [64, 0, 130], seed=43, shuffle=True)
+    w_o = syn.out_weight(syn.TINY, 43)
+    u = _run(hc, w_o)
+    for b in range(hc.base.batch):
+        assert_close(f64(u[b]), _oracle(hc, w_o, b), f"tiny u of seq {b} (cached {hc.base.cached[b]})")

@@ -12,7 +12,7 @@ from oracle import decode_ref, front_end, merge_query_weights
 
 pytestmark = pytest.mark.gpu
 
-from gpu_common import DEV, assert_close, bf16_round, canary_pool, f64, fill_cache, lib_dims  # noqa: E402
+from gpu_common import DEV, assert_close, store_round, canary_pool, f64, fill_cache, lib_dims  # noqa: E402
 
 
 def test_merge_query_weights_v2():
@@ -51,7 +51,7 @@ def _run(hc: syn.HiddenCase, seq_lens=None):
 def _oracle(hc: syn.HiddenCase, b: int, heads=None):
     base = hc.base
     f = [w.double().numpy() for w in hc.front]
-    c_new, k_new, q_c, q_r = (bf16_round(t) for t in
+    c_new, k_new, q_c, q_r = (store_round(t, base.dims.dtype) for t in
                               front_end(hc.h[b].double().numpy(), *f, n_heads=base.dims.n_heads))
     c_rows, k_rows = base.seq_rows(b)
     n = int(base.cached[b])

@@ -93,14 +93,15 @@ def test_decode_hidden_rejections_on_host(lib):
                               0x4000, 0x5000, 0x6000, 0x7000, 0x8000, 0x9000, 0xa000, 0xb000, 0xc000,
                               0xd000, 1 << 30, 0, None, None)
     tiny = _dims(n_heads=4, d_nope=16, d_rope=8, d_latent=32, dtype=1)
-    assert lib.mla_decode_hidden(*args(tiny, 128, 64)) == mla.MLA_ERR_UNSUPPORTED
-    assert b"V2" in lib.mla_last_error()
+    assert lib.mla_decode_hidden(*args(tiny, 128, 0)) == mla.MLA_ERR_INVALID_ARG   # generic: any K >= 1
+    assert b"d_q" in lib.mla_last_error()
     v2 = _dims()
     assert lib.mla_decode_hidden(*args(v2, 5000, 1536)) == mla.MLA_ERR_INVALID_ARG
     assert b"d_model" in lib.mla_last_error()
     assert lib.mla_decode_hidden(*args(v2, 5120, 0)) == mla.MLA_ERR_INVALID_ARG
     assert b"d_q" in lib.mla_last_error()
-    assert lib.mla_decode_hidden_workspace_size(ctypes.byref(tiny), 4, 0, 128, 64) == 0
+    assert lib.mla_decode_hidden_workspace_size(ctypes.byref(tiny), 4, 0, 128, 48) > 0
+    assert lib.mla_decode_hidden_workspace_size(ctypes.byref(tiny), 4, 0, 128, 0) == 0
     assert lib.mla_decode_hidden_workspace_size(ctypes.byref(v2), 4, 0, 5000, 1536) == 0
 
 
@@ -133,8 +134,8 @@ def test_prefill_chunk_rejections_on_host(lib):
 
 def test_layer_and_merge_rejections_on_host(lib):
     """The layer, merged-weight and merge entry points validate on the host:
-    the generic family is unsupported, K sizes must be multiples of 64, and a
-    NULL weight is named in the error."""
+    the merged forms exist for the V2 sizes only, K sizes must be positive
+    (multiples of 64 for the V2 sizes), and a NULL weight is named in the error."""
     cache = _lib._Cache(0x1000, 1, 1, 0x2000)   # never dereferenced
     tiny = _dims(n_heads=4, d_nope=16, d_rope=8, d_latent=32, dtype=1)
     v2 = _dims()
@@ -150,7 +151,10 @@ def test_layer_and_merge_rejections_on_host(lib):
 
     for fn, n_ptr, name in ((lib.mla_decode_layer, 11, b"w_o"), (lib.mla_decode_layer_merged, 10, b"w_ov")):
         assert len(fn.argtypes) == 6 + n_ptr + 4
-        assert layer(fn, n_ptr, tiny, 128, 64) == mla.MLA_ERR_UNSUPPORTED
+        if fn is lib.mla_decode_layer_merged:
+            assert layer(fn, n_ptr, tiny, 128, 64) == mla.MLA_ERR_UNSUPPORTED   # merged: V2 only
+        else:
+            assert layer(fn, n_ptr, tiny, 128, 0) == mla.MLA_ERR_INVALID_ARG
         assert layer(fn, n_ptr, v2, 5000, 1536) == mla.MLA_ERR_INVALID_ARG
         assert b"d_model" in lib.mla_last_error()
         assert layer(fn, n_ptr, v2, 5120, 1536, nulled=n_ptr - 3) == mla.MLA_ERR_INVALID_ARG
