@@ -42,7 +42,7 @@ namespace pj {
 #define PJ_DEPTH 4
 #endif
 #ifndef PJ_MIN_WG
-#define PJ_MIN_WG 256
+#define PJ_MIN_WG 128
 #endif
 constexpr int WR = PJ_WR;              // weight rows per workgroup
 constexpr int KC = 64;                 // K per stage
@@ -276,14 +276,15 @@ proj_reduce_kernel(const float* __restrict__ part, int M, int ksplit, Segs segs)
   *(ushort4*)(sg.out + (size_t)m * sg.rows + (row - base)) = o;
 }
 
-// K slices per launch: at least PJ_MIN_WG workgroups (twice that for long K,
-// where the fp32 partials stay small next to the weights), a power of two
-// dividing K / KC.
+// K slices per launch: a power of two dividing K / KC that gives at least
+// PJ_MIN_WG workgroups, or 4 x PJ_MIN_WG for long K, where the fp32 partials
+// stay small next to the weights (measured at batch 64: stage 1, K 5120, is
+// fastest split 4 ways; W^O, K 16384, split 8 ways).
 constexpr int kMinWorkgroups = PJ_MIN_WG;
 constexpr int kLongK = 8192;
 int choose_split(int n_total, int K) {
   const int tiles = (n_total + WR - 1) / WR;
-  const int target = K >= kLongK ? 2 * kMinWorkgroups : kMinWorkgroups;
+  const int target = K >= kLongK ? 4 * kMinWorkgroups : kMinWorkgroups;
   int s = 1;
   while (tiles * s < target && (K / KC) % (2 * s) == 0) s *= 2;
   return s;
