@@ -590,14 +590,54 @@ def chunk_bench(mla, syn, dims, dev, steps: int):
     flop = pairs * 2 * (d.d_nope + d.d_rope + d.d_nope)    # scores + weighted sum
     flop += 2 * B * ctx * d.d_latent * 2 * H * d.d_nope    # K^C and V^C of every position
     tflops = flop / (kern_ms * 1e-3) / 1e12
+    short = short_chunk_bench(mla, syn, dims, dev, steps)
     return {"workload": "v2_chunk_2x(3584+512): 2 sequences, 3584 cached + 512-token chunk, causal, "
                         "chunk rows written",
+            "short_chunk": short,
             "value": round(B * T / (ms * 1e-3), 1), "unit": "chunk tokens/s",
             "ms_per_call": round(ms, 4), "kernels_ms": round(kern_ms, 4),
             "roofline": {"kernel": "expand + prefill_attn", "bound": "mfma",
                          "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                          "algorithmic_flop": flop}}
+
+
+def short_chunk_bench(mla, syn, dims, dev, steps: int):
+    """A 128-token chunk after 3968 cached positions (2 sequences), timed in
+    both forms, expanded (every position's K/V) and absorbed (each chunk row a
+    decode query), and with the library's automatic choice."""
+    import numpy as np
+    import torch
+
+    P, T = 3968, 128
+    case = syn.chunk_case(syn.V2, [P, P], T, seed=3)
+    B, d = case.batch, case.dims
+    pool = torch.zeros((case.num_pages, d.page_size, d.row), dtype=d.torch_dtype, device=dev)
+    table = torch.from_numpy(case.table).to(dev)
+    mla.cache_append(dims, pool, table, torch.zeros(B, dtype=torch.int32, device=dev),
+                     case.c_all[:, :P].contiguous().to(dev), case.k_all[:, :P].contiguous().to(dev))
+    c_new, k_new = case.chunk_rows()
+    start = torch.from_numpy(case.start.astype(np.int32)).to(dev)
+    args = [case.q_c.to(dev), case.q_r.to(dev), c_new.contiguous().to(dev), k_new.contiguous().to(dev),
+            case.w_uk.to(dev), case.w_uv.to(dev)]
+    res = {}
+    for name, mode in (("expanded", mla.CHUNK_EXPAND), ("absorbed", mla.CHUNK_ABSORB),
+                       ("auto", mla.CHUNK_AUTO)):
+        call, _ = mla.prefill_chunk(dims, pool, table, start, *args, max_context=P + T, mode=mode,
+                                    prepare=True)
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(steps):
+            call()
+        t1.record()
+        torch.cuda.synchronize()
+        res[name + "_ms"] = round(t0.elapsed_time(t1) / steps, 4)
+    return {"workload": "v2_chunk_2x(3968+128): 2 sequences, 3968 cached + 128-token chunk",
+            **res, "value": round(B * T / (res["auto_ms"] * 1e-3), 1),
+            "unit": "chunk tokens/s (automatic choice)"}
 
 
 def cpu_baseline(case, budget_s: float):

@@ -283,7 +283,19 @@ mla_status mla_prefill(const mla_dims* dims, const mla_paged_cache* cache, int32
                        const void* w_uv, void* out, void* workspace, size_t workspace_bytes,
                        void* const* timing_events, void* stream);
 
-/* Bytes of device workspace mla_prefill_chunk needs (0 for invalid sizes). */
+/* How mla_prefill_chunk computes a chunk.  EXPAND: expand K^C and V^C for
+ * every position and run the causal attention (the prompt form).  ABSORB:
+ * treat chunk row t as a decode query at position start_pos[b] + t over the
+ * cache (the decode form: each row absorbed, scored against the latent rows),
+ * for chunks of at most 256 tokens, V2 sizes only.  AUTO: the cheaper of the
+ * two for the chunk length and max_context, from costs measured on MI355X
+ * (a short chunk after a long prefix is cheaper absorbed: expanding the
+ * prefix costs as much as attending it many times).                         */
+typedef enum { MLA_CHUNK_AUTO = 0, MLA_CHUNK_EXPAND = 1, MLA_CHUNK_ABSORB = 2 } mla_chunk_mode;
+
+/* Bytes of device workspace mla_prefill_chunk needs in any mode (0 for
+ * invalid sizes).  For the V2 sizes and chunk_len <= 256 it covers the
+ * absorbed form too, sized for the current device's compute units.          */
 size_t mla_prefill_chunk_workspace_size(const mla_dims* dims, int32_t batch, int32_t chunk_len,
                                         int32_t max_context);
 
@@ -307,11 +319,15 @@ size_t mla_prefill_chunk_workspace_size(const mla_dims* dims, int32_t batch, int
  *   sequence); the page table needs ceil(max_context / page_size) columns.
  * q_nope, q_rope, c_kv, k_rope, out: as for mla_prefill with seq_len =
  *   chunk_len (the chunk's tokens only).
- * mla_prefill(..., seq_len, ...) is this call with start_pos[b] = 0 and
- * max_context = seq_len.  timing_events as for mla_prefill.                 */
+ * mode: an mla_chunk_mode (MLA_CHUNK_ABSORB with more than 256 tokens:
+ *   MLA_ERR_INVALID_ARG; outside the V2 sizes: MLA_ERR_UNSUPPORTED; AUTO
+ *   uses EXPAND there).
+ * mla_prefill(..., seq_len, ...) is this call with start_pos[b] = 0,
+ * max_context = seq_len and MLA_CHUNK_EXPAND.  timing_events as for
+ * mla_prefill (ABSORB: around the split-KV attention kernel).               */
 mla_status mla_prefill_chunk(const mla_dims* dims, const mla_paged_cache* cache, int32_t batch,
                              const int32_t* start_pos, int32_t chunk_len, int32_t max_context,
-                             const void* q_nope, const void* q_rope, const void* c_kv,
+                             int32_t mode, const void* q_nope, const void* q_rope, const void* c_kv,
                              const void* k_rope, const void* w_uk, const void* w_uv, void* out,
                              void* workspace, size_t workspace_bytes, void* const* timing_events,
                              void* stream);

@@ -9,4 +9,5 @@ from ._lib import (  # noqa: F401
     decode_hidden_merged, merge_output_weights, decode_layer_merged, prefill, prefill_workspace_size, prefill_chunk,
     prefill_chunk_workspace_size, default_scale, LIB_PATH, EXPORTED,
     MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ERR_HIP,
+    CHUNK_AUTO, CHUNK_EXPAND, CHUNK_ABSORB,
 )

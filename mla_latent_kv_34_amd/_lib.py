@@ -19,6 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmla.so")
 
 MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ERR_HIP = range(5)
+CHUNK_AUTO, CHUNK_EXPAND, CHUNK_ABSORB = range(3)  # mla_chunk_mode
 MLA_BF16, MLA_F32 = 0, 1
 
 EXPORTED = (
@@ -138,7 +139,7 @@ def load() -> ctypes.CDLL:
                                                      ctypes.c_int32]
     lib.mla_prefill_chunk_workspace_size.restype = ctypes.c_size_t
     lib.mla_prefill_chunk.argtypes = [ctypes.POINTER(_Dims), ctypes.POINTER(_Cache), ctypes.c_int32,
-                                      ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32] + \
+                                      ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32] + \
         [ctypes.c_void_p] * 8 + [ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
     lib.mla_prefill_chunk.restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]
@@ -629,14 +630,15 @@ def prefill_chunk_workspace_size(dims: Dims, batch: int, chunk_len: int, max_con
 
 def prefill_chunk(dims: Dims, pool: torch.Tensor, page_table: torch.Tensor, start_pos: torch.Tensor,
                   q_nope: torch.Tensor, q_rope: torch.Tensor, c_kv: torch.Tensor, k_rope: torch.Tensor,
-                  w_uk: torch.Tensor, w_uv: torch.Tensor, max_context: int,
+                  w_uk: torch.Tensor, w_uv: torch.Tensor, max_context: int, mode: int = 0,
                   out: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None,
                   timing_events=None, prepare: bool = False):
     """Chunked prefill over an existing latent cache (mla_prefill_chunk): chunk
     row t of sequence b sits at position start_pos[b] + t and attends every
     position up to its own.  start_pos: int32 [batch] on the device;
     max_context bounds start_pos[b] + chunk_len.  Tensors as for prefill with
-    seq_len = chunk_len; timing_events and prepare as for decode()."""
+    seq_len = chunk_len; mode: CHUNK_AUTO, CHUNK_EXPAND or CHUNK_ABSORB
+    (mla_chunk_mode); timing_events and prepare as for decode()."""
     lib = load()
     cache = _cache(dims, pool, page_table)
     dev = pool.device
@@ -659,7 +661,7 @@ def prefill_chunk(dims: Dims, pool: torch.Tensor, page_table: torch.Tensor, star
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     d = dims._c()
-    args = [ctypes.byref(d), ctypes.byref(cache), B, _ptr(start_pos), T, int(max_context), _ptr(q_nope),
+    args = [ctypes.byref(d), ctypes.byref(cache), B, _ptr(start_pos), T, int(max_context), int(mode), _ptr(q_nope),
             _ptr(q_rope), _ptr(c_kv), _ptr(k_rope), _ptr(w_uk), _ptr(w_uv), _ptr(out), _ptr(workspace),
             wbytes]
     evs = _events(timing_events)

@@ -527,6 +527,9 @@ size_t mla_prefill_chunk_workspace_size(const mla_dims* dims, int32_t batch, int
   Family fam;
   if (check_dims(dims, &L, &fam) != MLA_OK || batch < 1 || chunk_len < 1 || max_context < chunk_len)
     return 0;
+  int wg = 0;
+  if (fam == Family::V2 && chunk_len <= mla::kChunkAbsorbMax && resolve_wg(0, &wg) == 0)
+    return mla::v2_prefill_workspace(batch, chunk_len, max_context, wg);
   return prefill_need(L, fam, batch, chunk_len, max_context);
 }
 
@@ -534,7 +537,7 @@ size_t mla_prefill_chunk_workspace_size(const mla_dims* dims, int32_t batch, int
 // mla_prefill_chunk.
 static mla_status prefill_common(const mla_dims* dims, const mla_paged_cache* cache, int32_t batch,
                                  const int32_t* start_pos, int32_t chunk_len, int32_t max_context,
-                                 const void* q_nope, const void* q_rope, const void* c_kv,
+                                 int32_t mode, const void* q_nope, const void* q_rope, const void* c_kv,
                                  const void* k_rope, const void* w_uk, const void* w_uv, void* out,
                                  void* workspace, size_t workspace_bytes,
                                  void* const* timing_events, void* stream, const char* ws_name) {
@@ -557,7 +560,18 @@ static mla_status prefill_common(const mla_dims* dims, const mla_paged_cache* ca
   MLA_TRY(check_ptr(w_uk, "w_uk"));
   MLA_TRY(check_ptr(w_uv, "w_uv"));
   MLA_TRY(check_ptr(out, "out"));
-  const size_t need = prefill_need(L, fam, batch, chunk_len, max_context);
+  if (mode < MLA_CHUNK_AUTO || mode > MLA_CHUNK_ABSORB) return fail(MLA_ERR_INVALID_ARG, "unknown mode");
+  if (mode == MLA_CHUNK_ABSORB && fam != Family::V2)
+    return fail(MLA_ERR_UNSUPPORTED, "the absorbed chunk form is implemented for the V2 sizes only");
+  if (mode == MLA_CHUNK_ABSORB && chunk_len > mla::kChunkAbsorbMax)
+    return fail(MLA_ERR_INVALID_ARG, "the absorbed chunk form takes at most 256 tokens per chunk");
+  const bool absorb = fam == Family::V2 &&
+                      (mode == MLA_CHUNK_ABSORB ||
+                       (mode == MLA_CHUNK_AUTO && mla::v2_chunk_absorbed(chunk_len, max_context)));
+  int wg = 0;
+  if (absorb && resolve_wg(0, &wg) != 0) return fail(MLA_ERR_HIP, "cannot query the device");
+  const size_t need = absorb ? mla::v2_prefill_workspace(batch, chunk_len, max_context, wg)
+                             : prefill_need(L, fam, batch, chunk_len, max_context);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(MLA_ERR_WORKSPACE, ws_name);
   if (need > 0) MLA_TRY(check_ptr(workspace, "workspace"));
@@ -568,6 +582,12 @@ static mla_status prefill_common(const mla_dims* dims, const mla_paged_cache* ca
   MLA_TRY(launched(mla::launch_append(L, cache->pool, cache->num_pages, cache->page_table,
                                       cache->max_pages, batch, start_pos, chunk_len, c_kv, k_rope, s),
                    "prefill append launch"));
+  if (absorb)
+    return launched(mla::launch_v2_chunk_absorbed(L, cache->pool, cache->num_pages,
+                                                  cache->page_table, cache->max_pages, batch,
+                                                  chunk_len, start_pos, max_context, q_nope, q_rope,
+                                                  w_uk, w_uv, out, workspace, wg, timing_events, s),
+                    "absorbed chunk launch");
   if (fam == Family::V2)
     return launched(mla::launch_v2_prefill(L, cache->pool, cache->num_pages, cache->page_table,
                                            cache->max_pages, batch, chunk_len, start_pos,
@@ -586,19 +606,19 @@ mla_status mla_prefill(const mla_dims* dims, const mla_paged_cache* cache, int32
                        const void* k_rope, const void* w_uk, const void* w_uv, void* out,
                        void* workspace, size_t workspace_bytes, void* const* timing_events,
                        void* stream) {
-  return prefill_common(dims, cache, batch, nullptr, seq_len, seq_len, q_nope, q_rope, c_kv, k_rope,
+  return prefill_common(dims, cache, batch, nullptr, seq_len, seq_len, MLA_CHUNK_EXPAND, q_nope, q_rope, c_kv, k_rope,
                         w_uk, w_uv, out, workspace, workspace_bytes, timing_events, stream,
                         "workspace smaller than mla_prefill_workspace_size()");
 }
 
 mla_status mla_prefill_chunk(const mla_dims* dims, const mla_paged_cache* cache, int32_t batch,
                              const int32_t* start_pos, int32_t chunk_len, int32_t max_context,
-                             const void* q_nope, const void* q_rope, const void* c_kv,
+                             int32_t mode, const void* q_nope, const void* q_rope, const void* c_kv,
                              const void* k_rope, const void* w_uk, const void* w_uv, void* out,
                              void* workspace, size_t workspace_bytes, void* const* timing_events,
                              void* stream) {
   if (!start_pos) return fail(MLA_ERR_INVALID_ARG, "start_pos is NULL");
-  return prefill_common(dims, cache, batch, start_pos, chunk_len, max_context, q_nope, q_rope, c_kv,
+  return prefill_common(dims, cache, batch, start_pos, chunk_len, max_context, mode, q_nope, q_rope, c_kv,
                         k_rope, w_uk, w_uv, out, workspace, workspace_bytes, timing_events, stream,
                         "workspace smaller than mla_prefill_chunk_workspace_size()");
 }

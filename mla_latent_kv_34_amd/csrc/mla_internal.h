@@ -173,8 +173,18 @@ hipError_t launch_v2_decode_layer(const Layer& L, const void* pool, int num_page
                                   const void* w_uq, const void* w_qr, const void* w_uk,
                                   const void* w_uv, const void* w_o, void* u, void* ws, int n_wg,
                                   void* const* ev, hipStream_t s);
-// chunked prefill as launch_generic_prefill (prefill_v2.hip)
-size_t v2_prefill_workspace(int batch, int chunk_len, int max_context);
+// chunked prefill as launch_generic_prefill (prefill_v2.hip).  n_wg > 0 also
+// sizes the absorbed form of a short chunk (chunk_len <= kChunkAbsorbMax).
+constexpr int kChunkAbsorbMax = 256;
+size_t v2_prefill_workspace(int batch, int chunk_len, int max_context, int n_wg = 0);
+// whether a chunk of chunk_len tokens is cheaper done the absorbed way (each
+// row a decode query) than by expanding every position
+bool v2_chunk_absorbed(int chunk_len, int max_context);
+hipError_t launch_v2_chunk_absorbed(const Layer& L, const void* pool, int num_pages,
+                                    const int32_t* table, int max_pages, int batch, int chunk_len,
+                                    const int32_t* start_pos, int max_context, const void* q_nope,
+                                    const void* q_rope, const void* w_uk, const void* w_uv, void* out,
+                                    void* ws, int n_wg, void* const* ev, hipStream_t s);
 hipError_t launch_v2_prefill(const Layer& L, const void* pool, int num_pages, const int32_t* table,
                              int max_pages, int batch, int chunk_len, const int32_t* start_pos,
                              int max_context, const void* q_nope, const void* q_rope,

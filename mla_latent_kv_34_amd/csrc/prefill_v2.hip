@@ -464,10 +464,67 @@ struct PfLayout {
   }
 };
 
+// A short chunk done the absorbed way: chunk row i = b T + t becomes one
+// decode query of length P_b + t + 1 over sequence b's pages.  Block i writes
+// that length and a copy of the first mp entries of table row b.
+__global__ void __launch_bounds__(256)
+chunk_rows_kernel(const int32_t* __restrict__ start_pos, const int32_t* __restrict__ table,
+                  int max_pages, int T, int ctx, int mp, int32_t* __restrict__ lens,
+                  int32_t* __restrict__ rows) {
+  const int i = blockIdx.x, b = i / T, t = i % T;
+  if (threadIdx.x == 0) lens[i] = chunk_start(start_pos, b, T, ctx) + t + 1;
+  for (int k = threadIdx.x; k < mp; k += 256)
+    rows[(size_t)i * mp + k] = table[(size_t)b * max_pages + k];
+}
+
+struct AbsLayout {
+  size_t lens, rows, decode, total;
+  AbsLayout(int B, int T, int ctx, int n_wg) {
+    const size_t n = (size_t)B * T, mp = (size_t)(ctx + PS - 1) / PS;
+    lens = 0;
+    rows = align256(n * 4);
+    decode = align256(rows + n * mp * 4);
+    total = decode + v2_decode_workspace((int)n, n_wg);
+  }
+};
+
 }  // namespace v2p
 
-size_t v2_prefill_workspace(int batch, int chunk_len, int max_context) {
-  return v2p::PfLayout(batch, chunk_len, max_context).total;
+size_t v2_prefill_workspace(int batch, int chunk_len, int max_context, int n_wg) {
+  const size_t e = v2p::PfLayout(batch, chunk_len, max_context).total;
+  if (n_wg <= 0 || chunk_len > kChunkAbsorbMax) return e;
+  const size_t a = v2p::AbsLayout(batch, chunk_len, max_context, n_wg).total;
+  return e > a ? e : a;
+}
+
+bool v2_chunk_absorbed(int chunk_len, int max_context) {
+  if (chunk_len > kChunkAbsorbMax) return false;
+  // measured costs per sequence on this chip: the absorbed decode ~0.457 ns
+  // per (query, key) pair; expanding a position ~47.5 ns; the expanded
+  // attention ~0.0987 ns per pair (the prefix estimated from max_context)
+  const double T = chunk_len, P = (double)max_context - chunk_len, pairs = T * (P + 0.5 * T);
+  return pairs * 0.457 < (P + T) * 47.5 + pairs * 0.0987;
+}
+
+hipError_t launch_v2_chunk_absorbed(const Layer& L, const void* pool, int num_pages,
+                                    const int32_t* table, int max_pages, int batch, int chunk_len,
+                                    const int32_t* start_pos, int max_context, const void* q_nope,
+                                    const void* q_rope, const void* w_uk, const void* w_uv, void* out,
+                                    void* ws, int n_wg, void* const* ev, hipStream_t s) {
+  using namespace v2p;
+  const int B = batch, T = chunk_len, ctx = max_context, mp = (ctx + PS - 1) / PS;
+  const AbsLayout lay(B, T, ctx, n_wg);
+  char* w = (char*)ws;
+  int32_t* lens = (int32_t*)(w + lay.lens);
+  int32_t* rows = (int32_t*)(w + lay.rows);
+  hipLaunchKernelGGL(chunk_rows_kernel, dim3((unsigned)(B * T)), dim3(256), 0, s, start_pos, table,
+                     max_pages, T, ctx, mp, lens, rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // q [B, T, H, .] is the query batch [B T, H, .] and out [B, T, H, d_nope] the
+  // decode output [B T, H, d_nope]
+  return launch_v2_decode(L, pool, num_pages, rows, mp, B * T, lens, q_nope, q_rope, w_uk, w_uv, out,
+                          w + lay.decode, n_wg, ev, s);
 }
 
 hipError_t launch_v2_prefill(const Layer& L, const void* pool, int num_pages, const int32_t* table,

@@ -25,7 +25,7 @@ def _fill_prefix(case, dims, pool, table):
                          case.k_all[b:b + 1, :n].contiguous().to(DEV))
 
 
-def _run(case, max_context=None, pool=None, fill=True):
+def _run(case, max_context=None, pool=None, fill=True, mode=mla.CHUNK_AUTO):
     dims = lib_dims(case.dims)
     if pool is None:
         pool = canary_pool(case.dims, case.num_pages)
@@ -37,7 +37,7 @@ def _run(case, max_context=None, pool=None, fill=True):
     start = torch.from_numpy(case.start.astype(np.int32)).to(DEV)
     out = mla.prefill_chunk(dims, pool, table, start, case.q_c.to(DEV), case.q_r.to(DEV),
                             c_new.contiguous().to(DEV), k_new.contiguous().to(DEV),
-                            case.w_uk.to(DEV), case.w_uv.to(DEV), max_context=ctx)
+                            case.w_uk.to(DEV), case.w_uv.to(DEV), max_context=ctx, mode=mode)
     torch.cuda.synchronize()
     return pool, out
 
@@ -81,6 +81,7 @@ def test_tiny_fp32_chunk():
         assert_close(f64(out[b]), _oracle(case, b), f"tiny chunk seq {b}")
 
 
+@pytest.mark.parametrize("mode", [mla.CHUNK_EXPAND, mla.CHUNK_ABSORB])
 @pytest.mark.parametrize("start,T,extra", [
     ([0, 64, 130], 1, 0),         # one-token chunks: a decode step done the expanded way
     ([5, 64, 127], 64, 0),        # one tile, prefix across a page edge
@@ -88,12 +89,13 @@ def test_tiny_fp32_chunk():
     ([0, 300], 200, 0),           # one sequence without a prefix
     ([700, 64], 129, 3),          # a prefix of several expansion tiles, the table full
 ])
-def test_v2_chunk_small(start, T, extra):
-    """V2 sizes, short chunks after ragged cached prefixes: every row and
-    head, and the cache bytes of every position."""
-    print(f"case v2 chunk start={start} T={T}", flush=True)
+def test_v2_chunk_small(start, T, extra, mode):
+    """V2 sizes, short chunks after ragged cached prefixes, in both forms (the
+    expanded prompt form and each row absorbed as a decode query): every row
+    and head, and the cache bytes of every position."""
+    print(f"case v2 chunk start={start} T={T} mode={mode}", flush=True)
     case = syn.chunk_case(syn.V2, start, T, seed=6 + T)
-    pool, out = _run(case, max_context=int(case.context.max()) + extra)
+    pool, out = _run(case, max_context=int(case.context.max()) + extra, mode=mode)
     _check_pool(case, pool)
     for b in range(case.batch):
         assert_close(f64(out[b]), _oracle(case, b), f"v2 chunk T={T} seq {b}")
@@ -145,3 +147,30 @@ def test_v2_chunk_2x_3584_512_full_size_sampled():
         got = f64(out[b])[rows][:, heads]
         assert_close(got, _oracle(case, b, rows=rows, heads=heads), f"chunk 2x(3584+512) seq {b}")
     _check_pool(case, pool, batches=[1])
+
+
+def test_v2_short_chunk_after_long_prefix_auto_absorbed():
+    """A 128-token chunk after 3968 cached positions, two sequences: the cost
+    rule picks the absorbed form; sampled rows and heads against the oracle."""
+    print("case v2 chunk 2 x (3968 + 128) auto", flush=True)
+    case = syn.chunk_case(syn.V2, [3968, 3968], 128, seed=3)
+    pool, out = _run(case)
+    assert torch.isfinite(out.float()).all()
+    rows = np.array([0, 1, 63, 64, 100, 127])
+    rng = np.random.default_rng(29)
+    heads = np.sort(rng.choice(case.dims.n_heads, size=6, replace=False))
+    for b in range(case.batch):
+        got = f64(out[b])[rows][:, heads]
+        assert_close(got, _oracle(case, b, rows=rows, heads=heads), f"chunk 2x(3968+128) seq {b}")
+    _check_pool(case, pool, batches=[0])
+
+
+def test_absorbed_mode_bounds():
+    """The absorbed form takes at most 256 tokens per chunk and only the V2
+    sizes: both are rejected on the host."""
+    case = syn.chunk_case(syn.V2, [0], 257, seed=1)
+    with pytest.raises(mla.MlaError):
+        _run(case, mode=mla.CHUNK_ABSORB)
+    tiny = syn.chunk_case(syn.TINY, [5], 8, seed=1)
+    with pytest.raises(mla.MlaError):
+        _run(tiny, mode=mla.CHUNK_ABSORB)

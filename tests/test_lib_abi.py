@@ -112,7 +112,7 @@ def test_prefill_chunk_rejections_on_host(lib):
     d = _dims(n_heads=4, d_nope=16, d_rope=8, d_latent=32, dtype=1)
     cache = _lib._Cache(0x1000, 4, 2, 0x2000)   # 2 pages of 64 positions per sequence
     def call(start, T, ctx, ws_bytes=1 << 30):
-        return lib.mla_prefill_chunk(ctypes.byref(d), ctypes.byref(cache), 1, start, T, ctx, 0x4000, 0x5000,
+        return lib.mla_prefill_chunk(ctypes.byref(d), ctypes.byref(cache), 1, start, T, ctx, 0, 0x4000, 0x5000,
                                      0x6000, 0x7000, 0x8000, 0x9000, 0xa000, 0xb000, ws_bytes, None, None)
     assert call(None, 8, 64) == mla.MLA_ERR_INVALID_ARG and b"start_pos" in lib.mla_last_error()
     assert call(0x3000, 8, 7) == mla.MLA_ERR_INVALID_ARG and b"max_context" in lib.mla_last_error()
