@@ -205,11 +205,16 @@ def _softmax_rows(s: np.ndarray) -> np.ndarray:
 
 
 def decode_ref(q_c, q_r, c_kv, k_r, w_uk, w_uv, *, base: float, scale: float = None,
-               query_pos: int = None, heads=None, chunk: int = 2048) -> np.ndarray:
+               query_pos: int = None, heads=None, chunk: int = 2048,
+               keys_rotated: bool = False) -> np.ndarray:
     """One decode query of one sequence, computed the expanded way.
 
     q_c [n_h, d_h^C], q_r [n_h, d_h^R] (pre-RoPE); c_kv [L, d_c], k_r [L, d_h^R]
     (pre-RoPE), token j at position j; w_uk, w_uv [n_h, d_h^C, d_c].
+    keys_rotated: k_r already holds RoPE(k^R_j, j), the form in which the tech
+    note's cache keeps the shared key ([what the KV cache stores]: the cached
+    k^R is the rotated one), e.g. the cache's stored values; it is then used
+    as given.
     The query sits at ``query_pos`` (default L - 1) and attends tokens
     0 .. query_pos inclusive.  Returns o [len(heads), d_h^C] in fp64 for the
     selected heads (default all).
@@ -233,7 +238,7 @@ def decode_ref(q_c, q_r, c_kv, k_r, w_uk, w_uv, *, base: float, scale: float = N
     n = t + 1
     qc = np.asarray(q_c, dtype=np.float64)[sel]
     qr = rope(np.asarray(q_r, dtype=np.float64)[sel], t, base)          # [h, d_R]
-    kr = rope(k_r[:n], np.arange(n), base)                              # [n, d_R]
+    kr = k_r[:n] if keys_rotated else rope(k_r[:n], np.arange(n), base)  # [n, d_R]
     wk = np.asarray(w_uk, dtype=np.float64)[sel]
     wv = np.asarray(w_uv, dtype=np.float64)[sel]
     scores = np.empty((len(sel), n))

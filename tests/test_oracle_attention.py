@@ -184,3 +184,19 @@ def test_head_subset_and_query_pos():
     a = decode_ref(q_c, q_r, c, kr, wuk, wuv, base=BASE, query_pos=40)
     b = decode_ref(q_c, q_r, c[:41], kr[:41], wuk, wuv, base=BASE)
     np.testing.assert_allclose(a, b, rtol=0, atol=1e-15)
+
+
+def test_decode_keys_as_cached():
+    """Keys handed over already rotated (the cache's form of the shared key,
+    tech note [what the KV cache stores]) give the same output as pre-RoPE
+    keys rotated by the oracle, with the rotation here formed independently as
+    complex multiplication; a mistake in the option (keys rotated twice, or
+    the query left unrotated) fails the comparison."""
+    q_c, q_r, c, kr, wuk, wuv = _tiny_inputs(17, 65)
+    d = kr.shape[1]
+    rot = _complex_rope(kr, np.arange(len(kr))[:, None], d)
+    want = decode_ref(q_c, q_r, c, kr, wuk, wuv, base=BASE)
+    got = decode_ref(q_c, q_r, c, rot, wuk, wuv, base=BASE, keys_rotated=True)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)
+    twice = decode_ref(q_c, q_r, c, rot, wuk, wuv, base=BASE)
+    assert np.max(np.abs(twice - want)) > 1e-6 * np.max(np.abs(want))
