@@ -122,7 +122,12 @@ size_t mla_decode_workspace_size(const mla_dims* dims, int32_t batch, int32_t n_
  * workspace: device memory of at least mla_decode_workspace_size(dims, batch,
  *   n_workgroups) bytes; its contents on entry do not matter.
  * timing_events: NULL, or two hipEvent_t that are recorded on `stream`
- *   immediately before and after the attention kernel (profiling only).       */
+ *   immediately before and after the attention kernel (profiling only).
+ * Range (V2 sizes): the splits hand their normalised latent sums to the
+ *   combine in fp16, so every cached c^KV element must have magnitude below
+ *   65504 (the largest fp16 value); a larger latent gives non-finite outputs,
+ *   never a fault.  bf16 c^KV of the magnitudes a projection produces are far
+ *   inside this range.  The generic family has no such limit.                  */
 mla_status mla_decode(const mla_dims* dims, const mla_paged_cache* cache, int32_t batch,
                       const int32_t* seq_lens, const void* q_nope, const void* q_rope,
                       const void* w_uk, const void* w_uv, void* out, void* workspace,
@@ -293,11 +298,14 @@ mla_status mla_prefill(const mla_dims* dims, const mla_paged_cache* cache, int32
  * prefix costs as much as attending it many times).                         */
 typedef enum { MLA_CHUNK_AUTO = 0, MLA_CHUNK_EXPAND = 1, MLA_CHUNK_ABSORB = 2 } mla_chunk_mode;
 
-/* Bytes of device workspace mla_prefill_chunk needs in any mode (0 for
- * invalid sizes).  For the V2 sizes and chunk_len <= 256 it covers the
- * absorbed form too, sized for the current device's compute units.          */
+/* Bytes of device workspace mla_prefill_chunk needs in the given mode: the
+ * form the call will run (AUTO: the form AUTO picks for chunk_len and
+ * max_context), so a short chunk after a long prefix run absorbed needs no
+ * room for expanded keys.  The absorbed form is sized for the current
+ * device's compute units.  0 for invalid sizes or modes (ABSORB outside the
+ * V2 sizes or above 256 tokens).                                            */
 size_t mla_prefill_chunk_workspace_size(const mla_dims* dims, int32_t batch, int32_t chunk_len,
-                                        int32_t max_context);
+                                        int32_t max_context, int32_t mode);
 
 /* Chunked prefill over an existing latent cache: every sequence b continues
  * with chunk_len prompt tokens at positions start_pos[b] .. start_pos[b] +

@@ -9,7 +9,6 @@ provides device memory and the stream.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 from dataclasses import dataclass
 
@@ -136,7 +135,7 @@ def load() -> ctypes.CDLL:
                                 P, P, P, P, P, P, P, P, ctypes.c_size_t, P, P]
     lib.mla_prefill.restype = ctypes.c_int
     lib.mla_prefill_chunk_workspace_size.argtypes = [ctypes.POINTER(_Dims), ctypes.c_int32, ctypes.c_int32,
-                                                     ctypes.c_int32]
+                                                     ctypes.c_int32, ctypes.c_int32]
     lib.mla_prefill_chunk_workspace_size.restype = ctypes.c_size_t
     lib.mla_prefill_chunk.argtypes = [ctypes.POINTER(_Dims), ctypes.POINTER(_Cache), ctypes.c_int32,
                                       ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32] + \
@@ -623,9 +622,11 @@ def prefill(dims: Dims, pool: torch.Tensor, page_table: torch.Tensor, q_nope: to
     return out
 
 
-def prefill_chunk_workspace_size(dims: Dims, batch: int, chunk_len: int, max_context: int) -> int:
+def prefill_chunk_workspace_size(dims: Dims, batch: int, chunk_len: int, max_context: int,
+                                 mode: int = CHUNK_AUTO) -> int:
     d = dims._c()
-    return int(load().mla_prefill_chunk_workspace_size(ctypes.byref(d), batch, chunk_len, max_context))
+    return int(load().mla_prefill_chunk_workspace_size(ctypes.byref(d), batch, chunk_len, max_context,
+                                                       int(mode)))
 
 
 def prefill_chunk(dims: Dims, pool: torch.Tensor, page_table: torch.Tensor, start_pos: torch.Tensor,
@@ -656,7 +657,7 @@ def prefill_chunk(dims: Dims, pool: torch.Tensor, page_table: torch.Tensor, star
     if out is None:
         out = torch.empty((B, T, H, dims.d_nope), dtype=dims.dtype, device=dev)
     _need(out, "out", dims.dtype, (B, T, H, dims.d_nope), dev)
-    need = prefill_chunk_workspace_size(dims, B, T, max_context)
+    need = prefill_chunk_workspace_size(dims, B, T, max_context, mode)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -674,6 +675,3 @@ def prefill_chunk(dims: Dims, pool: torch.Tensor, page_table: torch.Tensor, star
     call(stream)
     return out
 
-
-def default_scale(dims: Dims) -> float:
-    return dims.sm_scale if dims.sm_scale > 0 else 1.0 / math.sqrt(dims.d_nope + dims.d_rope)

@@ -521,16 +521,40 @@ size_t mla_prefill_workspace_size(const mla_dims* dims, int32_t batch, int32_t s
   return prefill_need(L, fam, batch, seq_len, seq_len);
 }
 
+// Whether a chunk runs in the absorbed form: ABSORB (validated by the
+// caller), or AUTO where the absorbed form is the cheaper one (V2 sizes).
+static bool chunk_absorbed(Family fam, int32_t mode, int chunk_len, int max_context) {
+  return fam == Family::V2 &&
+         (mode == MLA_CHUNK_ABSORB ||
+          (mode == MLA_CHUNK_AUTO && mla::v2_chunk_absorbed(chunk_len, max_context)));
+}
+
+// Workspace bytes of the form the chunk runs in (0 with *ok false when the
+// device cannot be queried for the absorbed form's split count).
+static size_t chunk_need(const mla::Layer& L, Family fam, bool absorb, int batch, int chunk_len,
+                         int max_context, bool* ok) {
+  *ok = true;
+  if (!absorb) return prefill_need(L, fam, batch, chunk_len, max_context);
+  int wg = 0;
+  if (resolve_wg(0, &wg) != 0) {
+    *ok = false;
+    return 0;
+  }
+  return mla::v2_chunk_absorbed_workspace(batch, chunk_len, max_context, wg);
+}
+
 size_t mla_prefill_chunk_workspace_size(const mla_dims* dims, int32_t batch, int32_t chunk_len,
-                                        int32_t max_context) {
+                                        int32_t max_context, int32_t mode) {
   mla::Layer L;
   Family fam;
   if (check_dims(dims, &L, &fam) != MLA_OK || batch < 1 || chunk_len < 1 || max_context < chunk_len)
     return 0;
-  int wg = 0;
-  if (fam == Family::V2 && chunk_len <= mla::kChunkAbsorbMax && resolve_wg(0, &wg) == 0)
-    return mla::v2_prefill_workspace(batch, chunk_len, max_context, wg);
-  return prefill_need(L, fam, batch, chunk_len, max_context);
+  if (mode < MLA_CHUNK_AUTO || mode > MLA_CHUNK_ABSORB) return 0;
+  if (mode == MLA_CHUNK_ABSORB && (fam != Family::V2 || chunk_len > mla::kChunkAbsorbMax)) return 0;
+  bool ok = true;
+  const size_t need = chunk_need(L, fam, chunk_absorbed(fam, mode, chunk_len, max_context), batch,
+                                 chunk_len, max_context, &ok);
+  return ok ? need : 0;
 }
 
 // Shared body of mla_prefill (start_pos NULL, max_context = seq_len) and
@@ -565,13 +589,12 @@ static mla_status prefill_common(const mla_dims* dims, const mla_paged_cache* ca
     return fail(MLA_ERR_UNSUPPORTED, "the absorbed chunk form is implemented for the V2 sizes only");
   if (mode == MLA_CHUNK_ABSORB && chunk_len > mla::kChunkAbsorbMax)
     return fail(MLA_ERR_INVALID_ARG, "the absorbed chunk form takes at most 256 tokens per chunk");
-  const bool absorb = fam == Family::V2 &&
-                      (mode == MLA_CHUNK_ABSORB ||
-                       (mode == MLA_CHUNK_AUTO && mla::v2_chunk_absorbed(chunk_len, max_context)));
+  const bool absorb = chunk_absorbed(fam, mode, chunk_len, max_context);
   int wg = 0;
   if (absorb && resolve_wg(0, &wg) != 0) return fail(MLA_ERR_HIP, "cannot query the device");
-  const size_t need = absorb ? mla::v2_prefill_workspace(batch, chunk_len, max_context, wg)
-                             : prefill_need(L, fam, batch, chunk_len, max_context);
+  bool ok = true;
+  const size_t need = chunk_need(L, fam, absorb, batch, chunk_len, max_context, &ok);
+  if (!ok) return fail(MLA_ERR_HIP, "cannot query the device");
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(MLA_ERR_WORKSPACE, ws_name);
   if (need > 0) MLA_TRY(check_ptr(workspace, "workspace"));

@@ -832,8 +832,9 @@ decode_splitkv_kernel(const char* __restrict__ pool, int num_pages, const int32_
 //     as O^T = W^UV_h o_lat^T; wave v owns rows 32v..32v+31, its W^UV
 //     fragments are loaded before step 1 so their latency hides behind it.
 // With olat_out given, step 1 also writes o_lat (the bf16 hi part, i.e.
-// o_lat rounded to nearest even) to olat_out[b, h, :] and step 2 is skipped:
-// the caller applies W^UV merged into W^O.
+// o_lat rounded to nearest even) to olat_out[b, h, :] (and the lo part to
+// olat_lo when given) and step 2 is skipped: the caller applies W^UV merged
+// into W^O.  out_lo: NULL, or the bf16 rounding residual of out.
 // LDS rows are 1 KiB (512 bf16); chunk c of row b sits at chunk c ^ (b & 15),
 // so a 16-lane read of one chunk of 16 rows hits 16 distinct bank groups.
 // ---------------------------------------------------------------------------
@@ -843,7 +844,8 @@ constexpr int CO_NT = 512;
 __global__ void __launch_bounds__(CO_NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 combine_out_kernel(const int32_t* __restrict__ plan, int B, const float* __restrict__ part_ml,
                    const uint16_t* __restrict__ part_o, const uint16_t* __restrict__ w_uv,
-                   uint16_t* __restrict__ out, uint16_t* __restrict__ olat_out) {
+                   uint16_t* __restrict__ out, uint16_t* __restrict__ olat_out,
+                   uint16_t* __restrict__ out_lo, uint16_t* __restrict__ olat_lo) {
   // the bf16 hi / lo rows of o_lat; before they are written, the same bytes
   // hold the per-group partials of a block with fewer than CO_NB sequences
   __shared__ __attribute__((aligned(16))) char lds[2 * CO_NB * DL * 2];
@@ -981,8 +983,10 @@ combine_out_kernel(const int32_t* __restrict__ plan, int B, const float* __restr
           const int byte = i * (DL * 2) + (((c >> 3) ^ (i & 15)) << 4) + (c & 7) * 2;
           *(uint2*)(ohi + byte) = make_uint2(hi2[0], hi2[1]);
           *(uint2*)(olo + byte) = make_uint2(lo2[0], lo2[1]);
-          if (olat_out)
+          if (olat_out) {
             *(uint2*)(olat_out + ((size_t)b * H + h) * DL + c) = make_uint2(hi2[0], hi2[1]);
+            if (olat_lo) *(uint2*)(olat_lo + ((size_t)b * H + h) * DL + c) = make_uint2(lo2[0], lo2[1]);
+          }
         }
       }
     }
@@ -1009,15 +1013,22 @@ combine_out_kernel(const int32_t* __restrict__ plan, int B, const float* __restr
   }
   const int b = b0 + n;
   if (b < B) {
-    uint16_t* dst = out + ((size_t)b * H + h) * DC + 32 * wave + 4 * g;
+    const size_t o0 = ((size_t)b * H + h) * DC + 32 * wave + 4 * g;
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
-      ushort4 v;
+      ushort4 v, vl;
       v.x = bf16_bits_rne_f32(acc[4 * q4 + 0]);
       v.y = bf16_bits_rne_f32(acc[4 * q4 + 1]);
       v.z = bf16_bits_rne_f32(acc[4 * q4 + 2]);
       v.w = bf16_bits_rne_f32(acc[4 * q4 + 3]);
-      *(ushort4*)(dst + 8 * q4) = v;
+      *(ushort4*)(out + o0 + 8 * q4) = v;
+      if (out_lo) {
+        vl.x = bf16_bits_rne_f32(acc[4 * q4 + 0] - bf16_bits_to_f32(v.x));
+        vl.y = bf16_bits_rne_f32(acc[4 * q4 + 1] - bf16_bits_to_f32(v.y));
+        vl.z = bf16_bits_rne_f32(acc[4 * q4 + 2] - bf16_bits_to_f32(v.z));
+        vl.w = bf16_bits_rne_f32(acc[4 * q4 + 3] - bf16_bits_to_f32(v.w));
+        *(ushort4*)(out_lo + o0 + 8 * q4) = vl;
+      }
     }
   }
 }
@@ -1030,7 +1041,8 @@ hipError_t launch_v2_decode(const Layer& L, const void* pool, int num_pages, con
                             int max_pages, int batch, const int32_t* seq_lens, const void* q_nope,
                             const void* q_rope, const void* w_uk, const void* w_uv, void* out,
                             void* ws, int n_wg, void* const* ev, hipStream_t s, const void* c_new,
-                            const void* k_new, const void* q_lat, void* olat_out) {
+                            const void* k_new, const void* q_lat, void* olat_out, void* out_lo,
+                            void* olat_lo) {
   using namespace v2;
   const WsLayout lay(batch, n_wg);
   char* base = (char*)ws;
@@ -1060,7 +1072,7 @@ hipError_t launch_v2_decode(const Layer& L, const void* pool, int num_pages, con
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(combine_out_kernel, dim3(H * ((batch + CO_NB - 1) / CO_NB)), dim3(CO_NT), 0, s,
                      plan, batch, part_ml, part_o, (const uint16_t*)w_uv, (uint16_t*)out,
-                     (uint16_t*)olat_out);
+                     (uint16_t*)olat_out, (uint16_t*)out_lo, (uint16_t*)olat_lo);
   return hipGetLastError();
 }
 

@@ -128,12 +128,15 @@ size_t v2_decode_workspace(int batch, int n_wg);
 // ([batch, n_heads, d_latent]); q_nope and w_uk are then not read.
 // olat_out: NULL, or [batch, n_heads, d_latent] that receives the normalised
 // latent outputs o_lat (bf16) in place of out = W^UV o_lat (w_uv, out unused).
+// out_lo / olat_lo: NULL, or where the bf16 rounding residual of out / of
+// o_lat goes (a later bf16 product then takes the value as hi + lo parts).
 hipError_t launch_v2_decode(const Layer& L, const void* pool, int num_pages, const int32_t* table,
                             int max_pages, int batch, const int32_t* seq_lens, const void* q_nope,
                             const void* q_rope, const void* w_uk, const void* w_uv, void* out,
                             void* ws, int n_wg, void* const* ev, hipStream_t s,
                             const void* c_new = nullptr, const void* k_new = nullptr,
-                            const void* q_lat = nullptr, void* olat_out = nullptr);
+                            const void* q_lat = nullptr, void* olat_out = nullptr,
+                            void* out_lo = nullptr, void* olat_lo = nullptr);
 // W^OV = [W^O_i W^UV_i]_i ([d_model, n_heads * d_latent], fp32 sums, bf16 RNE) (proj.hip)
 hipError_t launch_v2_merge_output(const Layer& L, int d_model, const void* w_o, const void* w_uv,
                                   void* w_ov, hipStream_t s);
@@ -173,10 +176,12 @@ hipError_t launch_v2_decode_layer(const Layer& L, const void* pool, int num_page
                                   const void* w_uq, const void* w_qr, const void* w_uk,
                                   const void* w_uv, const void* w_o, void* u, void* ws, int n_wg,
                                   void* const* ev, hipStream_t s);
-// chunked prefill as launch_generic_prefill (prefill_v2.hip).  n_wg > 0 also
-// sizes the absorbed form of a short chunk (chunk_len <= kChunkAbsorbMax).
+// chunked prefill as launch_generic_prefill (prefill_v2.hip): the workspace
+// of the expanded form, and of the absorbed form of a short chunk
+// (chunk_len <= kChunkAbsorbMax) run with n_wg split-KV workgroups
 constexpr int kChunkAbsorbMax = 256;
-size_t v2_prefill_workspace(int batch, int chunk_len, int max_context, int n_wg = 0);
+size_t v2_prefill_workspace(int batch, int chunk_len, int max_context);
+size_t v2_chunk_absorbed_workspace(int batch, int chunk_len, int max_context, int n_wg);
 // whether a chunk of chunk_len tokens is cheaper done the absorbed way (each
 // row a decode query) than by expanding every position
 bool v2_chunk_absorbed(int chunk_len, int max_context);

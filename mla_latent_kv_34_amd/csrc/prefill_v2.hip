@@ -490,11 +490,12 @@ struct AbsLayout {
 
 }  // namespace v2p
 
-size_t v2_prefill_workspace(int batch, int chunk_len, int max_context, int n_wg) {
-  const size_t e = v2p::PfLayout(batch, chunk_len, max_context).total;
-  if (n_wg <= 0 || chunk_len > kChunkAbsorbMax) return e;
-  const size_t a = v2p::AbsLayout(batch, chunk_len, max_context, n_wg).total;
-  return e > a ? e : a;
+size_t v2_prefill_workspace(int batch, int chunk_len, int max_context) {
+  return v2p::PfLayout(batch, chunk_len, max_context).total;
+}
+
+size_t v2_chunk_absorbed_workspace(int batch, int chunk_len, int max_context, int n_wg) {
+  return v2p::AbsLayout(batch, chunk_len, max_context, n_wg).total;
 }
 
 bool v2_chunk_absorbed(int chunk_len, int max_context) {

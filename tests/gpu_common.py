@@ -100,3 +100,14 @@ def store_round(x, dtype: str = "bf16") -> np.ndarray:
     if dtype == "f32":
         return np.asarray(f32_rne(x), dtype=np.float64)
     return (bf16_bits_rne(x).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def cached_keys(k_rows, dtype: str, base: float) -> np.ndarray:
+    """The shared RoPE keys as the cache holds them: RoPE(k^R_j, j) at
+    positions 0.. rounded once (nearest even) to the storage type.  These are
+    the bytes the append writes (bit-exact against the oracle's
+    append_expected in the append tests), i.e. the key values the decode
+    kernels receive; the decode oracle takes them with keys_rotated=True."""
+    from oracle import rope
+    k = np.asarray(k_rows, dtype=np.float64)
+    return store_round(rope(k, np.arange(len(k)), base), dtype)

@@ -165,6 +165,55 @@ def test_v2_short_chunk_after_long_prefix_auto_absorbed():
     _check_pool(case, pool, batches=[0])
 
 
+@pytest.mark.parametrize("mode", [mla.CHUNK_EXPAND, mla.CHUNK_ABSORB])
+def test_v2_chunk_peaky_softmax(mode):
+    """Chunk queries x 3 (a peaky softmax) after cached prefixes, in both
+    forms, every row and head at the path's bar."""
+    import dataclasses
+    print(f"case chunk peaky mode {mode}", flush=True)
+    case = syn.chunk_case(syn.V2, [500, 900], 64, seed=33)
+    case = dataclasses.replace(case, q_c=(case.q_c.float() * 3.0).to(case.q_c.dtype),
+                               q_r=(case.q_r.float() * 3.0).to(case.q_r.dtype))
+    pool, out = _run(case, mode=mode)
+    for b in range(case.batch):
+        assert_close(f64(out[b]), _oracle(case, b), f"peaky chunk seq {b} (start {case.start[b]})")
+    _check_pool(case, pool)
+
+
+def test_chunk_workspace_sized_by_form():
+    """The workspace query sizes the form that runs: a short chunk after a
+    long prefix needs far less absorbed (no expanded keys for the prefix);
+    ABSORB runs with exactly its own size, EXPAND rejects that size before
+    launching anything, and AUTO (which picks the absorbed form here) asks
+    for the absorbed size."""
+    print("case chunk workspace by form", flush=True)
+    case = syn.chunk_case(syn.V2, [3968, 3968], 128, seed=3)
+    dims = lib_dims(case.dims)
+    B, T, ctx = case.batch, case.chunk_len, int(case.context.max())
+    ws_abs = mla.prefill_chunk_workspace_size(dims, B, T, ctx, mla.CHUNK_ABSORB)
+    ws_exp = mla.prefill_chunk_workspace_size(dims, B, T, ctx, mla.CHUNK_EXPAND)
+    assert 0 < ws_abs < ws_exp
+    assert mla.prefill_chunk_workspace_size(dims, B, T, ctx, mla.CHUNK_AUTO) == ws_abs
+    pool = canary_pool(case.dims, case.num_pages)
+    table = torch.from_numpy(case.table).to(DEV)
+    _fill_prefix(case, dims, pool, table)
+    ws = torch.empty(ws_abs, dtype=torch.uint8, device=DEV)
+    c_new, k_new = case.chunk_rows()
+    start = torch.from_numpy(case.start.astype(np.int32)).to(DEV)
+    args = (dims, pool, table, start, case.q_c.to(DEV), case.q_r.to(DEV), c_new.contiguous().to(DEV),
+            k_new.contiguous().to(DEV), case.w_uk.to(DEV), case.w_uv.to(DEV))
+    before = pool_bits(pool)
+    with pytest.raises(mla.MlaError) as e:
+        mla.prefill_chunk(*args, max_context=ctx, mode=mla.CHUNK_EXPAND, workspace=ws)
+    assert e.value.status == mla.MLA_ERR_WORKSPACE
+    torch.cuda.synchronize()
+    assert np.array_equal(pool_bits(pool), before)      # nothing ran
+    out = mla.prefill_chunk(*args, max_context=ctx, mode=mla.CHUNK_ABSORB, workspace=ws)
+    torch.cuda.synchronize()
+    for b in range(B):
+        assert_close(f64(out[b]), _oracle(case, b), f"absorbed chunk seq {b}")
+
+
 def test_absorbed_mode_bounds():
     """The absorbed form takes at most 256 tokens per chunk and only the V2
     sizes: both are rejected on the host."""

@@ -12,7 +12,7 @@ from oracle import append_expected, decode_ref, front_end
 
 pytestmark = pytest.mark.gpu
 
-from gpu_common import DEV, assert_close, store_round, canary_pool, f64, fill_cache, lib_dims, pool_bits  # noqa: E402
+from gpu_common import DEV, assert_close, cached_keys, store_round, canary_pool, f64, fill_cache, lib_dims, pool_bits  # noqa: E402
 
 
 def _run(hc: syn.HiddenCase, n_workgroups=0):
@@ -39,9 +39,10 @@ def _oracle(hc: syn.HiddenCase, b: int, heads=None):
     c_rows, k_rows = base.seq_rows(b)
     n = int(base.cached[b])
     c_all = np.vstack([c_rows[:n].double().numpy(), c_new[None]])
-    k_all = np.vstack([k_rows[:n].double().numpy(), k_new[None]])
+    k_all = cached_keys(np.vstack([k_rows[:n].double().numpy(), k_new[None]]), base.dims.dtype,
+                        base.dims.rope_base)
     o = decode_ref(q_c, q_r, c_all, k_all, base.w_uk.double().numpy(), base.w_uv.double().numpy(),
-                   base=base.dims.rope_base, heads=heads)
+                   base=base.dims.rope_base, heads=heads, keys_rotated=True)
     return o, c_new, k_new
 
 
@@ -128,6 +129,22 @@ def test_decode_hidden_b64_ragged_full_size_sampled():
         ref, c_new, k_new = _oracle(hc, int(b), heads=heads)
         assert_close(f64(out[b])[heads], ref, f"seq {b} (cached {hc.base.cached[b]})")
         _check_new_row(hc, bits, int(b), c_new, k_new)
+
+
+def test_decode_hidden_peaky_softmax():
+    """W^DQ x 3, so queries and logits x 3 (a peaky softmax): the heads'
+    outputs o of the decode from hidden states at the path's bar (c^Q reaches
+    the second projection stage as bf16 hi + lo parts)."""
+    import dataclasses
+    print("case decode_hidden peaky", flush=True)
+    lens = syn.ragged_lengths(8, 200, 3000, seed=57)
+    hc = syn.hidden_case(syn.V2, lens, seed=57, shuffle=True)
+    w_dkv, w_kr, w_dq, w_uq, w_qr = hc.front
+    hc = dataclasses.replace(hc, front=(w_dkv, w_kr, (w_dq.float() * 3.0).to(w_dq.dtype), w_uq, w_qr))
+    pool, out = _run(hc)
+    for b in range(hc.base.batch):
+        ref, _, _ = _oracle(hc, b)
+        assert_close(f64(out[b]), ref, f"peaky seq {b} (cached {hc.base.cached[b]})")
 
 
 def test_decode_hidden_tiny_fp32():

@@ -11,7 +11,7 @@ from oracle import decode_ref, front_end, output_proj
 
 pytestmark = pytest.mark.gpu
 
-from gpu_common import DEV, assert_close, store_round, canary_pool, f64, fill_cache, lib_dims  # noqa: E402
+from gpu_common import DEV, assert_close, cached_keys, store_round, canary_pool, f64, fill_cache, lib_dims  # noqa: E402
 
 
 def _run(hc: syn.HiddenCase, w_o: torch.Tensor, seq_lens=None):
@@ -39,9 +39,10 @@ def _oracle(hc: syn.HiddenCase, w_o: torch.Tensor, b: int):
     c_rows, k_rows = base.seq_rows(b)
     n = int(base.cached[b])
     c_all = np.vstack([c_rows[:n].double().numpy(), c_new[None]])
-    k_all = np.vstack([k_rows[:n].double().numpy(), k_new[None]])
+    k_all = cached_keys(np.vstack([k_rows[:n].double().numpy(), k_new[None]]), base.dims.dtype,
+                        base.dims.rope_base)
     o = decode_ref(q_c, q_r, c_all, k_all, base.w_uk.double().numpy(), base.w_uv.double().numpy(),
-                   base=base.dims.rope_base)
+                   base=base.dims.rope_base, keys_rotated=True)
     return output_proj(o, w_o.double().numpy())
 
 

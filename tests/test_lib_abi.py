@@ -118,18 +118,21 @@ def test_prefill_chunk_rejections_on_host(lib):
     assert call(0x3000, 8, 7) == mla.MLA_ERR_INVALID_ARG and b"max_context" in lib.mla_last_error()
     assert call(0x3000, 8, 129) == mla.MLA_ERR_INVALID_ARG and b"page_table" in lib.mla_last_error()
     assert call(0x3002, 8, 64) == mla.MLA_ERR_INVALID_ARG and b"aligned" in lib.mla_last_error()
-    need = lib.mla_prefill_chunk_workspace_size(ctypes.byref(d), 1, 8, 100)
+    size = lambda dd, B, T, ctx, mode=0: lib.mla_prefill_chunk_workspace_size(  # noqa: E731
+        ctypes.byref(dd), B, T, ctx, mode)
+    need = size(d, 1, 8, 100)
     assert need == 100 * 2 * 4 * 16 * 4                  # fp32 K^C and V^C for 100 positions
+    assert size(d, 1, 8, 100, mla.CHUNK_EXPAND) == need
     assert call(0x3000, 8, 100, need - 1) == mla.MLA_ERR_WORKSPACE
-    assert lib.mla_prefill_chunk_workspace_size(ctypes.byref(d), 1, 8, 7) == 0
+    assert size(d, 1, 8, 7) == 0
+    assert size(d, 1, 8, 100, mla.CHUNK_ABSORB) == 0     # the absorbed form: V2 sizes only
+    assert size(d, 1, 8, 100, 3) == 0                    # not a mode
     # a whole prompt is the chunk at start 0 with max_context = its length
-    assert lib.mla_prefill_workspace_size(ctypes.byref(d), 3, 50) == \
-        lib.mla_prefill_chunk_workspace_size(ctypes.byref(d), 3, 50, 50)
+    assert lib.mla_prefill_workspace_size(ctypes.byref(d), 3, 50) == size(d, 3, 50, 50)
     v2 = _dims()
-    assert lib.mla_prefill_workspace_size(ctypes.byref(v2), 2, 4096) == \
-        lib.mla_prefill_chunk_workspace_size(ctypes.byref(v2), 2, 4096, 4096)
-    assert lib.mla_prefill_chunk_workspace_size(ctypes.byref(v2), 2, 512, 4096) > \
-        lib.mla_prefill_chunk_workspace_size(ctypes.byref(v2), 2, 512, 512)
+    assert lib.mla_prefill_workspace_size(ctypes.byref(v2), 2, 4096) == size(v2, 2, 4096, 4096)
+    assert size(v2, 2, 512, 4096) > size(v2, 2, 512, 512)
+    assert size(v2, 2, 512, 4096, mla.CHUNK_ABSORB) == 0  # above 256 tokens
 
 
 def test_layer_and_merge_rejections_on_host(lib):
