@@ -34,6 +34,7 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 BYTES_PER_TOKEN = 1152          # one cached row: 576 bf16
 FLOP_PER_TOKEN = 278528         # 2*128*576 (scores) + 2*128*512 (latent sum)
+WARM_S = 1.0                    # untimed sustained-load warm-up per leg (--warm-seconds)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_splitkv_v2_b64_ragged_traffic.json")
 KERNEL_SRCS = [os.path.join(ROOT, "mla_latent_kv_34_amd", "csrc", f)
                for f in ("decode_v2.hip", "splitkv_asm.h")]
@@ -54,6 +55,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--replicas", type=int, default=4)
+    ap.add_argument("--warm-seconds", type=float, default=1.0,
+                    help="untimed warm-up per leg after the --warmup steps, so that the timed steps "
+                         "run at the clock a sustained decode loop settles at")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-clock budget of the oracle sample (cpu_baseline)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
@@ -63,6 +67,10 @@ def parse():
     ap.add_argument("--no-hidden", action="store_true",
                     help="skip the decode-from-hidden-states measurement")
     ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--batch", type=int, default=64,
+                    help="batch of the ragged decode workload (64 is the headline configuration)")
+    ap.add_argument("--legs", default="tiny_decode,v2_b1_4k,v2_b4_128k",
+                    help="comma-separated other decode workloads to time ('none' for none)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device copy of this many bytes (HBM counter calibration)")
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
@@ -130,6 +138,8 @@ def main():
     if args.traffic_from:
         write_traffic(args)
         return
+    global WARM_S
+    WARM_S = args.warm_seconds
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
@@ -148,7 +158,7 @@ def main():
     d = syn.V2
     dims = mla.Dims(d.n_heads, d.d_nope, d.d_rope, d.d_latent, d.page_size, d.torch_dtype,
                     rope_base=d.rope_base)
-    lens = syn.ragged_lengths(64, 1024, 8192, seed=0)
+    lens = syn.ragged_lengths(args.batch, 1024, 8192, seed=0)
     B = len(lens)
     attended = lens + 1
     tokens = int(attended.sum())
@@ -174,28 +184,22 @@ def main():
         seq_lens = torch.tensor(attended, dtype=torch.int32, device=dev)
         q_c, q_r = case.q_c.to(dev), case.q_r.to(dev)
         w_uk, w_uv = case.w_uk.to(dev), case.w_uv.to(dev)
-        ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-        for e in ev:
-            e.record()
         dec, out = mla.decode_step(dims, pool, table, seq_lens, new_c, new_k, q_c, q_r, w_uk, w_uv,
                                    prepare=True)
-        dec_t, _ = mla.decode_step(dims, pool, table, seq_lens, new_c, new_k, q_c, q_r, w_uk, w_uv,
-                                   out=out, timing_events=ev, prepare=True)
-        reps.append(dict(dec=dec, dec_t=dec_t, ev=ev, out=out,
+        reps.append(dict(dec=dec, out=out,
                          keep=(pool, table, seq_lens, new_c, new_k, q_c, q_r, w_uk, w_uv)))
         if r > 0:
             del case
     torch.cuda.synchronize()
     resident = sum(r["keep"][0].numel() * 2 for r in reps) / 1e9
 
-    def step(i, timed=False):
-        r = reps[i % len(reps)]
-        (r["dec_t"] if timed else r["dec"])()
+    def step(i):
+        reps[i % len(reps)]["dec"]()
 
     # ---- eager: whole-step time and per-launch attention-kernel time
     for i in range(args.warmup):
         step(i)
-    torch.cuda.synchronize()
+    warm_s = warm_clock(step, args.warm_seconds)
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record()
     for i in range(args.steps):
@@ -203,13 +207,11 @@ def main():
     t1.record()
     torch.cuda.synchronize()
     eager_ms = t0.elapsed_time(t1) / args.steps
-    # attention kernel durations (events recorded by the library around it)
-    kern_ms = []
-    for i in range(args.steps):
-        step(i, timed=True)
-        r = reps[i % len(reps)]
-        torch.cuda.synchronize()
-        kern_ms.append(r["ev"][0].elapsed_time(r["ev"][1]))
+    # attention kernel durations (events the library records around it), the
+    # steps issued back to back as in the timed loop, one sync at the end
+    kern_ms = back_to_back_kernel_ms(
+        lambda i, ev: mla.decode_step(dims, *reps[i % len(reps)]["keep"][:9], out=reps[i % len(reps)]["out"],
+                                      timing_events=ev, prepare=True)[0], args.steps)
     kern_pct = [round(float(v), 5) for v in np.percentile(kern_ms, [10, 50, 90])]
     kern_ms = float(np.mean(kern_ms))
 
@@ -245,7 +247,7 @@ def main():
                 graphs[i].replay()
 
         replay_steps(args.warmup)
-        torch.cuda.synchronize()
+        warm_clock(lambda i: g_all.replay(), args.warm_seconds)  # capture left the GPU idle
         t0.record()
         replay_steps(args.steps)
         t1.record()
@@ -263,7 +265,7 @@ def main():
         try:
             tf = json.load(open(TRAFFIC_FILE))
             if (tf.get("kernel_source_sha256") == kernel_source_sha256()
-                    and tf.get("workload") == "v2_b64_ragged"):
+                    and tf.get("workload") == f"v2_b{B}_ragged"):
                 traffic = tf.get("bytes_per_launch")
         except Exception:
             traffic = None
@@ -280,6 +282,12 @@ def main():
     n_reps = len(reps)
     if not args.no_hidden:
         hid = hidden_bench(mla, syn, dims, dev, lens, args.steps, args.warmup, args.replicas)
+
+    legs = None
+    names = [] if args.legs == "none" else [x for x in args.legs.split(",") if x]
+    if names:
+        legs = {name: decode_leg(mla, syn, dev, name, args.steps, args.warmup, not args.no_cpu,
+                                 args.warm_seconds) for name in names}
 
     cpu = None
     if not args.no_cpu:
@@ -299,14 +307,15 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "v2_b64_ragged: DeepSeek-V2 MLA layer (128 heads, d_h^C 128, d_h^R 64, d_c 512), "
-                        "batch 64, cached 1024-8192 tokens (uniform), shuffled 64-token pages, "
+            "workload": f"v2_b{B}_ragged: DeepSeek-V2 MLA layer (128 heads, d_h^C 128, d_h^R 64, d_c 512), "
+                        f"batch {B}, cached 1024-8192 tokens (uniform), shuffled 64-token pages, "
                         "append 1 token + absorbed decode",
             "batch": B,
             "attended_tokens": tokens,
             "replicas": n_reps,
             "resident_cache_GB": round(resident, 3),
             "timing": "hip graph replay, one graph per %d consecutive steps" % n_reps if graph_ms is not None else "eager launches",
+            "warmup": f"{args.warmup} steps, then {warm_s:.2f} s of untimed steps (sustained-load clock)",
         },
         "latent_cache_GBps": round(cache_bytes / (ms * 1e-3) / 1e9, 1),
         "step_hbm_frac": round(cache_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
@@ -321,16 +330,249 @@ def main():
             "traffic": traffic,
             "kernel_ms": round(kern_ms, 5),
             "kernel_ms_p10_p50_p90": kern_pct,
+            "kernel_timing": "hip events the library records around the kernel, steps issued back to back",
             "algorithmic_bytes": cache_bytes,
             "mfma": {"achieved": round(kern_tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(kern_tflops / MFMA_BF16_PEAK_TFLOPS, 4)},
         },
         "cpu_baseline": cpu,
+        "decode_legs": legs,
         "prefill": pre,
         "prefill_chunk": chk,
         "decode_hidden": hid,
     }
     print(json.dumps(line), flush=True)
+
+
+def warm_clock(step, seconds: float) -> float:
+    """Untimed steps until `seconds` of wall time have passed (the GPU raises
+    its clock over the first few hundred ms of sustained work; a short burst
+    of steps would be timed at a lower clock than a serving loop runs at).
+    Returns the seconds spent."""
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(32):
+            step(i)
+            i += 1
+        torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+def back_to_back_kernel_ms(make_call, n: int):
+    """Durations (ms) of the kernel that the library brackets with its two
+    timing events, over n calls issued back to back on the current stream
+    with a single synchronisation at the end (the regime of a decode loop).
+    make_call(i, events) returns a prepared call that records into events."""
+    import torch
+    pairs = []
+    for _ in range(n):
+        ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        for e in ev:
+            e.record()  # creates the underlying HIP event
+        pairs.append(ev)
+    calls = [make_call(i, pairs[i]) for i in range(n)]
+    torch.cuda.synchronize()
+    for c in calls:
+        c()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in pairs]
+
+
+def graph_replay_ms(calls, steps: int, warmup: int):
+    """Mean ms per call when the calls (one per replica, in turn) are replayed
+    from HIP graphs: one graph holding a call on every replica, plus one graph
+    per replica for a step count that is not a multiple of the replica count."""
+    import torch
+    R = len(calls)
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        for c in calls:
+            c()
+    torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    g_all = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_all):
+        for c in calls:
+            c()
+    singles = []
+    for c in calls:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            c()
+        singles.append(g)
+
+    def replay(n):
+        for _ in range(n // R):
+            g_all.replay()
+        for i in range(n % R):
+            singles[i].replay()
+
+    replay(warmup)
+    warm_clock(lambda i: g_all.replay(), WARM_S)  # capture left the GPU idle
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    replay(steps)
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
+LEG_TEXT = {
+    "tiny_decode": "tiny fp32 layer (n_h 4, d_h^C 16, d_h^R 8, d_c 32), batch 1, 64 cached tokens + 1 "
+                   "appended, positions 0..64 (generic kernel family; latency only)",
+    "v2_b1_4k": "DeepSeek-V2 layer, batch 1, 4096 cached tokens in contiguous 64-token pages, the query "
+                "is the token at position 4095 (launch-bound latency)",
+    "v2_b4_128k": "DeepSeek-V2 layer, batch 4 x 131072 cached tokens (151 MB of latent cache per "
+                  "sequence), shuffled 64-token pages, split-KV over all compute units + combine",
+}
+LEG_REPLICAS = {"tiny_decode": 1, "v2_b1_4k": 8, "v2_b4_128k": 2}
+LEG_ORACLE_HEADS = {"tiny_decode": None, "v2_b1_4k": None, "v2_b4_128k": 16}
+
+
+def decode_leg(mla, syn, dev, name: str, steps: int, warmup: int, with_cpu: bool, warm_s: float):
+    """One of the other decode workloads: step time by graph replay over
+    cache/weight replicas (enough to exceed the 256 MB last-level cache where
+    the working set is small), the split-KV kernel by back-to-back events, and
+    the oracle timed on a sample of the same inputs."""
+    import numpy as np
+    import torch
+
+    R = LEG_REPLICAS[name]
+    print(f"[bench] decode leg {name}: {R} replicas", file=sys.stderr, flush=True)
+    reps = []
+    case0 = None
+    for r in range(R):
+        case = syn.config_case(name, seed=r)
+        d = case.dims
+        dims = mla.Dims(d.n_heads, d.d_nope, d.d_rope, d.d_latent, d.page_size, d.torch_dtype,
+                        rope_base=d.rope_base)
+        pool = torch.zeros((case.num_pages, d.page_size, d.row), dtype=d.torch_dtype, device=dev)
+        table = torch.from_numpy(case.table).to(dev)
+        zero = torch.zeros(1, dtype=torch.int32, device=dev)
+        for b in range(case.batch):
+            c, kr = case.seq_rows(b)
+            n = int(case.cached[b])
+            mla.cache_append(dims, pool, table[b:b + 1].contiguous(), zero,
+                             c[:n].unsqueeze(0).to(dev), kr[:n].unsqueeze(0).to(dev))
+        seq_lens = torch.tensor(case.attended, dtype=torch.int32, device=dev)
+        q_c, q_r = case.q_c.to(dev), case.q_r.to(dev)
+        w_uk, w_uv = case.w_uk.to(dev), case.w_uv.to(dev)
+        if case.append:
+            new_c = torch.stack([case.seq_rows(b)[0][-1] for b in range(case.batch)]).contiguous().to(dev)
+            new_k = torch.stack([case.seq_rows(b)[1][-1] for b in range(case.batch)]).contiguous().to(dev)
+            keep = (pool, table, seq_lens, new_c, new_k, q_c, q_r, w_uk, w_uv)
+            fn = mla.decode_step
+        else:
+            keep = (pool, table, seq_lens, q_c, q_r, w_uk, w_uv)
+            fn = mla.decode
+        call, out = fn(dims, *keep, prepare=True)
+        reps.append(dict(call=call, out=out, keep=keep, fn=fn, dims=dims))
+        if r == 0:
+            case0 = case
+        else:
+            del case
+    torch.cuda.synchronize()
+    tokens = int(case0.attended.sum())
+    for i in range(warmup):
+        reps[i % R]["call"]()
+    warm_clock(lambda i: reps[i % R]["call"](), warm_s)
+    ms = graph_replay_ms([r["call"] for r in reps], steps, warmup)
+    warm_clock(lambda i: reps[i % R]["call"](), WARM_S / 2)
+    kern = back_to_back_kernel_ms(
+        lambda i, ev: reps[i % R]["fn"](reps[i % R]["dims"], *reps[i % R]["keep"], out=reps[i % R]["out"],
+                                        timing_events=ev, prepare=True)[0], steps)
+    kern_pct = [round(float(v), 5) for v in np.percentile(kern, [10, 50, 90])]
+    kern_ms = float(np.mean(kern))
+    row_bytes = case0.dims.row * (2 if case0.dims.dtype == "bf16" else 4)
+    cache_bytes = tokens * row_bytes
+    flop = tokens * 2 * case0.dims.n_heads * (case0.dims.row + case0.dims.d_latent)
+    achieved = cache_bytes / (kern_ms * 1e-3) / 1e9
+    res = {
+        "workload": f"{name}: {LEG_TEXT[name]}",
+        "batch": int(case0.batch), "attended_tokens": tokens, "replicas": R,
+        "us_per_step": round(ms * 1e3, 2),
+        "value": round(tokens / (ms * 1e-3), 1), "unit": "cached tokens/s",
+        "latent_cache_GBps": round(cache_bytes / (ms * 1e-3) / 1e9, 1),
+        "step_hbm_frac": round(cache_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "timing": f"hip graph replay over {R} replica(s)",
+        "roofline": {
+            "kernel": "decode_splitkv" if case0.dims.dtype == "bf16" else "generic decode",
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4), "kernel_ms": round(kern_ms, 5),
+            "kernel_ms_p10_p50_p90": kern_pct, "algorithmic_bytes": cache_bytes,
+            "kernel_timing": "hip events the library records around the kernel, calls issued back to back",
+            "mfma": {"achieved": round(flop / (kern_ms * 1e-3) / 1e12, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(flop / (kern_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
+        },
+    }
+    del reps
+    torch.cuda.synchronize()
+    if with_cpu:
+        res["cpu_oracle"] = leg_oracle(case0, LEG_ORACLE_HEADS[name])
+    return res
+
+
+def _blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        return len(os.sched_getaffinity(0))
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def leg_oracle(case, heads):
+    """The fp64 oracle on the leg's workload: every sequence, or the first
+    `heads` heads of sequence 0 for the long-context leg; three runs on the
+    host's BLAS threads and, for the small workloads, three on one thread."""
+    import numpy as np
+    from oracle import decode_ref
+
+    f64 = lambda t: t.double().numpy()  # noqa: E731
+    wk, wv = f64(case.w_uk), f64(case.w_uv)
+    n_h = case.dims.n_heads
+    sel = None if heads is None else list(range(heads))
+    seqs = range(case.batch) if heads is None else [0]
+    tokens = sum(int(case.attended[b]) for b in seqs)
+    frac = 1.0 if heads is None else heads / n_h
+
+    def one():
+        t = time.perf_counter()
+        for b in seqs:
+            c, kr = case.seq_rows(b)
+            decode_ref(f64(case.q_c[b]), f64(case.q_r[b]), f64(c), f64(kr), wk, wv,
+                       base=case.dims.rope_base, heads=sel)
+        return time.perf_counter() - t
+
+    runs = [one() for _ in range(3 if heads is None else 1)]
+    out = {"kind": "oracle", "unit": "cached tokens/s", "cores": _blas_threads(), "cpu_model": cpu_model(),
+           "value": round(tokens * frac / min(runs), 1), "runs_s": [round(x, 3) for x in runs],
+           "sample": ("the whole workload" if heads is None else
+                      f"heads 0..{heads - 1} of sequence 0 ({tokens} attended tokens), tokens/s scaled "
+                      f"by {heads}/{n_h}") + ", fp64 numpy"}
+    if heads is None:
+        try:
+            from threadpoolctl import threadpool_limits
+            with threadpool_limits(1):
+                runs1 = [one() for _ in range(3)]
+            out["one_thread"] = {"value": round(tokens / min(runs1), 1), "cores": 1,
+                                 "runs_s": [round(x, 3) for x in runs1]}
+        except ImportError:
+            pass
+    return out
 
 
 def hidden_bench(mla, syn, dims, dev, lens, steps: int, warmup: int, replicas: int):
@@ -407,7 +649,7 @@ def hidden_bench(mla, syn, dims, dev, lens, steps: int, warmup: int, replicas: i
         """(mean event-bracketed ms, step ms by graph replay) of one call kind."""
         for i in range(warmup):
             reps[i % R][kc]()
-        torch.cuda.synchronize()
+        warm_clock(lambda i: reps[i % R][kc](), WARM_S / 2)
         evms = []
         for i in range(steps):
             r = reps[i % R]
@@ -439,7 +681,7 @@ def hidden_bench(mla, syn, dims, dev, lens, steps: int, warmup: int, replicas: i
                 singles[i].replay()
 
         replay(warmup)
-        torch.cuda.synchronize()
+        warm_clock(lambda i: g.replay(), WARM_S / 2)  # capture left the GPU idle
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0.record()
         replay(steps)
@@ -515,7 +757,7 @@ def prefill_bench(mla, syn, dims, dev, steps: int):
     call_t, _ = mla.prefill(dims, pool, table, *args, out=out, timing_events=ev, prepare=True)
     for _ in range(3):
         call()
-    torch.cuda.synchronize()
+    warm_clock(lambda i: call(), WARM_S)
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record()
     for _ in range(steps):
@@ -572,7 +814,7 @@ def chunk_bench(mla, syn, dims, dev, steps: int):
                                   timing_events=ev, prepare=True)
     for _ in range(3):
         call()
-    torch.cuda.synchronize()
+    warm_clock(lambda i: call(), WARM_S)
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record()
     for _ in range(steps):
@@ -645,11 +887,7 @@ def cpu_baseline(case, budget_s: float):
     import numpy as np
     from oracle import decode_ref
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
+    threads = _blas_threads()
     f64 = lambda t: t.double().numpy()  # noqa: E731
     wk, wv = f64(case.w_uk), f64(case.w_uv)
     done_tok = 0
@@ -664,8 +902,8 @@ def cpu_baseline(case, budget_s: float):
             break
     el = time.perf_counter() - t_start
     return {"value": round(done_tok / el, 1), "unit": "cached tokens/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{seqs} of 64 sequences (all 128 heads, {done_tok} attended tokens) of the "
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "sample": f"{seqs} of {case.batch} sequences (all 128 heads, {done_tok} attended tokens) of the "
                       f"same workload, fp64 numpy, {el:.1f} s"}
 
 
