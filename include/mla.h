@@ -150,6 +150,26 @@ mla_status mla_decode_step(const mla_dims* dims, const mla_paged_cache* cache, i
                            const void* q_nope, const void* q_rope, const void* w_uk,
                            const void* w_uv, void* out, void* workspace, size_t workspace_bytes,
                            int32_t n_workgroups, void* const* timing_events, void* stream);
+/* mla_decode_step without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  It allocates nothing; its kernels use a
+ * static device array inside the library (80 MiB, one copy on every GPU the
+ * library runs on, held until the process ends) as their workspace.
+ * Limit: the workspace mla_decode_workspace_size(dims, batch, n_workgroups)
+ * reports must fit in 80 MiB (batch up to about 170 with 256 workgroups);
+ * larger calls return MLA_ERR_WORKSPACE before anything is enqueued.
+ * Every call on a GPU shares that GPU's array: calls that overlap on one GPU
+ * (on different streams, or from different threads) race and give undefined
+ * results; calls ordered on one stream are safe.  Nothing in the array has to
+ * start at zero (each call writes the parts it reads).  V2 sizes only
+ * (MLA_ERR_UNSUPPORTED otherwise).  Every other argument, the results and
+ * the errors are as for mla_decode_step.                                    */
+mla_status mla_decode_step_noalloc(const mla_dims* dims, const mla_paged_cache* cache,
+                                   int32_t batch, const int32_t* seq_lens, const void* c_kv_new,
+                                   const void* k_rope_new, const void* q_nope, const void* q_rope,
+                                   const void* w_uk, const void* w_uv, void* out,
+                                   int32_t n_workgroups, void* const* timing_events, void* stream);
+
 /* Bytes of device workspace mla_decode_hidden needs (0 for unsupported sizes). */
 size_t mla_decode_hidden_workspace_size(const mla_dims* dims, int32_t batch, int32_t n_workgroups,
                                         int32_t d_model, int32_t d_q);

@@ -4,7 +4,8 @@ and un-absorbed causal prefill (whole prompts or chunks over an existing
 cache), as HIP kernels behind the C ABI in
 include/mla.h.  This package is the thin Python binding."""
 from ._lib import (  # noqa: F401
-    Dims, MlaError, LibraryMissing, load, cache_append, decode, decode_step, decode_workspace_size,
+    Dims, MlaError, LibraryMissing, load, cache_append, decode, decode_step, decode_step_noalloc,
+    decode_workspace_size,
     decode_hidden, decode_hidden_workspace_size, decode_layer, merge_query_weights,
     decode_hidden_merged, merge_output_weights, decode_layer_merged, prefill, prefill_workspace_size, prefill_chunk,
     prefill_chunk_workspace_size, LIB_PATH, EXPORTED,

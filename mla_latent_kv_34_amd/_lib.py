@@ -23,6 +23,7 @@ MLA_BF16, MLA_F32 = 0, 1
 
 EXPORTED = (
     "mla_cache_append", "mla_decode_workspace_size", "mla_decode", "mla_decode_step",
+    "mla_decode_step_noalloc",
     "mla_decode_hidden_workspace_size", "mla_decode_hidden",
     "mla_decode_layer", "mla_merge_query_weights", "mla_decode_hidden_merged",
     "mla_merge_output_weights", "mla_decode_layer_merged",
@@ -106,6 +107,9 @@ def load() -> ctypes.CDLL:
     lib.mla_decode_step.argtypes = [ctypes.POINTER(_Dims), ctypes.POINTER(_Cache), ctypes.c_int32, P, P, P,
                                     P, P, P, P, P, P, ctypes.c_size_t, ctypes.c_int32, P, P]
     lib.mla_decode_step.restype = ctypes.c_int
+    lib.mla_decode_step_noalloc.argtypes = [ctypes.POINTER(_Dims), ctypes.POINTER(_Cache), ctypes.c_int32, P,
+                                            P, P, P, P, P, P, P, ctypes.c_int32, P, P]
+    lib.mla_decode_step_noalloc.restype = ctypes.c_int
     lib.mla_decode_hidden_workspace_size.argtypes = [ctypes.POINTER(_Dims), ctypes.c_int32, ctypes.c_int32,
                                                      ctypes.c_int32, ctypes.c_int32]
     lib.mla_decode_hidden_workspace_size.restype = ctypes.c_size_t
@@ -323,6 +327,44 @@ def decode_step(dims: Dims, pool: torch.Tensor, page_table: torch.Tensor, seq_le
     call = _Prepared(lib.mla_decode_step, args, keep=(d, cache, seq_lens, c_kv_new, k_rope_new, q_nope,
                                                        q_rope, w_uk, w_uv, out, workspace, evs, pool,
                                                        page_table))
+    if prepare:
+        return call, out
+    call(stream)
+    return out
+
+
+def decode_step_noalloc(dims: Dims, pool: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor,
+                        c_kv_new: torch.Tensor, k_rope_new: torch.Tensor, q_nope: torch.Tensor,
+                        q_rope: torch.Tensor, w_uk: torch.Tensor, w_uv: torch.Tensor,
+                        out: torch.Tensor | None = None, n_workgroups: int = 0, stream=None,
+                        timing_events=None, prepare: bool = False):
+    """mla_decode_step_noalloc: decode_step with no workspace (the library's
+    static scratch serves as one).  Arguments as for decode_step."""
+    lib = load()
+    cache = _cache(dims, pool, page_table)
+    dev = pool.device
+    B = q_nope.shape[0]
+    H = dims.n_heads
+    _need(c_kv_new, "c_kv_new", dims.dtype, (B, dims.d_latent), dev)
+    _need(k_rope_new, "k_rope_new", dims.dtype, (B, dims.d_rope), dev)
+    _need(q_nope, "q_nope", dims.dtype, (B, H, dims.d_nope), dev)
+    _need(q_rope, "q_rope", dims.dtype, (B, H, dims.d_rope), dev)
+    _need(w_uk, "w_uk", dims.dtype, (H, dims.d_nope, dims.d_latent), dev)
+    _need(w_uv, "w_uv", dims.dtype, (H, dims.d_nope, dims.d_latent), dev)
+    _need(seq_lens, "seq_lens", torch.int32, (B,), dev)
+    if page_table.shape[0] < B:
+        raise ValueError("page_table has fewer rows than the batch")
+    if out is None:
+        out = torch.empty((B, H, dims.d_nope), dtype=dims.dtype, device=dev)
+    _need(out, "out", dims.dtype, (B, H, dims.d_nope), dev)
+    d = dims._c()
+    args = [ctypes.byref(d), ctypes.byref(cache), B, _ptr(seq_lens), _ptr(c_kv_new), _ptr(k_rope_new),
+            _ptr(q_nope), _ptr(q_rope), _ptr(w_uk), _ptr(w_uv), _ptr(out), n_workgroups]
+    evs = _events(timing_events)
+    args.append(evs.ptr)
+    call = _Prepared(lib.mla_decode_step_noalloc, args,
+                     keep=(d, cache, seq_lens, c_kv_new, k_rope_new, q_nope, q_rope, w_uk, w_uv, out, evs,
+                           pool, page_table))
     if prepare:
         return call, out
     call(stream)

@@ -260,6 +260,46 @@ mla_status mla_decode_step(const mla_dims* dims, const mla_paged_cache* cache, i
                   "decode step launch");
 }
 
+mla_status mla_decode_step_noalloc(const mla_dims* dims, const mla_paged_cache* cache,
+                                   int32_t batch, const int32_t* seq_lens, const void* c_kv_new,
+                                   const void* k_rope_new, const void* q_nope, const void* q_rope,
+                                   const void* w_uk, const void* w_uv, void* out,
+                                   int32_t n_workgroups, void* const* timing_events, void* stream) {
+  mla::Layer L;
+  Family fam;
+  MLA_TRY(check_dims(dims, &L, &fam));
+  if (fam != Family::V2)
+    return fail(MLA_ERR_UNSUPPORTED, "mla_decode_step_noalloc is implemented for the V2 sizes only");
+  MLA_TRY(check_cache(cache));
+  if (batch < 1) return fail(MLA_ERR_INVALID_ARG, "batch must be >= 1");
+  MLA_TRY(check_idx(seq_lens, "seq_lens"));
+  MLA_TRY(check_ptr(c_kv_new, "c_kv_new"));
+  MLA_TRY(check_ptr(k_rope_new, "k_rope_new"));
+  MLA_TRY(check_ptr(q_nope, "q_nope"));
+  MLA_TRY(check_ptr(q_rope, "q_rope"));
+  MLA_TRY(check_ptr(w_uk, "w_uk"));
+  MLA_TRY(check_ptr(w_uv, "w_uv"));
+  MLA_TRY(check_ptr(out, "out"));
+  if (n_workgroups < 0 || n_workgroups > 65536)
+    return fail(MLA_ERR_INVALID_ARG, "n_workgroups must be in [0, 65536]");
+  int wg = 0;
+  if (resolve_wg(n_workgroups, &wg) != 0) return fail(MLA_ERR_HIP, "cannot query the device");
+  const size_t need = mla::v2_decode_workspace(batch, wg);
+  if (need > mla::kStaticScratchBytes)
+    return fail(MLA_ERR_WORKSPACE,
+                "batch " + std::to_string(batch) + " with " + std::to_string(wg) + " workgroups needs " +
+                    std::to_string(need) + " bytes of scratch; the static scratch holds " +
+                    std::to_string(mla::kStaticScratchBytes) + " (use mla_decode_step with a workspace)");
+  void* ws = mla::v2_static_scratch();
+  if (!ws) return fail(MLA_ERR_HIP, "cannot look up the static scratch on the current device");
+  g_err.clear();
+  return launched(mla::launch_v2_decode(L, cache->pool, cache->num_pages, cache->page_table,
+                                        cache->max_pages, batch, seq_lens, q_nope, q_rope, w_uk,
+                                        w_uv, out, ws, wg, timing_events, (hipStream_t)stream,
+                                        c_kv_new, k_rope_new),
+                  "decode step launch");
+}
+
 namespace {
 // sizes of the projections around the decode.  The V2 family streams K in
 // 64-wide steps, so both K sizes must be multiples of 64 there; the generic

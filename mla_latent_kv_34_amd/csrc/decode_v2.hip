@@ -25,6 +25,7 @@
 // un-normalised o_lat) go to slot w + b of the workspace; combine_out merges
 // the slots of each sequence and applies W^UV.
 #include <cmath>
+#include <mutex>
 
 #include "mla_internal.h"
 
@@ -1036,6 +1037,31 @@ combine_out_kernel(const int32_t* __restrict__ plan, int B, const float* __restr
 }  // namespace v2
 
 size_t v2_decode_workspace(int batch, int n_wg) { return v2::WsLayout(batch, n_wg).total; }
+
+// ---------------------------------------------------------------------------
+// Static scratch of the decode step that takes no workspace (for callers that
+// cannot allocate).  One copy per GPU, held until the process ends.  Host
+// code never passes the array's name to a kernel (in host code it is a
+// stand-in, not a device address): it passes the address that
+// hipGetSymbolAddress gives for the current device, looked up once per device
+// on the first call there.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+void* v2_static_scratch() {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* ptr[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    ptr[dev] = p;
+  }
+  return ptr[dev];
+}
 
 hipError_t launch_v2_decode(const Layer& L, const void* pool, int num_pages, const int32_t* table,
                             int max_pages, int batch, const int32_t* seq_lens, const void* q_nope,

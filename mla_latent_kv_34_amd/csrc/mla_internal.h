@@ -121,6 +121,13 @@ hipError_t launch_generic_decode_hidden(const Layer& L, const void* pool, int nu
 
 // MFMA family for the V2 sizes
 size_t v2_decode_workspace(int batch, int n_wg);
+// The decode workspace in a static device array (one per GPU), for the decode
+// step without a workspace argument: its bytes, and its address on the
+// current device (NULL if the lookup fails).  Every call writes the parts it
+// reads, so nothing in it has to start at zero; calls that overlap on one GPU
+// share it and race.
+constexpr size_t kStaticScratchBytes = (size_t)80 << 20;
+void* v2_static_scratch();
 // c_new / k_new: NULL, or the token at position seq_lens[b] - 1 of every
 // sequence ([batch, d_latent], [batch, d_rope]), appended to the cache by the
 // first kernel of the decode (before any cache read).

@@ -173,3 +173,18 @@ def test_layer_and_merge_rejections_on_host(lib):
     assert lib.mla_merge_output_weights(ctypes.byref(v2), 5000, P[0], P[1], P[2], None) == mla.MLA_ERR_INVALID_ARG
     assert lib.mla_merge_output_weights(ctypes.byref(v2), 5120, P[0], P[1], None, None) == mla.MLA_ERR_INVALID_ARG
     assert b"w_ov" in lib.mla_last_error()
+
+
+def test_noalloc_step_rejections_on_host(lib):
+    """mla_decode_step_noalloc exists for the V2 sizes only and checks its
+    pointers before looking at any device."""
+    cache = _lib._Cache(0x1000, 1, 1, 0x2000)
+    P = [0x4000 + 0x1000 * i for i in range(8)]
+    tiny = _dims(n_heads=4, d_nope=16, d_rope=8, d_latent=32, dtype=1)
+    v2 = _dims()
+    call = lambda d, ptrs: lib.mla_decode_step_noalloc(  # noqa: E731
+        ctypes.byref(d), ctypes.byref(cache), 2, 0x3000, *ptrs, 0, None, None)
+    assert call(tiny, P[:7]) == mla.MLA_ERR_UNSUPPORTED
+    bad = list(P[:7])
+    bad[4] = None                                        # w_uk
+    assert call(v2, bad) == mla.MLA_ERR_INVALID_ARG and b"w_uk" in lib.mla_last_error()
