@@ -149,14 +149,25 @@ constexpr int SEG_UNITS = 10;     // a segment (query load, partial store, pipel
 constexpr int PLAN_NT = 256;      // threads of the block that builds the plan
 constexpr int PLAN_CACHE = 2048;  // sequences whose prefixes stay in LDS for the searches
 
+// LDS-only workgroup barrier: waits for this wave's LDS accesses, not for its
+// global stores (which nothing in the block reads back).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Builds the plan with one block of PLAN_NT threads.  cache: LDS scratch of
 // PLAN_CACHE * 12 bytes (S and P of the first PLAN_CACHE sequences, for the
-// binary searches; larger batches search the global copies).
+// searches; larger batches search the global copies, which then have to be
+// complete before the searches, so only they wait for the global stores).
+// The first and last workgroup of sequence b have a closed form: workgroup w
+// covers units [x_w, x_{w+1}) and touches b's sub-tiles exactly when
+// x_{w+1} > P_b + seg and x_w <= P_{b+1} - 2, so
+//   first_b = ceil((P_b + seg + 1) W_eff / U) - 1,
+//   last_b  = ceil((P_{b+1} - 1) W_eff / U) - 1.
 __device__ void plan_block(const int32_t* __restrict__ seq_lens, int B, int W,
                            int32_t* __restrict__ plan, long long* __restrict__ plan_u,
                            int4* __restrict__ wg, char* cache) {
   __shared__ long long wsum[2][PLAN_NT / 64];
-  __shared__ long long tot_s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   long long* c_p = (long long*)cache;                  // P (units)
   int32_t* c_s = (int32_t*)(cache + PLAN_CACHE * 8);   // S (sub-tiles)
@@ -179,7 +190,7 @@ __device__ void plan_block(const int32_t* __restrict__ seq_lens, int B, int W,
       wsum[0][wave] = xs;
       wsum[1][wave] = xu;
     }
-    __syncthreads();
+    lds_barrier();
     long long bs = 0, bu = 0, ts = 0, tu = 0;
 #pragma unroll
     for (int v = 0; v < PLAN_NT / 64; ++v) {
@@ -192,8 +203,6 @@ __device__ void plan_block(const int32_t* __restrict__ seq_lens, int B, int W,
       const long long es = carry_s + bs + xs - n, eu = carry_u + bu + xu - u;
       plan[b] = (int32_t)es;
       plan_u[b] = eu;
-      plan[B + 1 + 2 * b] = 0x7fffffff;  // first / last, lowered / raised below
-      plan[B + 2 + 2 * b] = -1;
       if (b < PLAN_CACHE) {
         c_s[b] = (int32_t)es;
         c_p[b] = eu;
@@ -201,7 +210,7 @@ __device__ void plan_block(const int32_t* __restrict__ seq_lens, int B, int W,
     }
     carry_s += ts;
     carry_u += tu;
-    __syncthreads();  // wsum is reused by the next chunk
+    lds_barrier();  // wsum is reused by the next chunk
   }
   const long long N = carry_s;
   const bool weighted = carry_u >= (long long)(SEG_UNITS + 2) * W;
@@ -214,12 +223,24 @@ __device__ void plan_block(const int32_t* __restrict__ seq_lens, int B, int W,
     plan[3 * B + 1] = We;
   }
   for (int ib = We + tid; ib < W; ib += PLAN_NT) wg[ib] = make_int4(0, 0, 0, 0);
-  __syncthreads();  // plan, plan_u and the cache are complete
+  if (B > PLAN_CACHE) __syncthreads();  // the searches read the global S and P
+  else lds_barrier();
   auto S_of = [&](int b) -> long long { return b >= B ? N : (b < PLAN_CACHE ? c_s[b] : plan[b]); };
   auto P_of = [&](int b) -> long long {
     if (!weighted) return 2 * S_of(b);
     return b >= B ? U : (b < PLAN_CACHE ? c_p[b] : plan_u[b]);
   };
+  // first and last workgroup of every sequence (first > last: no sub-tiles)
+  for (int b = tid; b < B; b += PLAN_NT) {
+    int first = 0x7fffffff, last = -1;
+    if (N > 0 && S_of(b + 1) > S_of(b)) {
+      const long long f = (P_of(b) + seg + 1) * We, l = (P_of(b + 1) - 1) * We;
+      first = (int)max(0LL, (f + U - 1) / U - 1);
+      last = (int)min((long long)We - 1, (l + U - 1) / U - 1);
+    }
+    plan[B + 1 + 2 * b] = first;
+    plan[B + 2 + 2 * b] = last;
+  }
   // sequence b with P_b <= x < P_{b+1} (the last such b for x == U: B - 1)
   auto seq_of_unit = [&](long long x) {
     int lo = 0, hi = B - 1;
@@ -244,13 +265,6 @@ __device__ void plan_block(const int32_t* __restrict__ seq_lens, int B, int W,
     const long long s1 = g_of(x1, x1 >= U ? B - 1 : seq_of_unit(x1));
     while (b0 + 1 < B && S_of(b0 + 1) <= s0) ++b0;  // the sequence holding sub-tile s0
     wg[launched_of_logical(w, We)] = make_int4((int)s0, (int)s1, b0, w);
-    if (s1 > s0) {
-      for (int b = b0; b < B && S_of(b) < s1; ++b) {
-        if (S_of(b + 1) == S_of(b)) continue;  // empty sequence
-        atomicMin(&plan[B + 1 + 2 * b], w);
-        atomicMax(&plan[B + 2 + 2 * b], w);
-      }
-    }
   }
   if (N == 0 && tid == 0) wg[0] = make_int4(0, 0, 0, 0);
 }
@@ -677,6 +691,9 @@ decode_splitkv_kernel(const char* __restrict__ pool, int num_pages, const int32_
 #pragma unroll
   for (int cb = 0; cb < DL / 32; ++cb) acc[cb] = (f32x16){};
   float m_run = -INFINITY, l_part = 0.f;
+  // wave-uniform: no sub-tile of the current segment has raised m_run yet, so
+  // the accumulators and l_part are still zero and need no rescale
+  bool fresh = true;
 
   // ---- the stream: the copies run up to three sub-tiles ahead
   for (int i = 0;; ++i) {
@@ -729,24 +746,27 @@ decode_splitkv_kernel(const char* __restrict__ pool, int num_pages, const int32_
     // AGPRs.
     if (__any(mx > m_run + 8.0f)) {
       const float m_new = fmaxf(m_run, mx);
-      const float alpha = (m_run == -INFINITY) ? 0.f : exp2_fast(m_run - m_new);
+      if (!fresh) {
+        const float alpha = (m_run == -INFINITY) ? 0.f : exp2_fast(m_run - m_new);
 #pragma unroll
-      for (int cb = 0; cb < DL / 32; ++cb)
+        for (int cb = 0; cb < DL / 32; ++cb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = acc[cb][r];
-          float tmp;
-          asm volatile(
-              "v_accvgpr_read_b32 %1, %0\n\t"
-              "v_mul_f32 %1, %1, %2\n\t"
-              "v_accvgpr_write_b32 %0, %1"
-              : "+a"(x), "=&v"(tmp)
-              : "v"(alpha));
-          acc[cb][r] = x;
-        }
-      asm volatile("s_nop 7");
-      l_part *= alpha;
+          for (int r = 0; r < 16; ++r) {
+            float x = acc[cb][r];
+            float tmp;
+            asm volatile(
+                "v_accvgpr_read_b32 %1, %0\n\t"
+                "v_mul_f32 %1, %1, %2\n\t"
+                "v_accvgpr_write_b32 %0, %1"
+                : "+a"(x), "=&v"(tmp)
+                : "v"(alpha));
+            acc[cb][r] = x;
+          }
+        asm volatile("s_nop 7");
+        l_part *= alpha;
+      }
       m_run = m_new;
+      fresh = false;
     }
     // (m_run is still -inf only while every token so far was masked; then
     // every score here is -inf too and every probability 0)
@@ -810,13 +830,17 @@ decode_splitkv_kernel(const char* __restrict__ pool, int num_pages, const int32_
       for (int cb = 0; cb < DL / 32; ++cb) acc[cb] = (f32x16){};
       m_run = -INFINITY;
       l_part = 0.f;
+      fresh = true;
     }
     cc = nx;
   }
 }
 
 // ---------------------------------------------------------------------------
-// combine_out: one workgroup of 8 waves per (head h, block of 32 sequences).
+// combine_out: one workgroup of 8 waves per (head h, block of nb sequences),
+// nb a power of two up to 32 that the host lowers until the launch has at
+// least two workgroups per compute unit (small batches: few sequences per
+// workgroup, many threads per sequence's slots).
 //  1. combine: o_lat[b] = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s over
 //     the partial slots (w + b) of the workgroups w that covered sequence b
 //     (M = max_s m_s), kept in LDS as bf16 hi + lo parts (hi = bf16(x), lo =
@@ -843,7 +867,7 @@ constexpr int CO_NB = 32;
 constexpr int CO_NT = 512;
 
 __global__ void __launch_bounds__(CO_NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
-combine_out_kernel(const int32_t* __restrict__ plan, int B, const float* __restrict__ part_ml,
+combine_out_kernel(const int32_t* __restrict__ plan, int B, int nb, const float* __restrict__ part_ml,
                    const uint16_t* __restrict__ part_o, const uint16_t* __restrict__ w_uv,
                    uint16_t* __restrict__ out, uint16_t* __restrict__ olat_out,
                    uint16_t* __restrict__ out_lo, uint16_t* __restrict__ olat_lo) {
@@ -853,13 +877,13 @@ combine_out_kernel(const int32_t* __restrict__ plan, int B, const float* __restr
   __shared__ float2 grp_ml[CO_NT / 16];
   char* const ohi = lds;
   char* const olo = lds + CO_NB * DL * 2;
-  const int nbb = (B + CO_NB - 1) / CO_NB;
+  const int nbb = (B + nb - 1) / nb;
   // launched workgroup ib runs on XCD ib % 8: the sequence blocks of one head
   // get neighbouring logical indices on one XCD, so W^UV_h is fetched into
   // that XCD's L2 once
   const int G8 = (int)gridDim.x, ib = (int)blockIdx.x;
   const int L = (ib & 7) * (G8 >> 3) + min(ib & 7, G8 & 7) + (ib >> 3);
-  const int h = L / nbb, b0 = (L % nbb) * CO_NB;
+  const int h = L / nbb, b0 = (L % nbb) * nb;
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int g = lane >> 5, n = lane & 31;
 
@@ -874,7 +898,7 @@ combine_out_kernel(const int32_t* __restrict__ plan, int B, const float* __restr
   // ---- 1. merged latent vectors into LDS
   {
     const int gi = tid >> 4, cq = tid & 15;
-    const int nseq = min(CO_NB, B - b0);
+    const int nseq = min(nb, B - b0);
     const int R = CO_NB / nseq;  // groups per sequence (block-uniform)
     const int i = gi / R, r = gi - i * R;
     const int b = b0 + i;
@@ -1012,8 +1036,10 @@ combine_out_kernel(const int32_t* __restrict__ plan, int B, const float* __restr
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ks], bh, acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ks], bl, acc, 0, 0, 0);
   }
+  // column n of the product is sequence b0 + n, the block's own sequences
+  // only (with nb < 32 the later columns belong to other workgroups)
   const int b = b0 + n;
-  if (b < B) {
+  if (n < nb && b < B) {
     const size_t o0 = ((size_t)b * H + h) * DC + 32 * wave + 4 * g;
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
@@ -1096,8 +1122,12 @@ hipError_t launch_v2_decode(const Layer& L, const void* pool, int num_pages, con
                      (const int4*)plan_wg, part_ml, part_o, sc_log2);
   e = mark(ev, 1, s);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(combine_out_kernel, dim3(H * ((batch + CO_NB - 1) / CO_NB)), dim3(CO_NT), 0, s,
-                     plan, batch, part_ml, part_o, (const uint16_t*)w_uv, (uint16_t*)out,
+  // sequences per combine workgroup: halved until the launch has at least
+  // two workgroups per compute unit (256 compute units on MI355X)
+  int nb = CO_NB;
+  while (nb > 1 && (long long)H * ((batch + nb - 1) / nb) < 2 * 256) nb >>= 1;
+  hipLaunchKernelGGL(combine_out_kernel, dim3(H * ((batch + nb - 1) / nb)), dim3(CO_NT), 0, s,
+                     plan, batch, nb, part_ml, part_o, (const uint16_t*)w_uv, (uint16_t*)out,
                      (uint16_t*)olat_out, (uint16_t*)out_lo, (uint16_t*)olat_lo);
   return hipGetLastError();
 }
