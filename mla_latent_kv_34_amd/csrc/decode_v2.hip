@@ -101,7 +101,7 @@ struct WsLayout {
     plan = 0;
     plan_u = align256(plan + sizeof(int32_t) * (size_t)(3 * B + 2));
     plan_wg = align256(plan_u + sizeof(long long) * (size_t)(B + 1));
-    q_abs = align256(plan_wg + sizeof(int32_t) * 4 * (size_t)W);
+    q_abs = align256(plan_wg + sizeof(int32_t) * 12 * (size_t)W);
     part_ml = align256(q_abs + (size_t)B * H * ROW * 2);
     part_o = align256(part_ml + slots * H * 2 * sizeof(float));
     total = align256(part_o + slots * H * DL * sizeof(uint16_t));
@@ -129,9 +129,13 @@ struct WsLayout {
 //                            when the sequence is empty)
 //   plan[3B+1]             = W_eff
 //   plan_u[0..B]           = P
-//   wg[ib] = (s0, s1, b0, w) for launched workgroup ib: logical index w,
-//            sub-tile range [s0, s1), b0 the sequence holding sub-tile s0
-//            (s0 == s1 for an idle workgroup).
+//   wg[3 ib .. 3 ib + 2] for launched workgroup ib, everything it needs to
+//            start its first copy without further dependent loads:
+//            (s0, s1, b0, w): logical index w, sub-tile range [s0, s1), b0 the
+//            sequence holding sub-tile s0 (s0 == s1 for an idle workgroup);
+//            (S_b0, S_b0+1, len_b0, 0);
+//            (page id of page j0 of b0, of page j0 + 1, 0, 0) with j0 =
+//            (s0 - S_b0) / 2, -1 for a page index past the table width.
 // Logical workgroups are laid out XCD by XCD: launched workgroup ib runs on
 // XCD ib % 8, and XCD x owns the contiguous logical block starting at
 // x * (W_eff / 8) + min(x, W_eff % 8), so neighbouring splits of a sequence
@@ -166,7 +170,8 @@ __device__ __forceinline__ void lds_barrier() {
 //   last_b  = ceil((P_{b+1} - 1) W_eff / U) - 1.
 __device__ void plan_block(const int32_t* __restrict__ seq_lens, int B, int W,
                            int32_t* __restrict__ plan, long long* __restrict__ plan_u,
-                           int4* __restrict__ wg, char* cache) {
+                           int4* __restrict__ wg, char* cache, const int32_t* __restrict__ table,
+                           int max_pages) {
   __shared__ long long wsum[2][PLAN_NT / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   long long* c_p = (long long*)cache;                  // P (units)
@@ -222,9 +227,17 @@ __device__ void plan_block(const int32_t* __restrict__ seq_lens, int B, int W,
     plan_u[B] = carry_u;
     plan[3 * B + 1] = We;
   }
-  for (int ib = We + tid; ib < W; ib += PLAN_NT) wg[ib] = make_int4(0, 0, 0, 0);
+  for (int ib = We + tid; ib < W; ib += PLAN_NT) wg[3 * ib] = make_int4(0, 0, 0, 0);
   if (B > PLAN_CACHE) __syncthreads();  // the searches read the global S and P
   else lds_barrier();
+  // floor((a b - d) / c) for 1 <= a <= U + SEG_UNITS + 1, b <= W_eff,
+  // d in {0, 1}: in 32-bit unsigned arithmetic when that cannot overflow
+  // (64-bit division is a long software sequence on the GPU), else in 64 bits
+  const bool narrow = (U + SEG_UNITS + 2) * (long long)(We + 1) < (1LL << 32);
+  auto muldiv = [&](long long a, long long b, long long c, int d = 0) -> long long {
+    if (narrow) return (long long)(((unsigned)a * (unsigned)b - (unsigned)d) / (unsigned)c);
+    return (a * b - d) / c;
+  };
   auto S_of = [&](int b) -> long long { return b >= B ? N : (b < PLAN_CACHE ? c_s[b] : plan[b]); };
   auto P_of = [&](int b) -> long long {
     if (!weighted) return 2 * S_of(b);
@@ -234,9 +247,9 @@ __device__ void plan_block(const int32_t* __restrict__ seq_lens, int B, int W,
   for (int b = tid; b < B; b += PLAN_NT) {
     int first = 0x7fffffff, last = -1;
     if (N > 0 && S_of(b + 1) > S_of(b)) {
-      const long long f = (P_of(b) + seg + 1) * We, l = (P_of(b + 1) - 1) * We;
-      first = (int)max(0LL, (f + U - 1) / U - 1);
-      last = (int)min((long long)We - 1, (l + U - 1) / U - 1);
+      // ceil(a We / U) - 1 = floor((a We - 1) / U) for a We >= 1 (here a >= 1)
+      first = (int)max(0LL, muldiv(P_of(b) + seg + 1, We, U, 1));
+      last = (int)min((long long)We - 1, muldiv(P_of(b + 1) - 1, We, U, 1));
     }
     plan[B + 1 + 2 * b] = first;
     plan[B + 2 + 2 * b] = last;
@@ -259,12 +272,20 @@ __device__ void plan_block(const int32_t* __restrict__ seq_lens, int B, int W,
     return S_of(b) + j;
   };
   for (int w = tid; w < We; w += PLAN_NT) {
-    const long long x0 = (long long)w * U / We, x1 = (long long)(w + 1) * U / We;
+    const long long x0 = muldiv(w, U, We), x1 = muldiv(w + 1, U, We);
     int b0 = seq_of_unit(x0);
     const long long s0 = g_of(x0, b0);
     const long long s1 = g_of(x1, x1 >= U ? B - 1 : seq_of_unit(x1));
     while (b0 + 1 < B && S_of(b0 + 1) <= s0) ++b0;  // the sequence holding sub-tile s0
-    wg[launched_of_logical(w, We)] = make_int4((int)s0, (int)s1, b0, w);
+    const int ib = launched_of_logical(w, We);
+    const long long sb = S_of(b0);
+    const int j0 = (int)((s0 - sb) >> 1);
+    auto page = [&](int j) {
+      return (s0 < s1 && j >= 0 && j < max_pages) ? table[(size_t)b0 * max_pages + j] : -1;
+    };
+    wg[3 * ib] = make_int4((int)s0, (int)s1, b0, w);
+    wg[3 * ib + 1] = make_int4((int)sb, (int)S_of(b0 + 1), seq_lens[b0], 0);
+    wg[3 * ib + 2] = make_int4(page(j0), page(j0 + 1), 0, 0);
   }
   if (N == 0 && tid == 0) wg[0] = make_int4(0, 0, 0, 0);
 }
@@ -297,7 +318,7 @@ q_absorb_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __restrict_
   __shared__ __attribute__((aligned(16))) char wl[2 * DC * 128];
   static_assert(2 * DC * 128 >= PLAN_CACHE * 12, "plan cache must fit the tile buffer");
   if (blockIdx.x == 0) {
-    plan_block(seq_lens, B, W, plan, plan_u, plan_wg, wl);
+    plan_block(seq_lens, B, W, plan, plan_u, plan_wg, wl, table, max_pages);
     return;
   }
   if (blockIdx.x > 4 * H) {
@@ -331,11 +352,17 @@ q_absorb_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __restrict_
   const int wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 5, n = lane & 31;
   const int nblk = (B + 31) / 32;
-  // B operand q^T[r][b] of an item (32 queries): 8 consecutive r of query b
-  // for each of the 8 k-steps; the first item's loads go out before staging
+  // Items: item t is the 32-column chunk t % 4 of the 128 columns for the
+  // 32 queries of block t / 4; wave v takes the nblk consecutive items
+  // [v nblk, (v + 1) nblk), so a wave meets at most two query blocks when
+  // nblk <= 4 (batches up to 128) and loads each of them once.
+  // B operand q^T[r][b] of a query block: 8 consecutive r of query b for each
+  // of the 8 k-steps; the wave's first two blocks are loaded before staging,
+  // each later block one block ahead.
   bf16x8 bq[DC / 16], bq_next[DC / 16];
-  auto load_q = [&](int item, bf16x8 (&dst)[DC / 16]) {
-    const int b = (item >> 2) * 32 + n;
+  const int t_begin = wave * nblk, t_end = t_begin + nblk;
+  auto load_q = [&](int qb, bf16x8 (&dst)[DC / 16]) {
+    const int b = qb * 32 + n;
     const uint16_t* qp = q_nope + ((size_t)min(b, B - 1) * H + h) * DC + 8 * g;
 #pragma unroll
     for (int s = 0; s < DC / 16; ++s) dst[s] = *(const bf16x8*)(qp + 16 * s);
@@ -359,7 +386,8 @@ q_absorb_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __restrict_
     }
   };
   rope_loads(i0_first);
-  if (!q_lat && wave < 4 * nblk) load_q(wave, bq);
+  if (!q_lat) load_q(t_begin >> 2, bq);
+  if (!q_lat && ((t_end - 1) >> 2) > (t_begin >> 2)) load_q((t_begin >> 2) + 1, bq_next);
   // W^UK_h[:, c0:c0+128] straight into LDS as two [128 rows r][64 cols]
   // halves with 16-byte chunk c of row r at chunk c ^ swz_w(r): 16-byte unit
   // U = (4m + wave) * 64 + lane of the tile is written by load m of the wave
@@ -424,10 +452,15 @@ q_absorb_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __restrict_
   // 16*(G%2) + 4*(s16%4) of the 32-column block mc
   const int rsub = 8 * (G >> 1) + (s16 >> 2);
   const int colsub = 16 * (G & 1) + 4 * (s16 & 3);
-  for (int item = wave; item < 4 * nblk; item += 4) {
+  for (int item = t_begin; item < t_end; ++item) {
     const int mc = item & 3, nb = item >> 2;
     const int b = nb * 32 + n;
-    if (item + 4 < 4 * nblk) load_q(item + 4, bq_next);  // the next item's queries
+    if (item > t_begin && mc == 0) {
+      // a new query block: the one loaded ahead, and the next one ahead
+#pragma unroll
+      for (int s = 0; s < DC / 16; ++s) bq[s] = bq_next[s];
+      if (nb + 1 <= ((t_end - 1) >> 2)) load_q(nb + 1, bq_next);
+    }
     f32x16 acc = {};
 #pragma unroll
     for (int s = 0; s < DC / 16; ++s) {
@@ -458,8 +491,6 @@ q_absorb_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __restrict_
         *(ushort4*)(q_abs + qfrag_index(b, h, c)) = v;
       }
     }
-#pragma unroll
-    for (int s = 0; s < DC / 16; ++s) bq[s] = bq_next[s];
   }
 }
 
@@ -530,6 +561,9 @@ __device__ __forceinline__ void issue_sub(const char* __restrict__ src, char* bu
 // A position in the workgroup's sub-tile stream: global sub-tile s, which is
 // sub-tile j = s - sbeg of sequence b (global sub-tiles [sbeg, send), len
 // tokens): the 32-token half j & 1 of its page j >> 1.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
 struct SubCursor {
   int b, sbeg, send, len, s;
 };
@@ -542,7 +576,20 @@ decode_splitkv_kernel(const char* __restrict__ pool, int num_pages, const int32_
                       const int4* __restrict__ wg, float* __restrict__ part_ml,
                       uint16_t* __restrict__ part_o, float sc_log2) {
   __shared__ __attribute__((aligned(1024))) char lds[NBUF * SUBB];
-  const int4 mine = wg[blockIdx.x];  // (s0, s1, first sequence, logical index)
+  // this workgroup's record, all 48 bytes in one round trip (scalar loads
+  // waited for inside the block)
+  i32x8 r01;
+  i32x4 r2;
+  asm volatile(
+      "s_load_dwordx8 %0, %2, 0x0\n\t"
+      "s_load_dwordx4 %1, %2, 0x20\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=s"(r01), "=s"(r2)
+      : "s"(wg + 3 * blockIdx.x)
+      : "memory");
+  const int4 mine = make_int4(r01[0], r01[1], r01[2], r01[3]);  // (s0, s1, first sequence, logical index)
+  const int4 mseq = make_int4(r01[4], r01[5], r01[6], r01[7]);  // (its first sub-tile, end, length)
+  const int4 mpg = make_int4(r2[0], r2[1], r2[2], r2[3]);  // page ids of the range's first two pages
   const int t0 = mine.x, t1 = mine.y, w = mine.w;  // sub-tile range [t0, t1)
   if (t0 >= t1) return;
   const int tid = threadIdx.x;
@@ -585,9 +632,9 @@ decode_splitkv_kernel(const char* __restrict__ pool, int num_pages, const int32_
   };
   SubCursor cc;
   cc.b = mine.z;
-  cc.sbeg = plan[cc.b];
-  cc.send = plan[cc.b + 1];
-  cc.len = seq_lens[cc.b];
+  cc.sbeg = mseq.x;
+  cc.send = mseq.y;
+  cc.len = mseq.z;
   cc.s = t0;
 
   // ---- DMA side: sub-tile k of the stream goes to LDS slot k % NBUF
@@ -600,9 +647,21 @@ decode_splitkv_kernel(const char* __restrict__ pool, int num_pages, const int32_
     return (ic.s < t1 && j < max_pages) ? table[(size_t)ic.b * max_pages + j] : -1;
   };
   auto half_at_ic = [&]() { return (ic.s - ic.sbeg) & 1; };
+  // the same for the prologue's copies: the range's first two pages come
+  // with the record
+  const int j0 = (t0 - cc.sbeg) >> 1;
+  auto first_page_at_ic = [&]() {
+    if (ic.s < t1 && ic.b == mine.z) {
+      const int j = (ic.s - ic.sbeg) >> 1;
+      if (j == j0) return mpg.x;
+      if (j == j0 + 1) return mpg.y;
+    }
+    return page_at_ic();
+  };
+  // a whole sub-tile copy in one go (prologue)
   auto issue_next = [&]() {
     if (ic.s >= t1) return;
-    const int p = page_at_ic();
+    const int p = first_page_at_ic();
     const bool ok = p >= 0 && p < num_pages;
     const int slot = issued & (NBUF - 1);
     okmask = (okmask & ~(1 << slot)) | ((ok ? 1 : 0) << slot);
@@ -610,9 +669,11 @@ decode_splitkv_kernel(const char* __restrict__ pool, int num_pages, const int32_
     ++issued;
     advance(ic);
   };
-  // The same copy split in three parts spread over a step, so the copies of
-  // the four waves do not all queue up at once in front of the address unit.
-  // copy_begin claims the next sub-tile (page id prefetched by the caller).
+  // The same copy split in three parts spread over a step.  (Spreading its
+  // nine loads singly between the MFMAs saves issue stalls but raises the
+  // power draw: at the power limit the clock drops by more than the cycles
+  // saved.)  copy_begin claims the next sub-tile (page id prefetched by the
+  // caller).
   const char* cp_src = pool;
   char* cp_dst = lds;
   bool cp_on = false;
@@ -636,18 +697,6 @@ decode_splitkv_kernel(const char* __restrict__ pool, int num_pages, const int32_
                                        16, 0, kStreamPolicy);
   };
 
-  // The first copies: the next sub-tile, or (past the end of the range) a
-  // second copy of sub-tile 0 into a slot that is never read, so that the
-  // number of copies after the query loads is fixed.
-  auto issue_or_repeat = [&]() {
-    if (ic.s < t1) {
-      issue_next();
-    } else {
-      const int slot = issued & (NBUF - 1);  // a slot past the last sub-tile
-      issue_sub(pool, lds + slot * SUBB, wave, dp);  // page 0 always exists
-      ++issued;
-    }
-  };
   // rows of sub-tile c that hold tokens (0 if its page is unusable)
   auto valid_rows = [&](const SubCursor& c, int slot) {
     return ((okmask >> slot) & 1) ? min(SUB, c.len - SUB * (c.s - c.sbeg)) : 0;
@@ -676,17 +725,15 @@ decode_splitkv_kernel(const char* __restrict__ pool, int num_pages, const int32_
   // fragment s of this lane: qptr(b) + 512 s (one KiB per fragment and wave)
   auto qptr = [&](int b) { return q_abs + (((size_t)b * 4 + wave) * KSTEPS * 64 + lane) * 8; };
 
-  // ---- prologue: the queries, then three sub-tiles in flight.  The copy
-  // count after the query loads is fixed (issue_or_repeat), so the compiler's
-  // wait for the queries at the first score chain leaves the copies in flight.
-  {
-    const uint16_t* qp = qptr(cc.b);
-#pragma unroll
-    for (int s2 = 0; s2 < KSTEPS; ++s2) qreg[s2] = *(const bf16x8*)(qp + 512 * s2);
-  }
-  issue_or_repeat();
-  issue_or_repeat();
-  issue_or_repeat();
+  // ---- prologue: the first sub-tile's copy and the queries travel
+  // together (the query block waits for both; the first score chain needs
+  // both), then two more sub-tiles go in flight.  Loading the queries inside
+  // the block also keeps the compiler from waiting for every copy before the
+  // loop, as it would for plain loads whose registers the loop reads.
+  issue_next();
+  load_q_sync(qreg, qptr(cc.b));
+  issue_next();
+  issue_next();
   f32x16 acc[DL / 32];
 #pragma unroll
   for (int cb = 0; cb < DL / 32; ++cb) acc[cb] = (f32x16){};
@@ -838,9 +885,9 @@ decode_splitkv_kernel(const char* __restrict__ pool, int num_pages, const int32_
 
 // ---------------------------------------------------------------------------
 // combine_out: one workgroup of 8 waves per (head h, block of nb sequences),
-// nb a power of two up to 32 that the host lowers until the launch has at
-// least two workgroups per compute unit (small batches: few sequences per
-// workgroup, many threads per sequence's slots).
+// nb the smallest power of two up to 32 that keeps the launch within one
+// workgroup per compute unit (small batches: few sequences per workgroup,
+// many threads per sequence's slots).
 //  1. combine: o_lat[b] = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s over
 //     the partial slots (w + b) of the workgroups w that covered sequence b
 //     (M = max_s m_s), kept in LDS as bf16 hi + lo parts (hi = bf16(x), lo =
@@ -953,9 +1000,31 @@ combine_out_kernel(const int32_t* __restrict__ plan, int B, int nb, const float*
         }
       }
     }
+    // o_lat of sequence i, dimensions c .. c + 3, into LDS row i as bf16 hi
+    // and lo parts (and to olat_out / olat_lo)
+    auto put_row = [&](int i, int c, const float (&x)[4]) {
+      uint32_t hi2[2], lo2[2];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const __bf16 h0 = (__bf16)x[2 * k], h1 = (__bf16)x[2 * k + 1];
+        const __bf16 l0 = (__bf16)(x[2 * k] - (float)h0), l1 = (__bf16)(x[2 * k + 1] - (float)h1);
+        hi2[k] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+        lo2[k] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+      }
+      const int byte = i * (DL * 2) + (((c >> 3) ^ (i & 15)) << 4) + (c & 7) * 2;
+      *(uint2*)(ohi + byte) = make_uint2(hi2[0], hi2[1]);
+      *(uint2*)(olo + byte) = make_uint2(lo2[0], lo2[1]);
+      if (olat_out) {
+        const size_t at = ((size_t)(b0 + i) * H + h) * DL + c;
+        *(uint2*)(olat_out + at) = make_uint2(hi2[0], hi2[1]);
+        if (olat_lo) *(uint2*)(olat_lo + at) = make_uint2(lo2[0], lo2[1]);
+      }
+    };
     if (R > 1) {
-      // partials float k of thread t at pf[k * CO_NT + t]; group maxima and
-      // sums in grp_ml
+      // The R group results of every sequence merged by all 512 threads:
+      // group float k of thread t sits at pf[k * CO_NT + t], group maxima
+      // and sums in grp_ml; thread t then merges 4 consecutive dimensions
+      // (16-byte unit cq + 16 j, half hf) of sequences t / 128 + 4 m.
       float* const pf = (float*)lds;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
@@ -963,58 +1032,51 @@ combine_out_kernel(const int32_t* __restrict__ plan, int B, int nb, const float*
         for (int k = 0; k < 8; ++k) pf[(8 * j + k) * CO_NT + tid] = o[j][k];
       if (cq == 0) grp_ml[gi] = make_float2(M, Lsum);
       __syncthreads();
-      if (r == 0 && i < nseq) {
+      const int uq = tid & 127, mcq = uq & 15, mj = (uq >> 4) & 3, hf = uq >> 6;
+      float res[4][4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int si = (tid >> 7) + 4 * m;
+        if (si >= nseq) break;
         float Mt = -INFINITY;
-        for (int q = 0; q < R; ++q) Mt = fmaxf(Mt, grp_ml[gi + q].x);
-        Lsum = 0.f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int k = 0; k < 8; ++k) o[j][k] = 0.f;
+        for (int q = 0; q < R; ++q) Mt = fmaxf(Mt, grp_ml[si * R + q].x);
+        float Ls = 0.f, v[4] = {0.f, 0.f, 0.f, 0.f};
         for (int q = 0; q < R; ++q) {
-          const float2 ml = grp_ml[gi + q];
+          const float2 ml = grp_ml[si * R + q];
           const float f = ml.x == -INFINITY ? 0.f : exp2_fast(ml.x - Mt);
-          Lsum += f * ml.y;
-          const int t = tid + 16 * q;
+          Ls += f * ml.y;
+          const int t = (si * R + q) * 16 + mcq;
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int k = 0; k < 8; ++k) o[j][k] += f * pf[(8 * j + k) * CO_NT + t];
+          for (int e = 0; e < 4; ++e) v[e] += f * pf[(8 * mj + 4 * hf + e) * CO_NT + t];
         }
+        const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) res[m][e] = v[e] * inv;
       }
-      __syncthreads();
-    }
-    // group gi writes row i (its sequence) if it holds the merged result;
-    // rows past the block's sequences are cleared (a row only feeds its own
-    // output column, but the MFMA should not read stale bytes)
-    const bool data_row = r == 0 && i < nseq;
-    if (data_row) {
+      __syncthreads();  // every thread is done with pf before the rows overwrite it
+      const int u = mcq + 16 * mj;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int si = (tid >> 7) + 4 * m;
+        if (si >= nseq) break;
+        put_row(si, 16 * (u >> 1) + 4 * (u & 1) + 8 * hf, res[m]);
+      }
+    } else if (i < nseq) {
+      // one group per sequence: group gi holds the merged result of row gi
       const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int u = cq + 16 * j;
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-          const int c = 16 * (u >> 1) + 4 * (u & 1) + 8 * half;
-          uint32_t hi2[2], lo2[2];
-#pragma unroll
-          for (int k = 0; k < 2; ++k) {
-            const float x0 = o[j][4 * half + 2 * k] * inv, x1 = o[j][4 * half + 2 * k + 1] * inv;
-            const __bf16 h0 = (__bf16)x0, h1 = (__bf16)x1;
-            const __bf16 l0 = (__bf16)(x0 - (float)h0), l1 = (__bf16)(x1 - (float)h1);
-            hi2[k] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-            lo2[k] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
-          }
-          const int byte = i * (DL * 2) + (((c >> 3) ^ (i & 15)) << 4) + (c & 7) * 2;
-          *(uint2*)(ohi + byte) = make_uint2(hi2[0], hi2[1]);
-          *(uint2*)(olo + byte) = make_uint2(lo2[0], lo2[1]);
-          if (olat_out) {
-            *(uint2*)(olat_out + ((size_t)b * H + h) * DL + c) = make_uint2(hi2[0], hi2[1]);
-            if (olat_lo) *(uint2*)(olat_lo + ((size_t)b * H + h) * DL + c) = make_uint2(lo2[0], lo2[1]);
-          }
+          const float x[4] = {o[j][4 * half] * inv, o[j][4 * half + 1] * inv, o[j][4 * half + 2] * inv,
+                              o[j][4 * half + 3] * inv};
+          put_row(i, 16 * (u >> 1) + 4 * (u & 1) + 8 * half, x);
         }
       }
     }
+    // rows past the block's sequences are cleared (a row only feeds its own
+    // output column, but the MFMA should not read stale bytes)
     if (gi >= nseq) {
       // 16 threads x 4 x 16 B clear the 1 KiB hi row and the 1 KiB lo row
 #pragma unroll
@@ -1122,10 +1184,12 @@ hipError_t launch_v2_decode(const Layer& L, const void* pool, int num_pages, con
                      (const int4*)plan_wg, part_ml, part_o, sc_log2);
   e = mark(ev, 1, s);
   if (e != hipSuccess) return e;
-  // sequences per combine workgroup: halved until the launch has at least
-  // two workgroups per compute unit (256 compute units on MI355X)
-  int nb = CO_NB;
-  while (nb > 1 && (long long)H * ((batch + nb - 1) / nb) < 2 * 256) nb >>= 1;
+  // sequences per combine workgroup: the fewest (most threads per
+  // sequence's slots) that still fit the launch in one workgroup per compute
+  // unit (256 on MI355X; a workgroup of 8 waves fills a compute unit), so the
+  // launch runs in one round of its latency-bound merge
+  int nb = 1;
+  while (nb < CO_NB && (long long)H * ((batch + nb - 1) / nb) > 256) nb <<= 1;
   hipLaunchKernelGGL(combine_out_kernel, dim3(H * ((batch + nb - 1) / nb)), dim3(CO_NT), 0, s,
                      plan, batch, nb, part_ml, part_o, (const uint16_t*)w_uv, (uint16_t*)out,
                      (uint16_t*)olat_out, (uint16_t*)out_lo, (uint16_t*)olat_lo);
