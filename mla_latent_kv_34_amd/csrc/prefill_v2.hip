@@ -40,6 +40,19 @@ constexpr int ROWB = 1152;  // cached row bytes
 constexpr int PS = 64;      // page size = key tile
 constexpr int TILEB = PS * ROWB;
 
+typedef unsigned int u32x16 __attribute__((ext_vector_type(16)));
+
+// One wave's ten direct-to-LDS loads of a key tile (prefill_attn): load m
+// reads base + voff[m] (base kb for loads 0-3, pb for 4-5, vb for 6-9) into
+// LDS at lb + 4096 m.
+struct TileCopy {
+  uint32_t voff[10];
+  uint32_t lb;
+  const char* kb;
+  const char* pb;
+  const char* vb;
+};
+
 #include "prefill_asm.h"
 
 // 16-byte-chunk swizzle of the LDS tiles whose rows are a multiple of 128
@@ -58,6 +71,21 @@ __device__ __forceinline__ void wait_vmcnt0() {
   __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
 }
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+// s_waitcnt vmcnt(N) with expcnt and lgkmcnt unconstrained (N <= 15).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 15, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(N | (7 << 4) | (15 << 8));
+}
+// max(x, the same value in lane l ^ 32)
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+__device__ __forceinline__ float add_xor32(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
 
 // An accumulator element read into a VGPR (the explicit read keeps the
 // accumulators in AGPRs, which the MFMAs write).
@@ -230,56 +258,74 @@ expand_kernel(const char* __restrict__ pool, int num_pages, const int32_t* __res
   else run(std::false_type{});
 }
 
-// ---------------------------------------------------------------------------
-// prefill_attn: one workgroup per (prompt b, head h, 128-query block of the
-// chunk); wave v owns chunk rows 32v..32v+31 of the block.  Key tiles of 64 (one cache page)
-// are double-buffered in LDS as four regions of 128-byte rows, each filled by
-// direct-to-LDS loads from one source: K^C dims 0-63 and 64-127 [64 keys],
-// the rotated k^R from the cache page [64 keys], and V^T [128 dims][64 keys].
-// Per tile a wave computes S^T = K Q^T (so each lane owns one query's
-// scores), masks the causal triangle on diagonal tiles, runs the online
-// softmax in log2 units, and accumulates O^T += V^T P^T with the
-// probabilities straight from registers.
-// ---------------------------------------------------------------------------
-constexpr int QB = 128;
 constexpr int KREG = PS * 128;             // 8192 bytes per key region
 constexpr int KTILEB = 3 * KREG;           // K^C lo, K^C hi, rotated k^R
 constexpr int VTILEB = DC * PS * 2;        // 16384
 constexpr int STAGEB = KTILEB + VTILEB;    // 40960
 constexpr int AT_DMA = STAGEB / 1024 / 4;  // 10 one-KiB loads per wave per tile
 
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// ---------------------------------------------------------------------------
+// prefill_attn: causal attention, one workgroup per (prompt b, head h,
+// 256-query block of the chunk), one wave per SIMD; wave v owns chunk rows
+// 64v..64v+63 as two halves of 32 (A and B), so every K and V^T fragment read
+// from LDS feeds the MFMAs of both halves.
+//
+// Key tiles of 64 (one cache page) sit in a 4-deep LDS ring (all 160 KiB), two
+// tiles in flight.  A tile is four regions of 128-byte rows, each filled by
+// direct-to-LDS loads from one source: K^C dims 0-63 and 64-127 [64 keys],
+// the rotated k^R read back from the cache page [64 keys], and V^T [128
+// dims][64 keys].  Per tile a wave computes S^T = K Q^T (each lane owns one
+// query's scores), masks the causal triangle on diagonal tiles, runs the
+// online softmax in log2 units, and accumulates O^T += V^T P^T with the
+// probabilities straight from registers.
+//
+// The tiles are software-pipelined by one: step t computes the scores of tile
+// t while the VALU turns the scores of tile t - 1 into probabilities (and the
+// ten copy loads of tile t + 2 stream), then the P.V of tile t - 1 while the
+// VALU sums those probabilities and takes the row maxima of tile t.  The lazy
+// rescale for tile t follows, so the exponentials of tile t (in step t + 1)
+// use the maximum that includes it, exactly as in the one-tile order.  Score
+// buffers alternate with the parity of t; they, the probabilities, the
+// accumulators and the queries live in fixed registers (prefill_asm.h).
+// ---------------------------------------------------------------------------
+constexpr int QB = 256;
+constexpr int NRING = 4;
+
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 prefill_attn_kernel(const char* __restrict__ pool, int num_pages, const int32_t* __restrict__ table,
-                    int max_pages, const uint16_t* __restrict__ q_nope,
-                    const uint16_t* __restrict__ q_rope, const float2* __restrict__ rope_tab,
-                    const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vt,
-                    const int32_t* __restrict__ start_pos, int B, int T, int ctx, int tp, int nqb,
-                    float sc_log2, uint16_t* __restrict__ out) {
-  __shared__ __attribute__((aligned(1024))) char lds[2 * STAGEB];
+                      int max_pages, const uint16_t* __restrict__ q_nope,
+                      const uint16_t* __restrict__ q_rope, const float2* __restrict__ rope_tab,
+                      const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vt,
+                      const int32_t* __restrict__ start_pos, int B, int T, int ctx, int tp, int nqb,
+                      float sc_log2, uint16_t* __restrict__ out) {
+  __shared__ __attribute__((aligned(1024))) char lds[NRING * STAGEB];
   const int L = logical_of_launched(blockIdx.x, B * H * nqb);
   const int bh = L / nqb, qb = nqb - 1 - L % nqb;  // longest query blocks first
   const int b = bh / H, h = bh % H;
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int g = lane >> 5, n = lane & 31;
   const int P = chunk_start(start_pos, b, T, ctx);  // position of chunk row 0
-  const int q0 = qb * QB + 32 * wave;       // first chunk row of this wave
-  const int tq = q0 + n;                    // this lane's chunk row
-  const int row = min(tq, T - 1);
-  const int lim = P + row;                  // keys at positions <= lim are visible to it
-  const int lim_lo = P + min(q0, T - 1), lim_hi = P + min(q0 + 31, T - 1);
+  const int q0 = qb * QB + 64 * wave;     // first chunk row of this wave
+  int lim[2];                               // keys at positions <= lim[half] are visible
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) lim[hf] = P + min(q0 + 32 * hf + n, T - 1);
+  const int lim_lo = P + min(q0, T - 1);
+  // tiles this wave attends (none when all its rows lie past the chunk)
+  const int ntw = q0 < T ? (P + min(q0 + 63, T - 1)) / PS + 1 : 0;
+  const int ntile = (P + min(qb * QB + QB - 1, T - 1)) / PS + 1;  // the workgroup's, <= tp / PS
 
-  // ---- query fragments: B operand of S^T = K Q^T, 8 dims per lane per
-  // k-step.  Each lane builds its 96 bf16 (K^C dims in k-slot order
-  // 16s + 4g + {0..3, 8..11}, then the rotated q^R dims 16(s-8) + 8g .. +7)
-  // in LDS (which the key tiles do not use yet) and reads them back as whole
-  // 16-byte fragments.
-  bf16x8 q[12];
-  {
-    char* qs = lds + (wave * 64 + lane) * 192;  // 12 fragments of 16 bytes
+  // ---- query fragments of both halves (B operand of S^T = K Q^T: K^C dims
+  // in k-slot order 16s + 4g + {0..3, 8..11}, then the rotated q^R dims
+  // 16(s-8) + 8g .. +7), built in LDS, which the key tiles do not use yet,
+  // and read back as whole 16-byte fragments
+  bf16x8 qf[2][12];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    const int row = min(q0 + 32 * hf + n, T - 1);
+    char* qs = lds + ((wave * 64 + lane) * 2 + hf) * 192;
     const uint16_t* qc = q_nope + (((size_t)b * T + row) * H + h) * DC;
     const uint16_t* qr = q_rope + (((size_t)b * T + row) * H + h) * DR;
     const float2* cs = rope_tab + ((size_t)b * T + row) * (DR / 2) + 4 * g;
-    // every load first, so the staging costs one memory round trip
     uint2 lo[8], hi[8];
     uint4 rr[4];
     float2 cs2[16];
@@ -297,7 +343,7 @@ prefill_attn_kernel(const char* __restrict__ pool, int num_pages, const int32_t*
 #pragma unroll
     for (int s = 0; s < 8; ++s) *(uint4*)(qs + 16 * s) = make_uint4(lo[s].x, lo[s].y, hi[s].x, hi[s].y);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {  // rotated q^R dims 16s + 8g .. +7 (pairs 8s + 4g + k)
+    for (int s = 0; s < 4; ++s) {
       const uint32_t w4[4] = {rr[s].x, rr[s].y, rr[s].z, rr[s].w};
       uint32_t rot[4];
 #pragma unroll
@@ -310,44 +356,48 @@ prefill_attn_kernel(const char* __restrict__ pool, int num_pages, const int32_t*
       }
       *(uint4*)(qs + 16 * (8 + s)) = make_uint4(rot[0], rot[1], rot[2], rot[3]);
     }
-    __syncthreads();
-#pragma unroll
-    for (int s = 0; s < 12; ++s) q[s] = *(const bf16x8*)(qs + 16 * s);
-    __syncthreads();  // the key tiles may overwrite the staging area now
   }
+  __syncthreads();
+  // read straight into their AGPRs, where the MFMAs take them from
+  p64_loadq(qf[0], qf[1],
+            (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)lds) +
+                (uint32_t)((wave * 64 + lane) * 384));
+  __syncthreads();  // the key tiles may overwrite the staging area now
 
   // ---- direct-to-LDS plan: load m of wave w fills LDS unit u = (4m + w) * 64
-  // + lane (16 bytes each).  Loads 0-1 fill K^C dims 0-63, 2-3 K^C dims
-  // 64-127, 4-5 the rotated k^R rows, 6-9 the V^T rows; every region stores
-  // chunk c of row r at chunk c ^ swz8(r).  Load m covers rows 32 * (m & 1)
-  // (key regions) or 32 * (m - 6) (V^T) on from those of load 0 / 6, so a
+  // + lane (16 bytes each) of a ring slot.  Loads 0-1 fill K^C dims 0-63, 2-3
+  // K^C dims 64-127, 4-5 the rotated k^R rows, 6-9 the V^T rows; every region
+  // stores chunk c of row r at chunk c ^ swz8(r).  Load m covers rows 32 * (m
+  // & 1) (key regions) or 32 * (m - 6) (V^T) on from those of load 0 / 6, so a
   // lane keeps three 32-bit source offsets and the rest are uniform steps.
   const size_t bhs = (size_t)b * H + h;
   const char* kc_bh = (const char*)(kc + bhs * tp * DC);
   const char* vt_bh = (const char*)(vt + bhs * DC * tp);
-  const int r0 = 8 * wave + (lane >> 3);           // row of load 0 / 6 in its region
-  const int c0 = (lane & 7) ^ swz8(r0);            // source chunk (swz8(r0 + 32) == swz8(r0))
+  const int r0 = 8 * wave + (lane >> 3);
+  const int c0 = (lane & 7) ^ swz8(r0);
   const uint32_t off_kc = (uint32_t)(r0 * 256 + 16 * c0);
   const uint32_t off_pg = (uint32_t)(r0 * ROWB + 1024 + 16 * c0);
   const uint32_t off_vt = (uint32_t)(r0 * tp * 2 + 16 * c0);
   const int32_t* trow = table + (size_t)b * max_pages;
-  auto issue = [&](int kt, int page) {
-    char* buf = lds + (kt & 1) * STAGEB + wave * 1024;
+  // page ids by scalar loads (wave-uniform index; a vector load's wait would
+  // also wait for the copies in flight), each loaded one step before its use
+  auto page_of = [&](int kt) {
+    const int p = trow[__builtin_amdgcn_readfirstlane(kt)];
+    return (p >= 0 && p < num_pages) ? p : 0;  // stay in bounds on a bad table
+  };
+  auto issue = [&](int kt, int page, int slot) {
+    char* buf = lds + slot * STAGEB + wave * 1024;
     const char* kbase = kc_bh + (size_t)kt * PS * 256;
     const char* pbase = pool + (size_t)page * TILEB;
     const char* vbase = vt_bh + (size_t)kt * 128;
 #pragma unroll
     for (int m = 0; m < AT_DMA; ++m) {
-      const char* s;
-      if (m < 4) s = kbase + (m >> 1) * 128 + (m & 1) * 32 * 256 + off_kc;
-      else if (m < 6) s = pbase + (m & 1) * 32 * ROWB + off_pg;
-      else s = vbase + (size_t)(m - 6) * 32 * tp * 2 + off_vt;
-      dma16(s, buf + m * 4096);
+      const char* src;
+      if (m < 4) src = kbase + (m >> 1) * 128 + (m & 1) * 32 * 256 + off_kc;
+      else if (m < 6) src = pbase + (m & 1) * 32 * ROWB + off_pg;
+      else src = vbase + (size_t)(m - 6) * 32 * tp * 2 + off_vt;
+      dma16(src, buf + m * 4096);
     }
-  };
-  auto page_of = [&](int kt) {
-    const int p = trow[kt];
-    return (p >= 0 && p < num_pages) ? p : 0;  // stay in bounds on a bad table
   };
 
   const int x = swz8(n);
@@ -359,96 +409,150 @@ prefill_attn_kernel(const char* __restrict__ pool, int num_pages, const int32_t*
     vof[k] = (uint32_t)(KTILEB + n * 128 + 16 * ((2 * k + g) ^ x));
   }
 
-  f32x16 o[4];
-#pragma unroll
-  for (int d = 0; d < 4; ++d) o[d] = (f32x16){};
-  float m_run = -INFINITY, l_part = 0.f;
+  f32x16 o[8];  // o[4 hf + d]: value dims 32d..32d+31 of half hf
+  p64_zero_o(o);
+  f32x16 S[2][4];   // score buffers (parity of the tile)
+  u32x16 pa, pb;    // bf16 probabilities of halves A and B
+  float m_run[2] = {-INFINITY, -INFINITY}, l_part[2] = {0.f, 0.f}, nm[2] = {0.f, 0.f};
 
-  const int ntile = (P + min(qb * QB + QB - 1, T - 1)) / PS + 1;  // <= tp / PS
-  issue(0, page_of(0));
-  for (int kt = 0; kt < ntile; ++kt) {
-    const int pnext = kt + 1 < ntile ? page_of(kt + 1) : 0;
-    wait_vmcnt0();
-    raw_barrier();  // tile kt is in LDS; every wave is done with tile kt - 1
-    if (kt + 1 < ntile) issue(kt + 1, pnext);
-    if (kt * PS > lim_hi) continue;  // every key of the tile is after every query of this wave
-    const uint32_t base = lds0 + (uint32_t)(kt & 1) * STAGEB;
-    uint32_t a[4], va[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      a[k] = base + kof[k];
-      va[k] = base + vof[k];
+  // The running maximum of each half moves only when some query's tile
+  // maximum exceeds it by more than 8 (probabilities stay below 2^8); the
+  // rescale reads, multiplies and writes the accumulators as AGPRs.
+  auto rescale = [&](int hf, float mx) {
+    if (__any(mx > m_run[hf] + 8.0f)) {
+      const float m_new = fmaxf(m_run[hf], mx);
+      const float alpha = (m_run[hf] == -INFINITY) ? 0.f : exp2_fast(m_run[hf] - m_new);
+      if (hf == 0) p64_rescale_0(o, alpha);
+      else p64_rescale_1(o, alpha);
+      l_part[hf] *= alpha;
+      m_run[hf] = m_new;
     }
-    f32x16 s0, s1;
-    prefill_qk(q, a, s0, s1);
-    if (kt * PS + PS - 1 > lim_lo) {  // causal mask on the diagonal
+    nm[hf] = (m_run[hf] == -INFINITY) ? 0.f : -m_run[hf];
+  };
+
+  // per-lane source offsets of the ten loads (the plan above)
+  TileCopy cp;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = kt * PS + 8 * (i >> 2) + 4 * g + (i & 3);
-        if (key > lim) s0[i] = -INFINITY;
-        if (key + 32 > lim) s1[i] = -INFINITY;
-      }
-    }
-    float mx = fmaxf(s0[0], s1[0]);
-#pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * sc_log2;
-    // lazy rescale: the reference maximum moves only when some query's tile
-    // maximum exceeds it by more than 8 (probabilities stay below 2^8)
-    if (__any(mx > m_run + 8.0f)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = (m_run == -INFINITY) ? 0.f : exp2_fast(m_run - m_new);
-#pragma unroll
-      for (int d = 0; d < 4; ++d)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float xv = o[d][i];
-          float tmp;
-          asm volatile(
-              "v_accvgpr_read_b32 %1, %0\n\t"
-              "v_mul_f32 %1, %1, %2\n\t"
-              "v_accvgpr_write_b32 %0, %1"
-              : "+a"(xv), "=&v"(tmp)
-              : "v"(alpha));
-          o[d][i] = xv;
-        }
-      asm volatile("s_nop 7");
-      l_part *= alpha;
-      m_run = m_new;
-    }
-    const float nm = (m_run == -INFINITY) ? 0.f : -m_run;
-    bf16x8 p[4];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float p0 = exp2_fast(__builtin_fmaf(s0[e], sc_log2, nm));
-      const float p1 = exp2_fast(__builtin_fmaf(s0[8 + e], sc_log2, nm));
-      const float p2 = exp2_fast(__builtin_fmaf(s1[e], sc_log2, nm));
-      const float p3 = exp2_fast(__builtin_fmaf(s1[8 + e], sc_log2, nm));
-      l_part += (p0 + p1) + (p2 + p3);
-      p[0][e] = (__bf16)p0;
-      p[1][e] = (__bf16)p1;
-      p[2][e] = (__bf16)p2;
-      p[3][e] = (__bf16)p3;
-    }
-    prefill_pv(o, p, va);
+  for (int m = 0; m < AT_DMA; ++m) {
+    if (m < 4) cp.voff[m] = (uint32_t)((m >> 1) * 128 + (m & 1) * 32 * 256) + off_kc;
+    else if (m < 6) cp.voff[m] = (uint32_t)((m & 1) * 32 * ROWB) + off_pg;
+    else cp.voff[m] = (uint32_t)((m - 6) * 32 * tp * 2) + off_vt;
   }
+  // the copy of step t: tile t + 2 into its ring slot (the slot of tile t - 2)
+  // or, past the last tile, the last tile again into that slot, which no wave
+  // reads any more, so that every step has exactly AT_DMA loads in flight
+  auto set_copy = [&](int t, int page) {
+    const int src = min(t + 2, ntile - 1);
+    cp.lb = lds0 + (uint32_t)((t + 2) & (NRING - 1)) * STAGEB + (uint32_t)wave * 1024;
+    cp.kb = kc_bh + (size_t)src * PS * 256;
+    cp.pb = pool + (size_t)page * TILEB;
+    cp.vb = vt_bh + (size_t)src * 128;
+  };
+  auto issue_cp = [&]() {
+#pragma unroll
+    for (int m = 0; m < AT_DMA; ++m)
+      dma16((m < 4 ? cp.kb : m < 6 ? cp.pb : cp.vb) + cp.voff[m], lds + (cp.lb - lds0) + m * 4096);
+  };
+  const int pg_last = page_of(ntile - 1);
 
-  // ---- normalise and store o[b, t, h, :]
-  const float l_tot = l_part + __shfl_xor(l_part, 32);
-  if (tq < T) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    uint16_t* dst = out + (((size_t)b * T + tq) * H + h) * DC;
+  int pg_next = 0;  // page id of the tile two ahead of the next step
+  auto step = [&](auto par_c, int t) {
+    constexpr int par = decltype(par_c)::value;
+    wait_vmcnt<AT_DMA>();  // this step's tile (step t - 2's copy) is in
+    raw_barrier();         // ... for every wave; all are done with tile t - 2
+    set_copy(t, t + 2 < ntile ? pg_next : pg_last);
+    const bool act = t <= ntw && ntw > 0;
+    if (!act) {
+      issue_cp();
+      if (t + 3 < ntile) pg_next = page_of(t + 3);
+    }
+    if (t <= ntw && ntw > 0) {
+      const bool live = t < ntw;
+      const uint32_t kb = lds0 + (uint32_t)(t & (NRING - 1)) * STAGEB;
+      uint32_t a[4];
 #pragma unroll
-    for (int d = 0; d < 4; ++d)
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        ushort4 v;
-        v.x = bf16_bits_rne_f32(o[d][4 * qq + 0] * inv);
-        v.y = bf16_bits_rne_f32(o[d][4 * qq + 1] * inv);
-        v.z = bf16_bits_rne_f32(o[d][4 * qq + 2] * inv);
-        v.w = bf16_bits_rne_f32(o[d][4 * qq + 3] * inv);
-        *(ushort4*)(dst + 32 * d + 8 * qq + 4 * g) = v;
+      for (int k = 0; k < 4; ++k) a[k] = kb + kof[k];
+      if (t == 0) {
+        if constexpr (par == 0) p64_qk_cp_0(qf[0], qf[1], a, S[0], cp);
+      } else {
+        if constexpr (par == 0) p64_qk_exp_cp_0(qf[0], qf[1], a, S[0], S[1], sc_log2, nm[0], nm[1], pa, pb, cp);
+        else p64_qk_exp_cp_1(qf[0], qf[1], a, S[1], S[0], sc_log2, nm[0], nm[1], pa, pb, cp);
       }
+      if (t + 3 < ntile) pg_next = page_of(t + 3);
+      if (live && t * PS + PS - 1 > lim_lo) {  // causal mask on the diagonal
+        const int d0 = lim[0] - t * PS - 4 * g, d1 = lim[1] - t * PS - 4 * g;
+        if constexpr (par == 0) p64_mask_0(S[0], d0, d1);
+        else p64_mask_1(S[1], d0, d1);
+      }
+      float mx[2];
+      if (t == 0) {
+        if constexpr (par == 0) p64_max_0(S[0], mx[0], mx[1]);
+      } else {
+        const uint32_t vb = lds0 + (uint32_t)((t - 1) & (NRING - 1)) * STAGEB;
+        uint32_t va[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) va[k] = vb + vof[k];
+        if constexpr (par == 0) p64_pv_max_0(o, pa, pb, va, S[1], l_part[0], l_part[1], S[0], mx[0], mx[1]);
+        else p64_pv_max_1(o, pa, pb, va, S[0], l_part[0], l_part[1], S[1], mx[0], mx[1]);
+      }
+      if (t == 0) {
+        // first tile (key 0 is visible to every query): the running maximum
+        // starts at the tile's, with nothing accumulated yet to rescale
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          m_run[hf] = max_xor32(mx[hf]) * sc_log2;
+          nm[hf] = -m_run[hf];
+        }
+      } else if (live) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) rescale(hf, max_xor32(mx[hf]) * sc_log2);
+      }
+    }
+  };
+
+  // tiles 0 and 1 (tile 0 again into slot 1 for a one-tile workgroup)
+  issue(0, page_of(0), 0);
+  issue(min(1, ntile - 1), page_of(min(1, ntile - 1)), 1);
+  if (ntile > 2) pg_next = page_of(2);
+  for (int t = 0; t <= ntile; t += 2) {
+    step(std::integral_constant<int, 0>(), t);
+    if (t + 1 > ntile) break;
+    step(std::integral_constant<int, 1>(), t + 1);
+  }
+  wait_vmcnt<0>();  // the last copies land before the workgroup's LDS is released
+
+  // ---- normalise and store o[b, t, h, :] for both halves
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    const float l_tot = add_xor32(l_part[hf]);
+    const int tq = q0 + 32 * hf + n;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    uint16_t* dst = out + (((size_t)b * T + min(tq, T - 1)) * H + h) * DC;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      f32x16 r;
+      switch (4 * hf + d) {
+        case 0: p64_get_o_0(o, r); break;
+        case 1: p64_get_o_1(o, r); break;
+        case 2: p64_get_o_2(o, r); break;
+        case 3: p64_get_o_3(o, r); break;
+        case 4: p64_get_o_4(o, r); break;
+        case 5: p64_get_o_5(o, r); break;
+        case 6: p64_get_o_6(o, r); break;
+        default: p64_get_o_7(o, r); break;
+      }
+      if (tq < T) {
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          ushort4 v;
+          v.x = bf16_bits_rne_f32(r[4 * qq + 0] * inv);
+          v.y = bf16_bits_rne_f32(r[4 * qq + 1] * inv);
+          v.z = bf16_bits_rne_f32(r[4 * qq + 2] * inv);
+          v.w = bf16_bits_rne_f32(r[4 * qq + 3] * inv);
+          *(ushort4*)(dst + 32 * d + 8 * qq + 4 * g) = v;
+        }
+      }
+    }
   }
 }
 
