@@ -165,7 +165,9 @@ def _exp_ops(q, all_cvt=True):
 
 def _sum_ops(q, ks):
     """l0 / l1 += the 8 probabilities of 16-key step ks of half A / B in
-    buffer q (a pairwise tree in place: run after that key step is packed)."""
+    buffer q (a pairwise tree in place: run after that key step is packed).
+    Plain fp32 adds: a v_dot2_f32_bf16 on the packed pairs was measured to
+    slow the MFMA stream down."""
     acc_st, kk = ks // 2, ks % 2
     out = []
     for half in range(2):
@@ -268,7 +270,7 @@ def p64_qk(par, with_exp, with_copy=False):
     if with_copy:
         ins += [f'[c{m}] "v"(cp.voff[{m}])' for m in range(10)]
         ins += ['[lb] "s"(cp.lb)', '[kb] "s"(cp.kb)', '[pb] "s"(cp.pb)', '[vb] "s"(cp.vb)']
-        clob += ', "m0", "memory"'
+        clob += ', "m0", "scc", "memory"'
     name = f"p64_qk{'_exp' if with_exp else ''}{'_cp' if with_copy else ''}_{par}"
     extra = (", f32x16 (&x)[4], float sc, float nm0, float nm1, u32x16& pa, u32x16& pb"
              if with_exp else "")
@@ -427,14 +429,16 @@ __device__ __forceinline__ void p64_mask_{par}(f32x16 (&c)[4], int d0, int d1) {
 
 
 def p64_max(par):
-    """Row maxima of the scores in buffer par (the first tile)."""
-    lines = _max_ops(par)
-    ins = [f'"{_pin(par, acc)}"(c[{acc}])' for acc in range(4)]
-    return f"""// m0 / m1 = maxima of the scores of halves A / B in buffer {par}.
-__device__ __forceinline__ void p64_max_{par}(const f32x16 (&c)[4], float& m0, float& m1) {{
+    """Row maxima of the scores in buffer par (the first tile), over both lanes
+    of a query, times sc."""
+    lines = _max_ops(par) + _xlane_ops()
+    ins = [f'"{_pin(par, acc)}"(c[{acc}])' for acc in range(4)] + ['[sc] "v"(sc)']
+    return f"""// m0 / m1 = maxima of the scores of halves A / B in buffer {par}, times sc.
+__device__ __forceinline__ void p64_max_{par}(const f32x16 (&c)[4], float sc, float& m0, float& m1) {{
+  float t0, t1;
   asm volatile(
 {_emit64(lines)}
-      : [m0] "=&v"(m0), [m1] "=&v"(m1)
+      : [m0] "=&v"(m0), [m1] "=&v"(m1), [t0] "=&v"(t0), [t1] "=&v"(t1)
       : {", ".join(ins)});
 }}
 """
@@ -467,6 +471,131 @@ __device__ __forceinline__ void p64_get_o_{j}(const f32x16 (&o)[8], f32x16& r) {
 """
 
 
+def _xlane_ops():
+    """m0 / m1 = max over lanes l and l ^ 32 (the two halves of a query's keys),
+    times sc.  v_permlane32_swap exchanges the upper 32 lanes of its first
+    operand with the lower 32 of its second, so after swapping a copy both
+    hold the partner's value in one half and the own in the other."""
+    ops = []
+    for h in range(2):
+        ops += [f"v_mov_b32 %[t{h}], %[m{h}]", "s_nop 1", f"v_permlane32_swap_b32 %[m{h}], %[t{h}]",
+                f"v_max_f32 %[m{h}], %[m{h}], %[t{h}]", f"v_mul_f32 %[m{h}], %[m{h}], %[sc]"]
+    return ops
+
+
+def _mask_ops(par):
+    """Causal mask of the scores in buffer par (see p64_mask)."""
+    ops = []
+    for half in range(2):
+        for st in range(2):
+            for e in range(16):
+                off = 8 * (e // 4) + (e % 4) + 32 * st
+                x = _sel(par, 2 * half + st, e)
+                ops.append(f"v_cmp_gt_i32 vcc, {off}, %[d{half}]")
+                ops.append(f"v_cndmask_b32 {x}, {x}, %[ninf], vcc")
+    return ops
+
+
+def p64_step(par):
+    """One pipelined step (t >= 1) as a single stream of 80 MFMAs: the scores
+    of tile t for both halves (48), then the P.V of tile t - 1 (32), with the
+    K and V^T reads running AH64 ahead across the two parts.  The VALU, in the
+    score part: the probabilities of tile t - 1 (buffer 1 - par) and the bf16
+    packing of their key step 0; the ten copy loads of tile t + 2 ride along.
+    In the P.V part: the packing of key steps 1..3 just ahead of their MFMAs,
+    the sums of the probabilities, and - from the fifth P.V MFMA on, when the
+    score MFMAs' results are long written - the row maxima of tile t, after
+    the causal mask when dg != 0 (a group the block branches over otherwise;
+    only diagonal tiles need it)."""
+    q = 1 - par
+    nq, npv = 2 * QK_STEPS, 16          # reads of each part (two MFMAs each)
+    lines = ["s_waitcnt lgkmcnt(0)"]
+
+    def read(r):
+        if r < nq:
+            s_, st = r // 2, r % 2
+            return f"ds_read_b128 {_scr(r)}, %[a{s_ & 3}] offset:{(s_ >> 2) * KREG + st * 32 * 128}"
+        i = r - nq
+        ks, dt = i // 4, i % 4
+        return f"ds_read_b128 {_scr(r)}, %[v{ks}] offset:{dt * 32 * VROWB}"
+
+    nr = nq + npv
+    for r in range(min(AH64, nr)):
+        lines.append(read(r))
+    per = [[] for _ in range(2 * nr)]
+    # score part
+    sp = _spread(2 * nq, _exp_ops(q, all_cvt=False))
+    for j in range(2 * nq):
+        per[j] += sp[j]
+    for m, ops in enumerate(_copy_ops()):
+        per[1 + 4 * m] = ops + per[1 + 4 * m]
+    # P.V part
+    base = 2 * nq
+    for ks in range(4):
+        ops = _sum_ops(q, ks)
+        if ks < 3:
+            cv = _cvt_ops(q, ks + 1)
+            ops = [o for pair in zip(cv, ops[:len(cv)]) for o in pair] + ops[len(cv):]
+        sp = _spread(6, ops)
+        for j in range(6):
+            per[base + 8 * ks + j] += sp[j]
+    sp = _spread(2 * npv - 4, _max_ops(par))
+    for j in range(2 * npv - 4):
+        per[base + 4 + j] += sp[j]
+    per[base + 4] = (["s_cmp_eq_u32 %[dg], 0", "s_cbranch_scc1 7f"] + _mask_ops(par) + ["7:"]
+                     + per[base + 4])
+    k = 0
+    for r in range(nr):
+        lines.append(f"s_waitcnt lgkmcnt({min(AH64 - 1, nr - 1 - r)})")
+        for half in range(2):
+            if r < nq:
+                s_, st = r // 2, r % 2
+                acc = 2 * half + st
+                src_c = "0" if s_ == 0 else _sacc(par, acc)
+                lines.append(f"v_mfma_f32_32x32x16_bf16 {_sacc(par, acc)}, {_scr(r)}, {_qreg(half, s_)}, {src_c}")
+            else:
+                i = r - nq
+                ks, dt = i // 4, i % 4
+                o = _oreg(4 * half + dt)
+                lines.append(f"v_mfma_f32_32x32x16_bf16 {o}, {_scr(r)}, {_pfrag(half, ks)}, {o}")
+            lines += per[k]
+            k += 1
+        if r + AH64 < nr:
+            lines.append(read(r + AH64))
+    lines += _xlane_ops()
+    outs = [f'"=&{_pin(par, acc)}"(c[{acc}])' for acc in range(4)]
+    outs += [f'"+{_pin(q, acc)}"(x[{acc}])' for acc in range(4)]
+    outs += [f'"+{{{_oreg(d)}}}"(o[{d}])' for d in range(8)]
+    outs += ['[l0] "+v"(l0)', '[l1] "+v"(l1)', '[m0] "=&v"(m0)', '[m1] "=&v"(m1)',
+             '[t0] "=&v"(t0)', '[t1] "=&v"(t1)']
+    ins = [f'"{{{_qreg(h, s_)}}}"(q{h}[{s_}])' for h in range(2) for s_ in range(QK_STEPS)]
+    ins += [f'[a{k}] "v"(a[{k}])' for k in range(4)] + [f'[v{k}] "v"(v[{k}])' for k in range(4)]
+    ins += ['[sc] "v"(sc)', '[nm0] "v"(nm0)', '[nm1] "v"(nm1)']
+    ins += [f'[c{m}] "v"(cp.voff[{m}])' for m in range(10)]
+    ins += ['[lb] "s"(cp.lb)', '[kb] "s"(cp.kb)', '[pb] "s"(cp.pb)', '[vb] "s"(cp.vb)']
+    ins += ['[dg] "s"(dg)', '[d0] "v"(d0)', '[d1] "v"(d1)', '[ninf] "v"(ninf)']
+    clob = (SCR64 + ", " + ", ".join(f'"v{r}"' for r in range(96, 128)) +
+            ', "m0", "scc", "vcc", "memory"')
+    return f"""// One pipelined step t >= 1 (see gen_prefill_asm.py): scores of tile t into
+// buffer {par} (c), probabilities of tile t - 1 from buffer {q} (x, consumed),
+// o += their P.V, l0 / l1 += their sums, m0 / m1 = row maxima of tile t (after
+// the causal mask with d0 / d1 as in p64_mask when dg != 0) over both lanes
+// of a query, times sc.
+__device__ __forceinline__ void p64_step_{par}(const bf16x8 (&q0)[{QK_STEPS}], const bf16x8 (&q1)[{QK_STEPS}],
+                                       const uint32_t (&a)[4], const uint32_t (&v)[4], f32x16 (&c)[4],
+                                       f32x16 (&x)[4], f32x16 (&o)[8], float sc, float nm0, float nm1,
+                                       float& l0, float& l1, float& m0, float& m1,
+                                       const TileCopy& cp, int dg, int d0, int d1) {{
+  const float ninf = -__builtin_inff();
+  float t0, t1;
+  asm volatile(
+{_emit64(lines)}
+      : {", ".join(outs)}
+      : {", ".join(ins)}
+      : {clob});
+}}
+"""
+
 def main():
     print("// Generated by gen_prefill_asm.py -- do not edit by hand.")
     print("// Inline-assembly blocks of the prefill kernels (see that script).")
@@ -487,11 +616,10 @@ def main():
     print(p64_rescale(0))
     print(p64_rescale(1))
     print(p64_qk(0, False, True))  # the first tile (no previous scores)
+    print(p64_mask(0))
     print(p64_max(0))
     for par in range(2):
-        print(p64_qk(par, True, True))
-        print(p64_pv(par, True))
-        print(p64_mask(par))
+        print(p64_step(par))
     print("#pragma clang diagnostic pop")
 
 

@@ -77,11 +77,7 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N <= 15, "vmcnt range");
   __builtin_amdgcn_s_waitcnt(N | (7 << 4) | (15 << 8));
 }
-// max(x, the same value in lane l ^ 32)
-__device__ __forceinline__ float max_xor32(float x) {
-  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-}
+// x + the same value in lane l ^ 32
 __device__ __forceinline__ float add_xor32(float x) {
   const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
@@ -381,10 +377,9 @@ prefill_attn_kernel(const char* __restrict__ pool, int num_pages, const int32_t*
   const int32_t* trow = table + (size_t)b * max_pages;
   // page ids by scalar loads (wave-uniform index; a vector load's wait would
   // also wait for the copies in flight), each loaded one step before its use
-  auto page_of = [&](int kt) {
-    const int p = trow[__builtin_amdgcn_readfirstlane(kt)];
-    return (p >= 0 && p < num_pages) ? p : 0;  // stay in bounds on a bad table
-  };
+  auto page_raw = [&](int kt) { return trow[__builtin_amdgcn_readfirstlane(kt)]; };
+  auto page_ok = [&](int p) { return (p >= 0 && p < num_pages) ? p : 0; };  // in bounds on a bad table
+  auto page_of = [&](int kt) { return page_ok(page_raw(kt)); };
   auto issue = [&](int kt, int page, int slot) {
     char* buf = lds + slot * STAGEB + wave * 1024;
     const char* kbase = kc_bh + (size_t)kt * PS * 256;
@@ -455,16 +450,16 @@ prefill_attn_kernel(const char* __restrict__ pool, int num_pages, const int32_t*
   };
   const int pg_last = page_of(ntile - 1);
 
-  int pg_next = 0;  // page id of the tile two ahead of the next step
+  int pg_next = 0;  // page id (unchecked: read a step before its use) of the tile two ahead of the next step
   auto step = [&](auto par_c, int t) {
     constexpr int par = decltype(par_c)::value;
     wait_vmcnt<AT_DMA>();  // this step's tile (step t - 2's copy) is in
     raw_barrier();         // ... for every wave; all are done with tile t - 2
-    set_copy(t, t + 2 < ntile ? pg_next : pg_last);
+    set_copy(t, t + 2 < ntile ? page_ok(pg_next) : pg_last);
     const bool act = t <= ntw && ntw > 0;
     if (!act) {
       issue_cp();
-      if (t + 3 < ntile) pg_next = page_of(t + 3);
+      if (t + 3 < ntile) pg_next = page_raw(t + 3);
     }
     if (t <= ntw && ntw > 0) {
       const bool live = t < ntw;
@@ -472,40 +467,41 @@ prefill_attn_kernel(const char* __restrict__ pool, int num_pages, const int32_t*
       uint32_t a[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) a[k] = kb + kof[k];
-      if (t == 0) {
-        if constexpr (par == 0) p64_qk_cp_0(qf[0], qf[1], a, S[0], cp);
-      } else {
-        if constexpr (par == 0) p64_qk_exp_cp_0(qf[0], qf[1], a, S[0], S[1], sc_log2, nm[0], nm[1], pa, pb, cp);
-        else p64_qk_exp_cp_1(qf[0], qf[1], a, S[1], S[0], sc_log2, nm[0], nm[1], pa, pb, cp);
-      }
-      if (t + 3 < ntile) pg_next = page_of(t + 3);
-      if (live && t * PS + PS - 1 > lim_lo) {  // causal mask on the diagonal
-        const int d0 = lim[0] - t * PS - 4 * g, d1 = lim[1] - t * PS - 4 * g;
-        if constexpr (par == 0) p64_mask_0(S[0], d0, d1);
-        else p64_mask_1(S[1], d0, d1);
-      }
       float mx[2];
       if (t == 0) {
-        if constexpr (par == 0) p64_max_0(S[0], mx[0], mx[1]);
+        // scores of tile 0 (with the copies of tile 2), then their maxima
+        if constexpr (par == 0) {
+          p64_qk_cp_0(qf[0], qf[1], a, S[0], cp);
+          if (lim_lo < PS - 1) p64_mask_0(S[0], lim[0] - 4 * g, lim[1] - 4 * g);
+          p64_max_0(S[0], sc_log2, mx[0], mx[1]);
+        }
       } else {
         const uint32_t vb = lds0 + (uint32_t)((t - 1) & (NRING - 1)) * STAGEB;
         uint32_t va[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) va[k] = vb + vof[k];
-        if constexpr (par == 0) p64_pv_max_0(o, pa, pb, va, S[1], l_part[0], l_part[1], S[0], mx[0], mx[1]);
-        else p64_pv_max_1(o, pa, pb, va, S[0], l_part[0], l_part[1], S[1], mx[0], mx[1]);
+        const int d0 = lim[0] - t * PS - 4 * g, d1 = lim[1] - t * PS - 4 * g;
+        // causal mask on the diagonal (wave-uniform: lim_lo is the wave's first row)
+        const int dg = __builtin_amdgcn_readfirstlane((int)(live && t * PS + PS - 1 > lim_lo));
+        if constexpr (par == 0)
+          p64_step_0(qf[0], qf[1], a, va, S[0], S[1], o, sc_log2, nm[0], nm[1], l_part[0], l_part[1],
+                     mx[0], mx[1], cp, dg, d0, d1);
+        else
+          p64_step_1(qf[0], qf[1], a, va, S[1], S[0], o, sc_log2, nm[0], nm[1], l_part[0], l_part[1],
+                     mx[0], mx[1], cp, dg, d0, d1);
       }
+      if (t + 3 < ntile) pg_next = page_raw(t + 3);
       if (t == 0) {
         // first tile (key 0 is visible to every query): the running maximum
         // starts at the tile's, with nothing accumulated yet to rescale
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
-          m_run[hf] = max_xor32(mx[hf]) * sc_log2;
+          m_run[hf] = mx[hf];
           nm[hf] = -m_run[hf];
         }
       } else if (live) {
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) rescale(hf, max_xor32(mx[hf]) * sc_log2);
+        for (int hf = 0; hf < 2; ++hf) rescale(hf, mx[hf]);
       }
     }
   };
@@ -513,7 +509,7 @@ prefill_attn_kernel(const char* __restrict__ pool, int num_pages, const int32_t*
   // tiles 0 and 1 (tile 0 again into slot 1 for a one-tile workgroup)
   issue(0, page_of(0), 0);
   issue(min(1, ntile - 1), page_of(min(1, ntile - 1)), 1);
-  if (ntile > 2) pg_next = page_of(2);
+  if (ntile > 2) pg_next = page_raw(2);
   for (int t = 0; t <= ntile; t += 2) {
     step(std::integral_constant<int, 0>(), t);
     if (t + 1 > ntile) break;
