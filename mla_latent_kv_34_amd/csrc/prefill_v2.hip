@@ -322,22 +322,36 @@ prefill_attn_kernel(const char* __restrict__ pool, int num_pages, const int32_t*
     const uint16_t* qc = q_nope + (((size_t)b * T + row) * H + h) * DC;
     const uint16_t* qr = q_rope + (((size_t)b * T + row) * H + h) * DR;
     const float2* cs = rope_tab + ((size_t)b * T + row) * (DR / 2) + 4 * g;
-    uint2 lo[8], hi[8];
-    uint4 rr[4];
-    float2 cs2[16];
+    // 16-byte loads only (fewer, wider requests): lane g takes K^C dims
+    // 16s + 8g .. +7 and trades four of them with its partner lane (l ^ 32),
+    // so that g = 0 holds 16s + {0..3, 8..11} and g = 1 holds 16s + {4..7, 12..15}
+    uint4 cv[8], rr[4];
+    float4 cs4[8];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      lo[s] = *(const uint2*)(qc + 16 * s + 4 * g);
-      hi[s] = *(const uint2*)(qc + 16 * s + 4 * g + 8);
-    }
+    for (int s = 0; s < 8; ++s) cv[s] = *(const uint4*)(qc + 16 * s + 8 * g);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       rr[s] = *(const uint4*)(qr + 16 * s + 8 * g);
+      cs4[2 * s] = *(const float4*)(cs + 8 * s);
+      cs4[2 * s + 1] = *(const float4*)(cs + 8 * s + 2);
+    }
+    float2 cs2[16];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) cs2[4 * s + k] = cs[8 * s + k];
+    for (int s = 0; s < 4; ++s) {
+      cs2[4 * s] = make_float2(cs4[2 * s].x, cs4[2 * s].y);
+      cs2[4 * s + 1] = make_float2(cs4[2 * s].z, cs4[2 * s].w);
+      cs2[4 * s + 2] = make_float2(cs4[2 * s + 1].x, cs4[2 * s + 1].y);
+      cs2[4 * s + 3] = make_float2(cs4[2 * s + 1].z, cs4[2 * s + 1].w);
     }
 #pragma unroll
-    for (int s = 0; s < 8; ++s) *(uint4*)(qs + 16 * s) = make_uint4(lo[s].x, lo[s].y, hi[s].x, hi[s].y);
+    for (int s = 0; s < 8; ++s) {
+      // g = 0 sends dims 4..7 and receives 8..11; g = 1 sends 8..11 and receives 4..7
+      const uint32_t s0 = g ? cv[s].x : cv[s].z, s1 = g ? cv[s].y : cv[s].w;
+      const auto w0 = __builtin_amdgcn_permlane32_swap(s0, s0, false, false);
+      const auto w1 = __builtin_amdgcn_permlane32_swap(s1, s1, false, false);
+      const uint32_t r0 = g ? w0[0] : w0[1], r1 = g ? w1[0] : w1[1];  // the partner's value
+      *(uint4*)(qs + 16 * s) = g ? make_uint4(r0, r1, cv[s].z, cv[s].w) : make_uint4(cv[s].x, cv[s].y, r0, r1);
+    }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const uint32_t w4[4] = {rr[s].x, rr[s].y, rr[s].z, rr[s].w};
