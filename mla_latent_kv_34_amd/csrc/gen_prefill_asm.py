@@ -363,16 +363,17 @@ def p64_loadq():
     lines = []
     for half in range(2):
         for st in range(QK_STEPS):
-            lines.append(f"ds_read_b128 {_qreg(half, st)}, %[p] offset:{192 * half + 16 * st}")
+            lines.append(f"ds_read_b128 {_qreg(half, st)}, %[p{half}] offset:{4096 * st}")
     lines.append("s_waitcnt lgkmcnt(0)")
     outs = [f'"={{{_qreg(h, s)}}}"(q{h}[{s}])' for h in range(2) for s in range(QK_STEPS)]
     return f"""// q0 / q1 = the 12 query fragments of halves A / B, read from LDS at byte
-// address p (192 bytes per half), complete on return.
-__device__ __forceinline__ void p64_loadq(bf16x8 (&q0)[{QK_STEPS}], bf16x8 (&q1)[{QK_STEPS}], uint32_t p) {{
+// addresses p0 / p1 + 4096 s (s = 0..11), complete on return.
+__device__ __forceinline__ void p64_loadq(bf16x8 (&q0)[{QK_STEPS}], bf16x8 (&q1)[{QK_STEPS}], uint32_t p0,
+                                         uint32_t p1) {{
   asm volatile(
 {_emit64(lines)}
       : {", ".join(outs)}
-      : [p] "v"(p));
+      : [p0] "v"(p0), [p1] "v"(p1));
 }}
 """
 

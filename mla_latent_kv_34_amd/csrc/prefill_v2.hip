@@ -318,7 +318,9 @@ prefill_attn_kernel(const char* __restrict__ pool, int num_pages, const int32_t*
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
     const int row = min(q0 + 32 * hf + n, T - 1);
-    char* qs = lds + ((wave * 64 + lane) * 2 + hf) * 192;
+    // fragment s of this lane at qs + 4096 s: the 64 lanes of a wave write
+    // (and read back) one contiguous KiB per fragment, free of bank conflicts
+    char* qs = lds + (hf * 12 * 256 + wave * 64 + lane) * 16;
     const uint16_t* qc = q_nope + (((size_t)b * T + row) * H + h) * DC;
     const uint16_t* qr = q_rope + (((size_t)b * T + row) * H + h) * DR;
     const float2* cs = rope_tab + ((size_t)b * T + row) * (DR / 2) + 4 * g;
@@ -350,7 +352,7 @@ prefill_attn_kernel(const char* __restrict__ pool, int num_pages, const int32_t*
       const auto w0 = __builtin_amdgcn_permlane32_swap(s0, s0, false, false);
       const auto w1 = __builtin_amdgcn_permlane32_swap(s1, s1, false, false);
       const uint32_t r0 = g ? w0[0] : w0[1], r1 = g ? w1[0] : w1[1];  // the partner's value
-      *(uint4*)(qs + 16 * s) = g ? make_uint4(r0, r1, cv[s].z, cv[s].w) : make_uint4(cv[s].x, cv[s].y, r0, r1);
+      *(uint4*)(qs + 4096 * s) = g ? make_uint4(r0, r1, cv[s].z, cv[s].w) : make_uint4(cv[s].x, cv[s].y, r0, r1);
     }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -364,14 +366,16 @@ prefill_attn_kernel(const char* __restrict__ pool, int num_pages, const int32_t*
         rot[k] = (uint32_t)bf16_bits_rne_f32(a * c.x - bb * c.y) |
                  ((uint32_t)bf16_bits_rne_f32(a * c.y + bb * c.x) << 16);
       }
-      *(uint4*)(qs + 16 * (8 + s)) = make_uint4(rot[0], rot[1], rot[2], rot[3]);
+      *(uint4*)(qs + 4096 * (8 + s)) = make_uint4(rot[0], rot[1], rot[2], rot[3]);
     }
   }
   __syncthreads();
   // read straight into their AGPRs, where the MFMAs take them from
-  p64_loadq(qf[0], qf[1],
-            (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)lds) +
-                (uint32_t)((wave * 64 + lane) * 384));
+  {
+    const uint32_t p0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)lds) +
+                        (uint32_t)((wave * 64 + lane) * 16);
+    p64_loadq(qf[0], qf[1], p0, p0 + 12 * 4096);
+  }
   __syncthreads();  // the key tiles may overwrite the staging area now
 
   // ---- direct-to-LDS plan: load m of wave w fills LDS unit u = (4m + w) * 64
