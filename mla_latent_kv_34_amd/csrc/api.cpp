@@ -24,6 +24,9 @@ mla_status fail(mla_status s, const std::string& msg) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
+}  // namespace
+
+namespace mla {
 // Compute units of the current device (cached per device id).
 int device_cus(int* out) {
   static std::mutex mu;
@@ -40,6 +43,9 @@ int device_cus(int* out) {
   *out = cache[dev];
   return 0;
 }
+}  // namespace mla
+
+namespace {
 
 enum class Family { V2, Generic };
 
@@ -111,7 +117,7 @@ int resolve_wg(int n_workgroups, int* out) {
     *out = n_workgroups;
     return 0;
   }
-  return device_cus(out);
+  return mla::device_cus(out);
 }
 
 }  // namespace

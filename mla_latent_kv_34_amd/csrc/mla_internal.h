@@ -203,6 +203,9 @@ hipError_t launch_v2_prefill(const Layer& L, const void* pool, int num_pages, co
                              const void* w_uk, const void* w_uv, void* out, void* ws,
                              void* const* ev, hipStream_t s);
 
+// Compute units of the current device in *out (api.cpp); 0 on success, -1 on error.
+int device_cus(int* out);
+
 // Record timing event ev[i] (a hipEvent_t) on s when ev is non-null.
 static inline hipError_t mark(void* const* ev, int i, hipStream_t s) {
   return ev ? hipEventRecord((hipEvent_t)ev[i], s) : hipSuccess;

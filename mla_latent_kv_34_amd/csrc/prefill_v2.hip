@@ -25,6 +25,7 @@
 //   V^T   [b][h][128][Tp] bf16, keys in the same order within 16-key groups,
 //         so one 16-byte LDS read gives a lane the 8 keys its probabilities
 //         cover; rows past P_b + T hold zeros.
+#include <algorithm>
 #include <type_traits>
 
 #include "mla_internal.h"
@@ -91,13 +92,6 @@ __device__ __forceinline__ float agpr_read(float a) {
   return v;
 }
 
-// Launched workgroup ib runs on XCD ib % 8; give every XCD a contiguous range
-// of logical indices so neighbouring work shares that XCD's L2.
-__device__ __forceinline__ int logical_of_launched(int ib, int n) {
-  const int x = ib & 7, k = ib >> 3, q8 = n >> 3, r8 = n & 7;
-  return x * q8 + min(x, r8) + k;
-}
-
 __device__ __forceinline__ void dma16(const void* src, char* lds_block) {
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_block, 16,
                                    0, 0);
@@ -112,11 +106,13 @@ __device__ __forceinline__ int chunk_start(const int32_t* start_pos, int b, int 
 // ---------------------------------------------------------------------------
 // rope_table: tab[b][t][k] = (cos, sin) of (P_b + t) * base^(-2k/64),
 // computed in fp64 and stored in fp32 (the rotated query is rounded to bf16
-// afterwards).
+// afterwards).  It also clears the eight work counters of prefill_attn, which
+// runs later on the same stream.
 // ---------------------------------------------------------------------------
 __global__ void rope_table_kernel(int B, int T, const int32_t* __restrict__ start_pos, int ctx,
-                                  double base, float2* __restrict__ tab) {
+                                  double base, float2* __restrict__ tab, int* __restrict__ queue) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < 8) queue[i] = 0;
   if (i >= B * T * (DR / 2)) return;
   const int bt = i / (DR / 2), k = i % (DR / 2);
   const int b = bt / T, t = bt % T;
@@ -286,17 +282,21 @@ constexpr int AT_DMA = STAGEB / 1024 / 4;  // 10 one-KiB loads per wave per tile
 // ---------------------------------------------------------------------------
 constexpr int QB = 256;
 constexpr int NRING = 4;
+constexpr int TAIL_HEADS = 4;  // see prefill_attn_kernel
 
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-prefill_attn_kernel(const char* __restrict__ pool, int num_pages, const int32_t* __restrict__ table,
-                      int max_pages, const uint16_t* __restrict__ q_nope,
-                      const uint16_t* __restrict__ q_rope, const float2* __restrict__ rope_tab,
-                      const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vt,
-                      const int32_t* __restrict__ start_pos, int B, int T, int ctx, int tp, int nqb,
-                      float sc_log2, uint16_t* __restrict__ out) {
-  __shared__ __attribute__((aligned(1024))) char lds[NRING * STAGEB];
-  const int L = logical_of_launched(blockIdx.x, B * H * nqb);
-  const int bh = L / nqb, qb = nqb - 1 - L % nqb;  // longest query blocks first
+// One work item: logical index L = (b H + h) nqb + (nqb - 1 - query block),
+// so each head's blocks come longest first.
+__device__ __forceinline__ void attn_item(const char* __restrict__ pool, int num_pages,
+                                          const int32_t* __restrict__ table, int max_pages,
+                                          const uint16_t* __restrict__ q_nope,
+                                          const uint16_t* __restrict__ q_rope,
+                                          const float2* __restrict__ rope_tab,
+                                          const uint16_t* __restrict__ kc,
+                                          const uint16_t* __restrict__ vt,
+                                          const int32_t* __restrict__ start_pos, int T, int ctx,
+                                          int tp, int nqb, float sc_log2, uint16_t* __restrict__ out,
+                                          int L, char* lds) {
+  const int bh = L / nqb, qb = nqb - 1 - L % nqb;
   const int b = bh / H, h = bh % H;
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int g = lane >> 5, n = lane & 31;
@@ -570,15 +570,60 @@ prefill_attn_kernel(const char* __restrict__ pool, int num_pages, const int32_t*
   }
 }
 
+// Persistent: at most one workgroup per CU (the ring takes all of a CU's
+// LDS).  A CU is never left waiting for a launch: the dispatcher hands an
+// XCD's workgroups to its shader engines in turn, whichever has a free CU, so
+// with blocks of unequal length one workgroup per block leaves CUs idle.  The
+// workgroups on XCD x (launched index % 8) take the items of that XCD's
+// contiguous logical range in order from counter x, so the blocks of a head
+// run side by side and share its K/V tiles in that XCD's L2.
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+prefill_attn_kernel(const char* __restrict__ pool, int num_pages, const int32_t* __restrict__ table,
+                      int max_pages, const uint16_t* __restrict__ q_nope,
+                      const uint16_t* __restrict__ q_rope, const float2* __restrict__ rope_tab,
+                      const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vt,
+                      const int32_t* __restrict__ start_pos, int B, int T, int ctx, int tp, int nqb,
+                      float sc_log2, int* __restrict__ queue, uint16_t* __restrict__ out) {
+  __shared__ __attribute__((aligned(1024))) char lds[NRING * STAGEB];
+  const int n = B * H * nqb, xc = blockIdx.x & 7;
+  const int first = xc * (n >> 3) + min(xc, n & 7), count = (n >> 3) + (xc < (n & 7));
+  // The last TAIL_HEADS heads' worth of the range go longest first across
+  // heads, so the range ends on short blocks: item p of the tail [s, e) is
+  // the p-th in the order (descending query block, ascending index).
+  const int tail = min(count, TAIL_HEADS * nqb), s0 = first + count - tail, e0 = first + count;
+  auto item_of = [&](int k) {
+    if (k < count - tail) return first + k;
+    int p = k - (count - tail);
+    for (int r = 0; r < nqb - 1; ++r) {  // r = nqb - 1 - query block
+      const int l0 = s0 + (r - s0 % nqb + nqb) % nqb;  // first index >= s0 with index % nqb == r
+      const int c = l0 < e0 ? (e0 - 1 - l0) / nqb + 1 : 0;
+      if (p < c) return l0 + p * nqb;
+      p -= c;
+    }
+    return s0 + (nqb - 1 - s0 % nqb + nqb) % nqb + p * nqb;  // query block 0
+  };
+  volatile int* const bcast = (volatile int*)(lds + NRING * STAGEB - 4);
+  for (;;) {
+    raw_barrier();  // every wave is done with the ring (its copies landed)
+    if (threadIdx.x == 0) *bcast = atomicAdd(queue + xc, 1);
+    __syncthreads();
+    const int k = __builtin_amdgcn_readfirstlane(*bcast);
+    if (k >= count) break;
+    attn_item(pool, num_pages, table, max_pages, q_nope, q_rope, rope_tab, kc, vt, start_pos, T,
+              ctx, tp, nqb, sc_log2, out, item_of(k), lds);
+  }
+}
+
 struct PfLayout {
-  size_t rope, kc, vt, total;
+  size_t rope, kc, vt, queue, total;
   int tp;
   PfLayout(int B, int T, int ctx) {
     tp = (ctx + PS - 1) / PS * PS;
     rope = 0;
     kc = align256(rope + (size_t)B * T * (DR / 2) * sizeof(float2));
     vt = align256(kc + (size_t)B * H * tp * DC * 2);
-    total = align256(vt + (size_t)B * H * DC * tp * 2);
+    queue = align256(vt + (size_t)B * H * DC * tp * 2);
+    total = queue + 256;
   }
 };
 
@@ -660,18 +705,23 @@ hipError_t launch_v2_prefill(const Layer& L, const void* pool, int num_pages, co
   uint16_t* vt = (uint16_t*)(w + lay.vt);
   hipError_t e = mark(ev, 0, s);
   if (e != hipSuccess) return e;
+  int* queue = (int*)(w + lay.queue);
   hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((B * T * (DR / 2) + 255) / 256)),
-                     dim3(256), 0, s, B, T, start_pos, ctx, L.rope_base, tab);
+                     dim3(256), 0, s, B, T, start_pos, ctx, L.rope_base, tab, queue);
   const int nt = (ctx + EX_TOK - 1) / EX_TOK;
   hipLaunchKernelGGL(expand_kernel, dim3((unsigned)(H * B * nt)), dim3(64 * EX_NW), 0, s,
                      (const char*)pool, num_pages, table, max_pages, start_pos,
                      (const uint16_t*)w_uk, (const uint16_t*)w_uv, B, T, ctx, lay.tp, nt, kc, vt);
   const int nqb = (T + QB - 1) / QB;
   const float sc_log2 = L.scale * 1.4426950408889634f;
-  hipLaunchKernelGGL(prefill_attn_kernel, dim3((unsigned)(B * H * nqb)), dim3(256), 0, s,
+  // one workgroup per CU, at least one per XCD that has items
+  int cus = 0;
+  if (device_cus(&cus) != 0) return hipErrorInvalidDevice;
+  const int n_item = B * H * nqb, grid = std::min(n_item, std::max(cus, 8));
+  hipLaunchKernelGGL(prefill_attn_kernel, dim3((unsigned)grid), dim3(256), 0, s,
                      (const char*)pool, num_pages, table, max_pages, (const uint16_t*)q_nope,
                      (const uint16_t*)q_rope, (const float2*)tab, (const uint16_t*)kc,
-                     (const uint16_t*)vt, start_pos, B, T, ctx, lay.tp, nqb, sc_log2,
+                     (const uint16_t*)vt, start_pos, B, T, ctx, lay.tp, nqb, sc_log2, queue,
                      (uint16_t*)out);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
