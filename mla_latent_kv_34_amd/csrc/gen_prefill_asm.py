@@ -15,11 +15,13 @@ VROWB = 128        # bytes per V^T row in LDS (64 keys)
 XDL_TO_VALU_NOPS = ["s_nop 7", "s_nop 7", "s_nop 7"]
 
 
-def expand_block(vhalf):
+def expand_block(vhalf, first=False):
     """One 64-column stage of the K^C / V^T expansion GEMM for one wave:
     4 k-steps x (2 token blocks x 4 output-dim blocks).  Fragments of k-step
-    ks + 1 are read while the MFMAs of k-step ks run (two register sets)."""
-    name = "expand_stage_v" if vhalf else "expand_stage_k"
+    ks + 1 are read while the MFMAs of k-step ks run (two register sets).
+    The first stage's variant starts the accumulators from zero (its first
+    MFMAs take the constant 0 as their addend)."""
+    name = ("expand_stage_v" if vhalf else "expand_stage_k") + ("_first" if first else "")
 
     def regs(ks):
         base = 6 * (ks & 1)
@@ -41,16 +43,18 @@ def expand_block(vhalf):
             for j in range(4):
                 a, b = (r[i], r[2 + j]) if vhalf else (r[2 + j], r[i])
                 acc = f"%[o{4 * i + j}]"
-                lines.append(f"v_mfma_f32_32x32x16_bf16 {acc}, {a}, {b}, {acc}")
+                addend = "0" if (first and ks == 0) else acc
+                lines.append(f"v_mfma_f32_32x32x16_bf16 {acc}, {a}, {b}, {addend}")
     lines += XDL_TO_VALU_NOPS
     body = "\n".join(f'      "{l}\\n\\t"' for l in lines)
-    outs = ", ".join([f'[o{k}] "+a"(o[{k}])' for k in range(8)] +
+    outs = ", ".join([f'[o{k}] "{"=a" if first else "+a"}"(o[{k}])' for k in range(8)] +
                      [f'[t{k}] "=&v"(t{k})' for k in range(12)])
     ins = ", ".join([f'[c{k}] "v"(c[{k}])' for k in range(4)] +
                     [f'[w{k}] "v"(w[{k}])' for k in range(4)])
     temps = "\n".join(f"  u32x4 t{k};" for k in range(12))
     what = ("V (token rows, value-dim columns): o[4i+j] += C_i W_j^T" if vhalf else
             "K^T (key-dim rows, token columns): o[4i+j] += W_j C_i^T")
+    what += " (the first stage: o[4i+j] = the product alone)" if first else ""
     return f"""// One 64-column stage of the expansion for {what}.
 // c[ks] / w[ks]: LDS byte address of this lane's C / W row chunk for k-step ks
 // (token block i adds 32 rows of C, output block j adds 32 rows of W).
@@ -610,6 +614,8 @@ def main():
     print()
     print(expand_block(False))
     print(expand_block(True))
+    print(expand_block(False, first=True))
+    print(expand_block(True, first=True))
     print(p64_loadq())
     print(p64_zero_o())
     for j in range(8):

@@ -125,15 +125,18 @@ __global__ void rope_table_kernel(int B, int T, const int32_t* __restrict__ star
 }
 
 // ---------------------------------------------------------------------------
-// expand: one workgroup of 8 waves (two per SIMD) per (head h, 256-position
-// tile of prompt b); tiles at or past P_b + T exit at once.  Waves 0-3 compute K^C for tokens 64w..64w+63 of the tile as
+// expand: workgroups of 8 waves (two per SIMD), each looping over work items
+// (head h, 256-position tile of prompt b) launched index + k * grid; tiles at
+// or past P_b + T are skipped.  Waves 0-3 compute K^C for tokens 64w..64w+63 of the tile as
 // K^T = W^UK_h C^T (rows = key dims, so a lane ends with 8 key dims of one
 // token in k-slot order); waves 4-7 compute V = C W^UV_h^T for the same token
 // blocks (rows = tokens, so a lane ends with 8 tokens of one value dim).  The
 // latent dimension runs in 8 stages of 64 columns, double-buffered in LDS with
 // direct-to-LDS loads: C rows of the tile [256][64] (from the cache pages)
 // then W^UK_h and W^UV_h rows [256][64], 128 bytes per row.  Two waves per SIMD keep the MFMA pipe
-// fed while the other waits for its stage.
+// fed while the other waits for its stage.  The stages run on across items:
+// the first stage of the next item is loaded during the last stage of this
+// one, so its latency overlaps the last MFMAs and the stores of the outputs.
 // ---------------------------------------------------------------------------
 constexpr int EX_TOK = 256;
 constexpr int EX_NW = 8;                   // waves per workgroup
@@ -148,45 +151,67 @@ expand_kernel(const char* __restrict__ pool, int num_pages, const int32_t* __res
               const uint16_t* __restrict__ w_uk, const uint16_t* __restrict__ w_uv, int B, int T,
               int ctx, int tp, int nt, uint16_t* __restrict__ kc, uint16_t* __restrict__ vt) {
   __shared__ __attribute__((aligned(1024))) char lds[2 * EX_STAGEB];
-  const int ttiles = B * nt;
-  const int h = blockIdx.x / ttiles, tile = blockIdx.x % ttiles;
-  const int b = tile / nt, t0 = (tile % nt) * EX_TOK;
-  const int n_pos = chunk_start(start_pos, b, T, ctx) + T;  // positions of prompt b
-  if (t0 >= n_pos) return;  // uniform: no key of this tile is ever read
-  const int32_t* trow = table + (size_t)b * max_pages;
+  const int ttiles = B * nt, n_items = H * ttiles, G = gridDim.x;
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int g = lane >> 5, n = lane & 31;
+  // item i = (head i / ttiles, tile i % ttiles); positions of its prompt
+  auto n_pos_of = [&](int i) { return chunk_start(start_pos, (i % ttiles) / nt, T, ctx) + T; };
+  auto t0_of = [&](int i) { return (i % ttiles % nt) * EX_TOK; };
+  // the first item from i on (step G) with a key that is ever read (uniform)
+  auto next_item = [&](int i) {
+    while (i < n_items && t0_of(i) >= n_pos_of(i)) i += G;
+    return i;
+  };
 
   // direct-to-LDS plan: load m of wave w fills LDS unit u = (8m + w) * 64 +
-  // lane (16 bytes each); units 0..2047 are C rows, 2048..4095 W rows
-  const char* src[EX_DMA];
+  // lane (16 bytes each); units 0..2047 are C rows, 2048..4095 W rows.  Row
+  // r = u / 8 of the stage takes chunk (u % 8) ^ swz8(r) of its 128 bytes.
+  // C load m covers tile rows 64m .. 64m + 63, i.e. one cache page (rows past
+  // the prompt read the last page; their outputs are written as zeros); W
+  // loads 4-5 cover W^UK_h rows 0-127, loads 6-7 W^UV_h rows 0-127.  The
+  // lane's row within a page (or a 64-row W block) is 8w + lane / 8 for every
+  // load, so one C offset and one W offset per lane serve all loads.
+  constexpr int NCL = EX_CU / (64 * EX_NW);  // 4 loads of C rows
+  const int lrow = 8 * wave + (lane >> 3), lchunk = (lane & 7) ^ swz8(lrow);
+  const uint32_t c_off = (uint32_t)(lrow * ROWB + 16 * lchunk);
+  const uint32_t w_off = (uint32_t)(lrow * DL * 2 + 16 * lchunk);
+  int pg[NCL];          // pages of the current item's C loads (uniform)
+  const char* wsrc[2];  // W^UK_h, W^UV_h of the current item (uniform)
+  // page ids by scalar loads, range-checked only at their use (a check right
+  // after the load would wait for it)
+  auto load_pages = [&](int i, int* out) {
+    const int b = (i % ttiles) / nt, kt0 = t0_of(i) / PS, kt_last = (n_pos_of(i) - 1) / PS;
+    const int32_t* trow = table + (size_t)b * max_pages;
 #pragma unroll
-  for (int m = 0; m < EX_DMA; ++m) {
-    const int u = (EX_NW * m + wave) * 64 + lane;
-    if (m < EX_CU / (64 * EX_NW)) {
-      const int r = u >> 3, c = (u & 7) ^ swz8(u >> 3);
-      const int t = min(t0 + r, n_pos - 1);
-      int page = trow[t / PS];
-      if (page < 0 || page >= num_pages) page = 0;  // stay in bounds on a bad table
-      src[m] = pool + (size_t)page * TILEB + (size_t)(t % PS) * ROWB + 16 * c;
-    } else {
-      const int v = u - EX_CU, r = v >> 3, c = (v & 7) ^ swz8(v >> 3);
-      const uint16_t* w = r < DC ? w_uk + ((size_t)h * DC + r) * DL
-                                 : w_uv + ((size_t)h * DC + r - DC) * DL;
-      src[m] = (const char*)w + 16 * c;
-    }
-  }
+    for (int m = 0; m < NCL; ++m) out[m] = trow[__builtin_amdgcn_readfirstlane(min(kt0 + m, kt_last))];
+  };
+  auto page_ok = [&](int p) { return (p >= 0 && p < num_pages) ? p : 0; };  // in bounds on a bad table
+  auto set_w = [&](int i) {
+    const int h = i / ttiles;
+    wsrc[0] = (const char*)(w_uk + (size_t)h * DC * DL);
+    wsrc[1] = (const char*)(w_uv + (size_t)h * DC * DL);
+  };
   auto issue = [&](int stage) {
     char* buf = lds + (stage & 1) * EX_STAGEB;
 #pragma unroll
-    for (int m = 0; m < EX_DMA; ++m) dma16(src[m] + stage * 128, buf + (EX_NW * m + wave) * 1024);
+    for (int m = 0; m < EX_DMA; ++m) {
+      const char* src = m < NCL ? pool + (size_t)pg[m] * TILEB + c_off
+                                : wsrc[(m - NCL) >> 1] + (size_t)((m - NCL) & 1) * 64 * DL * 2 + w_off;
+      dma16(src + stage * 128, buf + (EX_NW * m + wave) * 1024);
+    }
   };
 
   const bool vhalf = wave >= 4;
   const int tb = 64 * (wave & 3);  // first token of this wave inside the tile
   const int x = swz8(n);
   const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)lds);
-  const size_t bh = (size_t)b * H + h;
+  int item = next_item(blockIdx.x);
+  if (item >= n_items) return;  // uniform
+  load_pages(item, pg);
+#pragma unroll
+  for (int m = 0; m < NCL; ++m) pg[m] = page_ok(pg[m]);
+  set_w(item);
+  issue(0);
 
   // The K and V waves run separate copies of the loop (the branch is uniform
   // per wave), so each copy keeps its 128 accumulators in fixed AGPRs.
@@ -198,53 +223,73 @@ expand_kernel(const char* __restrict__ pool, int num_pages, const int32_t* __res
       cof[ks] = (uint32_t)((tb + n) * 128 + 16 * ((2 * ks + g) ^ x));
       wof[ks] = (uint32_t)(EX_CB + (128 * (V ? 1 : 0) + n) * 128 + 16 * ((2 * ks + g) ^ x));
     }
-    f32x16 acc[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) acc[k] = (f32x16){};
+    for (;;) {
+      const int h = item / ttiles, b = (item % ttiles) / nt, t0 = t0_of(item), n_pos = n_pos_of(item);
+      const size_t bh = (size_t)b * H + h;
+      const int next = next_item(item + G);
+      int pg_next[NCL];
+      f32x16 acc[8];  // set by the first stage
 
-    issue(0);
-    for (int st = 0; st < DL / 64; ++st) {
-      wait_vmcnt0();
-      raw_barrier();  // stage st is in LDS; every wave is done with stage st - 1
-      if (st + 1 < DL / 64) issue(st + 1);
-      const uint32_t base = lds0 + (uint32_t)(st & 1) * EX_STAGEB;
-      uint32_t ca[4], wa[4];
+      for (int st = 0; st < DL / 64; ++st) {
+        wait_vmcnt0();
+        raw_barrier();  // stage st is in LDS; every wave is done with stage st - 1
+        if (st + 1 < DL / 64) {
+          issue(st + 1);
+        } else if (next < n_items) {  // the next item's first stage, into the other buffer
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        ca[ks] = base + cof[ks];
-        wa[ks] = base + wof[ks];
-      }
-      if constexpr (V) expand_stage_v(acc, ca, wa);
-      else expand_stage_k(acc, ca, wa);
-    }
-
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          bf16x8 v;
-          if constexpr (!V) {
-            // token t0 + tb + 32i + n; key dims 32j + 16hh + (k-slot order) 8g..8g+7
-            const int t = t0 + tb + 32 * i + n;
-            if (t >= tp) continue;
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              v[e] = t < n_pos ? (__bf16)agpr_read(acc[4 * i + j][8 * hh + e]) : (__bf16)0.f;
-            *(bf16x8*)(kc + (bh * tp + t) * DC + 32 * j + 16 * hh + 8 * g) = v;
-          } else {
-            // value dim 32j + n; stored key positions p0 .. p0+7 of the tile
-            const int p0 = t0 + tb + 32 * i + 16 * hh + 8 * g;
-            if (p0 >= tp) continue;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int t = t0 + tb + 32 * i + 16 * hh + 8 * (e >> 2) + 4 * g + (e & 3);
-              v[e] = t < n_pos ? (__bf16)agpr_read(acc[4 * i + j][8 * hh + e]) : (__bf16)0.f;
-            }
-            *(bf16x8*)(vt + (bh * DC + 32 * j + n) * tp + p0) = v;
-          }
+          for (int m = 0; m < NCL; ++m) pg[m] = page_ok(pg_next[m]);
+          set_w(next);
+          issue(0);
         }
+        const uint32_t base = lds0 + (uint32_t)(st & 1) * EX_STAGEB;
+        uint32_t ca[4], wa[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          ca[ks] = base + cof[ks];
+          wa[ks] = base + wof[ks];
+        }
+        if (st == 0) {
+          if constexpr (V) expand_stage_v_first(acc, ca, wa);
+          else expand_stage_k_first(acc, ca, wa);
+        } else {
+          if constexpr (V) expand_stage_v(acc, ca, wa);
+          else expand_stage_k(acc, ca, wa);
+        }
+        // the next item's pages, after this stage's MFMAs (the next stage's
+        // LDS wait would otherwise wait for them)
+        if (st == 0 && next < n_items) load_pages(next, pg_next);
+      }
+
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            bf16x8 v;
+            if constexpr (!V) {
+              // token t0 + tb + 32i + n; key dims 32j + 16hh + (k-slot order) 8g..8g+7
+              const int t = t0 + tb + 32 * i + n;
+              if (t >= tp) continue;
+#pragma unroll
+              for (int e = 0; e < 8; ++e)
+                v[e] = t < n_pos ? (__bf16)agpr_read(acc[4 * i + j][8 * hh + e]) : (__bf16)0.f;
+              *(bf16x8*)(kc + (bh * tp + t) * DC + 32 * j + 16 * hh + 8 * g) = v;
+            } else {
+              // value dim 32j + n; stored key positions p0 .. p0+7 of the tile
+              const int p0 = t0 + tb + 32 * i + 16 * hh + 8 * g;
+              if (p0 >= tp) continue;
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                const int t = t0 + tb + 32 * i + 16 * hh + 8 * (e >> 2) + 4 * g + (e & 3);
+                v[e] = t < n_pos ? (__bf16)agpr_read(acc[4 * i + j][8 * hh + e]) : (__bf16)0.f;
+              }
+              *(bf16x8*)(vt + (bh * DC + 32 * j + n) * tp + p0) = v;
+            }
+          }
+      if (next >= n_items) break;
+      item = next;
+    }
   };
   if (vhalf) run(std::true_type{});
   else run(std::false_type{});
@@ -708,15 +753,17 @@ hipError_t launch_v2_prefill(const Layer& L, const void* pool, int num_pages, co
   int* queue = (int*)(w + lay.queue);
   hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((B * T * (DR / 2) + 255) / 256)),
                      dim3(256), 0, s, B, T, start_pos, ctx, L.rope_base, tab, queue);
+  // both kernels below run one workgroup per CU (and at least one per XCD
+  // that has work), each looping over work items
+  int cus = 0;
+  if (device_cus(&cus) != 0) return hipErrorInvalidDevice;
   const int nt = (ctx + EX_TOK - 1) / EX_TOK;
-  hipLaunchKernelGGL(expand_kernel, dim3((unsigned)(H * B * nt)), dim3(64 * EX_NW), 0, s,
+  hipLaunchKernelGGL(expand_kernel, dim3((unsigned)std::min(H * B * nt, std::max(cus, 8))),
+                     dim3(64 * EX_NW), 0, s,
                      (const char*)pool, num_pages, table, max_pages, start_pos,
                      (const uint16_t*)w_uk, (const uint16_t*)w_uv, B, T, ctx, lay.tp, nt, kc, vt);
   const int nqb = (T + QB - 1) / QB;
   const float sc_log2 = L.scale * 1.4426950408889634f;
-  // one workgroup per CU, at least one per XCD that has items
-  int cus = 0;
-  if (device_cus(&cus) != 0) return hipErrorInvalidDevice;
   const int n_item = B * H * nqb, grid = std::min(n_item, std::max(cus, 8));
   hipLaunchKernelGGL(prefill_attn_kernel, dim3((unsigned)grid), dim3(256), 0, s,
                      (const char*)pool, num_pages, table, max_pages, (const uint16_t*)q_nope,
