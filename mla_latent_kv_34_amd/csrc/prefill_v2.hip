@@ -302,10 +302,10 @@ constexpr int STAGEB = KTILEB + VTILEB;    // 40960
 constexpr int AT_DMA = STAGEB / 1024 / 4;  // 10 one-KiB loads per wave per tile
 
 // ---------------------------------------------------------------------------
-// prefill_attn: causal attention, one workgroup per (prompt b, head h,
-// 256-query block of the chunk), one wave per SIMD; wave v owns chunk rows
-// 64v..64v+63 as two halves of 32 (A and B), so every K and V^T fragment read
-// from LDS feeds the MFMAs of both halves.
+// prefill_attn: causal attention; a work item is (prompt b, head h, 256-query
+// block of the chunk), run by a workgroup of four waves, one per SIMD; wave v
+// owns chunk rows 64v..64v+63 as two halves of 32 (A and B), so every K and
+// V^T fragment read from LDS feeds the MFMAs of both halves.
 //
 // Key tiles of 64 (one cache page) sit in a 4-deep LDS ring (all 160 KiB), two
 // tiles in flight.  A tile is four regions of 128-byte rows, each filled by
