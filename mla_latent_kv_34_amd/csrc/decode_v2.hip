@@ -346,7 +346,12 @@ q_absorb_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __restrict_
     }
     return;
   }
-  const int h = (blockIdx.x - 1) >> 2, chunk = (blockIdx.x - 1) & 3;
+  // Workgroup j = blockIdx - 1 runs on XCD (j + 1) % 8.  A 128-byte line of the
+  // fragment layout holds 8 dims of 8 heads 8i..8i+7, so the 8 workgroups of
+  // head group i and one column chunk go to one XCD: their pieces of each
+  // line meet in that XCD's L2 and leave it as whole lines.
+  const int jb = blockIdx.x - 1, kx = jb >> 3, gi = ((kx >> 3) << 3) | (jb & 7);
+  const int h = ((gi >> 2) << 3) | (kx & 7), chunk = gi & 3;
   const int c0 = chunk * 128;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
