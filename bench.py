@@ -69,6 +69,9 @@ def parse():
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--batch", type=int, default=64,
                     help="batch of the ragged decode workload (64 is the headline configuration)")
+    ap.add_argument("--workgroups", type=int, default=0,
+                    help="split-KV workgroups of every decode call (0: one per compute unit, the "
+                         "library's default)")
     ap.add_argument("--legs", default="tiny_decode,v2_b1_4k,v2_b4_128k",
                     help="comma-separated other decode workloads to time ('none' for none)")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -185,7 +188,7 @@ def main():
         q_c, q_r = case.q_c.to(dev), case.q_r.to(dev)
         w_uk, w_uv = case.w_uk.to(dev), case.w_uv.to(dev)
         dec, out = mla.decode_step(dims, pool, table, seq_lens, new_c, new_k, q_c, q_r, w_uk, w_uv,
-                                   prepare=True)
+                                   n_workgroups=args.workgroups, prepare=True)
         reps.append(dict(dec=dec, out=out,
                          keep=(pool, table, seq_lens, new_c, new_k, q_c, q_r, w_uk, w_uv)))
         if r > 0:
@@ -211,7 +214,8 @@ def main():
     # steps issued back to back as in the timed loop, one sync at the end
     kern_ms = back_to_back_kernel_ms(
         lambda i, ev: mla.decode_step(dims, *reps[i % len(reps)]["keep"][:9], out=reps[i % len(reps)]["out"],
-                                      timing_events=ev, prepare=True)[0], args.steps,
+                                      n_workgroups=args.workgroups, timing_events=ev, prepare=True)[0],
+        args.steps,
         warm=lambda: warm_clock(step, args.warm_seconds))
     kern_pct = [round(float(v), 5) for v in np.percentile(kern_ms, [10, 50, 90])]
     kern_ms = float(np.mean(kern_ms))
@@ -288,7 +292,7 @@ def main():
     names = [] if args.legs == "none" else [x for x in args.legs.split(",") if x]
     if names:
         legs = {name: decode_leg(mla, syn, dev, name, args.steps, args.warmup, not args.no_cpu,
-                                 args.warm_seconds) for name in names}
+                                 args.warm_seconds, args.workgroups) for name in names}
 
     cpu = None
     if not args.no_cpu:
@@ -314,6 +318,7 @@ def main():
             "batch": B,
             "attended_tokens": tokens,
             "replicas": n_reps,
+            "split_kv_workgroups": args.workgroups or "one per compute unit",
             "resident_cache_GB": round(resident, 3),
             "timing": "hip graph replay, one graph per %d consecutive steps" % n_reps if graph_ms is not None else "eager launches",
             "warmup": f"{args.warmup} steps, then {warm_s:.2f} s of untimed steps (sustained-load clock)",
@@ -482,7 +487,8 @@ LEG_REPLICAS = {"tiny_decode": 1, "v2_b1_4k": 8, "v2_b4_128k": 2}
 LEG_ORACLE_HEADS = {"tiny_decode": None, "v2_b1_4k": None, "v2_b4_128k": 16}
 
 
-def decode_leg(mla, syn, dev, name: str, steps: int, warmup: int, with_cpu: bool, warm_s: float):
+def decode_leg(mla, syn, dev, name: str, steps: int, warmup: int, with_cpu: bool, warm_s: float,
+               n_wg: int = 0):
     """One of the other decode workloads: step time by graph replay over
     cache/weight replicas (enough to exceed the 256 MB last-level cache where
     the working set is small), the split-KV kernel by back-to-back events, and
@@ -518,7 +524,7 @@ def decode_leg(mla, syn, dev, name: str, steps: int, warmup: int, with_cpu: bool
         else:
             keep = (pool, table, seq_lens, q_c, q_r, w_uk, w_uv)
             fn = mla.decode
-        call, out = fn(dims, *keep, prepare=True)
+        call, out = fn(dims, *keep, n_workgroups=n_wg, prepare=True)
         reps.append(dict(call=call, out=out, keep=keep, fn=fn, dims=dims))
         if r == 0:
             case0 = case
@@ -532,7 +538,7 @@ def decode_leg(mla, syn, dev, name: str, steps: int, warmup: int, with_cpu: bool
     ms = graph_replay_ms([r["call"] for r in reps], steps, warmup)
     kern = back_to_back_kernel_ms(
         lambda i, ev: reps[i % R]["fn"](reps[i % R]["dims"], *reps[i % R]["keep"], out=reps[i % R]["out"],
-                                        timing_events=ev, prepare=True)[0], steps,
+                                        n_workgroups=n_wg, timing_events=ev, prepare=True)[0], steps,
         warm=lambda: warm_clock(lambda i: reps[i % R]["call"](), warm_s))
     kern_pct = [round(float(v), 5) for v in np.percentile(kern, [10, 50, 90])]
     kern_ms = float(np.mean(kern))
@@ -543,6 +549,7 @@ def decode_leg(mla, syn, dev, name: str, steps: int, warmup: int, with_cpu: bool
     res = {
         "workload": f"{name}: {LEG_TEXT[name]}",
         "batch": int(case0.batch), "attended_tokens": tokens, "replicas": R,
+        "split_kv_workgroups": n_wg or "one per compute unit",
         "us_per_step": round(ms * 1e3, 2),
         "value": round(tokens / (ms * 1e-3), 1), "unit": "cached tokens/s",
         "latent_cache_GBps": round(cache_bytes / (ms * 1e-3) / 1e9, 1),
