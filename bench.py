@@ -49,6 +49,22 @@ def kernel_source_sha256() -> str:
     return h.hexdigest()
 
 
+def recorded_traffic(workload: str, workgroups: int, path: str = TRAFFIC_FILE):
+    """HBM bytes per launch of decode_splitkv from the counter record, or None
+    when the record does not describe this run: another workload, a
+    non-default split-KV workgroup count (the counters were taken with one
+    workgroup per compute unit), or kernel sources that changed since."""
+    if workgroups != 0 or not os.path.exists(path):
+        return None
+    try:
+        tf = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if tf.get("kernel_source_sha256") != kernel_source_sha256() or tf.get("workload") != workload:
+        return None
+    return tf.get("bytes_per_launch")
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -265,15 +281,7 @@ def main():
     achieved = cache_bytes / (kern_ms * 1e-3) / 1e9
     kern_tflops = tokens * FLOP_PER_TOKEN / (kern_ms * 1e-3) / 1e12
 
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        try:
-            tf = json.load(open(TRAFFIC_FILE))
-            if (tf.get("kernel_source_sha256") == kernel_source_sha256()
-                    and tf.get("workload") == f"v2_b{B}_ragged"):
-                traffic = tf.get("bytes_per_launch")
-        except Exception:
-            traffic = None
+    traffic = recorded_traffic(f"v2_b{B}_ragged", args.workgroups)
 
     pre = None
     if not args.no_prefill:
