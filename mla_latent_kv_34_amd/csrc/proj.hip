@@ -40,7 +40,7 @@ namespace mla {
 namespace pj {
 
 #ifndef PJ_WR
-#define PJ_WR 64
+#define PJ_WR 128
 #endif
 #ifndef PJ_DEPTH
 #define PJ_DEPTH 4
@@ -355,8 +355,9 @@ proj_reduce_kernel(const float* __restrict__ part, int M, int ksplit, Segs segs)
 
 // K slices per launch: a power of two dividing K / KC that gives at least
 // PJ_MIN_WG workgroups, or 4 x PJ_MIN_WG for long K, where the fp32 partials
-// stay small next to the weights (measured at batch 64: stage 1, K 5120, is
-// fastest split 4 ways; W^O, K 16384, split 8 ways).
+// stay small next to the weights.  With 128-row workgroups at batch 64 this
+// splits stage 1 (K 5120) 8 ways and W^O (K 16384) 16 ways; targets twice as
+// large measured slower.
 constexpr int kMinWorkgroups = PJ_MIN_WG;
 constexpr int kLongK = 8192;
 int choose_split(int n_total, int K) {
