@@ -106,14 +106,13 @@ __device__ __forceinline__ int chunk_start(const int32_t* start_pos, int b, int 
 // ---------------------------------------------------------------------------
 // rope_table: tab[b][t][k] = (cos, sin) of (P_b + t) * base^(-2k/64),
 // computed in fp64 and stored in fp32 (the rotated query is rounded to bf16
-// afterwards).  It also clears the eight work counters of prefill_attn and
-// their mask of emptied ranges, which prefill_attn uses later on the same
-// stream.
+// afterwards).  It also clears the eight work counters of prefill_attn, which
+// runs later on the same stream.
 // ---------------------------------------------------------------------------
 __global__ void rope_table_kernel(int B, int T, const int32_t* __restrict__ start_pos, int ctx,
                                   double base, float2* __restrict__ tab, int* __restrict__ queue) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < 9) queue[i] = 0;
+  if (i < 8) queue[i] = 0;
   if (i >= B * T * (DR / 2)) return;
   const int bt = i / (DR / 2), k = i % (DR / 2);
   const int b = bt / T, t = bt % T;
@@ -622,14 +621,7 @@ __device__ __forceinline__ void attn_item(const char* __restrict__ pool, int num
 // with blocks of unequal length one workgroup per block leaves CUs idle.  The
 // workgroups on XCD x (launched index % 8) take the items of that XCD's
 // contiguous logical range in order from counter x, so the blocks of a head
-// run side by side and share its K/V tiles in that XCD's L2.  A workgroup
-// whose own range is empty goes on to the other XCDs' ranges, in turn from
-// XCD x + 1, and takes their next items from their counters (the short
-// blocks their tails end on): the XCDs hold different clocks under load, so
-// equal ranges do not end together.  A counter that returned past its
-// range's end sets the range's bit in queue[8]; workgroups read that mask
-// before each item taken from another range and skip the emptied ranges, so
-// the search past the last item costs about two atomic round trips.
+// run side by side and share its K/V tiles in that XCD's L2.
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 prefill_attn_kernel(const char* __restrict__ pool, int num_pages, const int32_t* __restrict__ table,
                       int max_pages, const uint16_t* __restrict__ q_nope,
@@ -639,13 +631,12 @@ prefill_attn_kernel(const char* __restrict__ pool, int num_pages, const int32_t*
                       float sc_log2, int* __restrict__ queue, uint16_t* __restrict__ out) {
   __shared__ __attribute__((aligned(1024))) char lds[NRING * STAGEB];
   const int n = B * H * nqb, xc = blockIdx.x & 7;
-  auto count_of = [&](int y) { return (n >> 3) + (y < (n & 7)); };
-  // The last TAIL_HEADS heads' worth of a range go longest first across
+  const int first = xc * (n >> 3) + min(xc, n & 7), count = (n >> 3) + (xc < (n & 7));
+  // The last TAIL_HEADS heads' worth of the range go longest first across
   // heads, so the range ends on short blocks: item p of the tail [s, e) is
   // the p-th in the order (descending query block, ascending index).
-  auto item_of = [&](int y, int k) {
-    const int first = y * (n >> 3) + min(y, n & 7), count = count_of(y);
-    const int tail = min(count, TAIL_HEADS * nqb), s0 = first + count - tail, e0 = first + count;
+  const int tail = min(count, TAIL_HEADS * nqb), s0 = first + count - tail, e0 = first + count;
+  auto item_of = [&](int k) {
     if (k < count - tail) return first + k;
     int p = k - (count - tail);
     for (int r = 0; r < nqb - 1; ++r) {  // r = nqb - 1 - query block
@@ -657,34 +648,14 @@ prefill_attn_kernel(const char* __restrict__ pool, int num_pages, const int32_t*
     return s0 + (nqb - 1 - s0 % nqb + nqb) % nqb + p * nqb;  // query block 0
   };
   volatile int* const bcast = (volatile int*)(lds + NRING * STAGEB - 4);
-  // thread 0 only: ranges (xc + o) & 7 for o < off are known to be empty
-  int off = 0, seen = 0;
   for (;;) {
     raw_barrier();  // every wave is done with the ring (its copies landed)
-    if (threadIdx.x == 0) {
-      // item k of range y as (y << 24) | k (k < 2^23: B T n_h < 2^31), -1 when
-      // every range is empty; at most 8 - off + 1 atomics, each either takes
-      // an item or empties a range
-      int code = -1;
-      if (off > 0) seen |= atomicOr(queue + 8, 0);
-      for (; off < 8; ++off) {
-        const int y = (xc + off) & 7;
-        if ((seen >> y) & 1) continue;
-        const int v = atomicAdd(queue + y, 1);
-        if (v < count_of(y)) {
-          code = (y << 24) | v;
-          break;
-        }
-        seen |= 1 << y;
-        atomicOr(queue + 8, 1 << y);
-      }
-      *bcast = code;
-    }
+    if (threadIdx.x == 0) *bcast = atomicAdd(queue + xc, 1);
     __syncthreads();
-    const int code = __builtin_amdgcn_readfirstlane(*bcast);
-    if (code < 0) break;
+    const int k = __builtin_amdgcn_readfirstlane(*bcast);
+    if (k >= count) break;
     attn_item(pool, num_pages, table, max_pages, q_nope, q_rope, rope_tab, kc, vt, start_pos, T,
-              ctx, tp, nqb, sc_log2, out, item_of(code >> 24, code & 0xffffff), lds);
+              ctx, tp, nqb, sc_log2, out, item_of(k), lds);
   }
 }
 
