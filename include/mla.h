@@ -104,7 +104,7 @@ mla_status mla_cache_append(const mla_dims* dims, const mla_paged_cache* cache, 
 
 /* Bytes of device workspace mla_decode needs for `batch` sequences when it runs
  * with n_workgroups split-KV workgroups (0 = one per compute unit of the
- * current device).                                                             */
+ * current device; enough for any page-table width).                            */
 size_t mla_decode_workspace_size(const mla_dims* dims, int32_t batch, int32_t n_workgroups);
 
 /* Weight-absorbed decode: one query per sequence over its paged latent cache.
@@ -117,7 +117,8 @@ size_t mla_decode_workspace_size(const mla_dims* dims, int32_t batch, int32_t n_
  * Steps: q_lat_i = W^UK_i^T q^C_i and RoPE of q^R; split-KV attention over the
  * 576-wide rows with an online softmax; log-sum-exp combine of the splits;
  * output projection through W^UV.
- * n_workgroups: number of split-KV workgroups (0 = one per compute unit); it
+ * n_workgroups: number of split-KV workgroups (0 = one per compute unit, but
+ *   no more than batch x max_pages, one per page the table can address); it
  *   changes how the work is split, not the result beyond rounding.
  * workspace: device memory of at least mla_decode_workspace_size(dims, batch,
  *   n_workgroups) bytes; its contents on entry do not matter.

@@ -3,6 +3,7 @@
 // in include/mla.h.  Nothing here allocates device memory or synchronises.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -120,6 +121,20 @@ int resolve_wg(int n_workgroups, int* out) {
   return mla::device_cus(out);
 }
 
+// Split-KV workgroups of a decode launch: n_workgroups when given, else one
+// per compute unit but no more than one per page the table can address
+// (batch x max_pages), so a short context gets a launch of few workgroups that
+// each take at least a whole page instead of one with hundreds of idle ones
+// (batch 1 x 4096: 30.9 us per step with 64 workgroups, 33.3 us with 256).
+int resolve_decode_wg(int n_workgroups, int batch, int max_pages, int* out) {
+  if (resolve_wg(n_workgroups, out) != 0) return -1;
+  if (n_workgroups == 0) {
+    const long long pages = (long long)batch * std::max(max_pages, 1);
+    if (pages < *out) *out = (int)std::max(1LL, pages);
+  }
+  return 0;
+}
+
 }  // namespace
 
 #define MLA_TRY(expr)                 \
@@ -203,7 +218,7 @@ mla_status mla_decode(const mla_dims* dims, const mla_paged_cache* cache, int32_
                     "generic decode launch");
   }
   int wg = 0;
-  if (resolve_wg(n_workgroups, &wg) != 0) return fail(MLA_ERR_HIP, "cannot query the device");
+  if (resolve_decode_wg(n_workgroups, batch, cache->max_pages, &wg) != 0) return fail(MLA_ERR_HIP, "cannot query the device");
   const size_t need = mla::v2_decode_workspace(batch, wg);
   if (!workspace || workspace_bytes < need)
     return fail(MLA_ERR_WORKSPACE, "workspace smaller than mla_decode_workspace_size()");
@@ -253,7 +268,7 @@ mla_status mla_decode_step(const mla_dims* dims, const mla_paged_cache* cache, i
                     "generic decode launch");
   }
   int wg = 0;
-  if (resolve_wg(n_workgroups, &wg) != 0) return fail(MLA_ERR_HIP, "cannot query the device");
+  if (resolve_decode_wg(n_workgroups, batch, cache->max_pages, &wg) != 0) return fail(MLA_ERR_HIP, "cannot query the device");
   const size_t need = mla::v2_decode_workspace(batch, wg);
   if (!workspace || workspace_bytes < need)
     return fail(MLA_ERR_WORKSPACE, "workspace smaller than mla_decode_workspace_size()");
@@ -289,7 +304,7 @@ mla_status mla_decode_step_noalloc(const mla_dims* dims, const mla_paged_cache* 
   if (n_workgroups < 0 || n_workgroups > 65536)
     return fail(MLA_ERR_INVALID_ARG, "n_workgroups must be in [0, 65536]");
   int wg = 0;
-  if (resolve_wg(n_workgroups, &wg) != 0) return fail(MLA_ERR_HIP, "cannot query the device");
+  if (resolve_decode_wg(n_workgroups, batch, cache->max_pages, &wg) != 0) return fail(MLA_ERR_HIP, "cannot query the device");
   const size_t need = mla::v2_decode_workspace(batch, wg);
   if (need > mla::kStaticScratchBytes)
     return fail(MLA_ERR_WORKSPACE,
@@ -389,7 +404,7 @@ mla_status mla_decode_hidden(const mla_dims* dims, const mla_paged_cache* cache,
     return generic_hidden(L, cache, batch, seq_lens, d_model, d_q, h, w_dkv, w_kr, w_dq, w_uq, w_qr,
                           w_uk, w_uv, nullptr, out, workspace, workspace_bytes, timing_events, stream);
   int wg = 0;
-  if (resolve_wg(n_workgroups, &wg) != 0) return fail(MLA_ERR_HIP, "cannot query the device");
+  if (resolve_decode_wg(n_workgroups, batch, cache->max_pages, &wg) != 0) return fail(MLA_ERR_HIP, "cannot query the device");
   const size_t need = mla::v2_hidden_workspace(L, batch, wg, d_model, d_q);
   if (!workspace || workspace_bytes < need)
     return fail(MLA_ERR_WORKSPACE, "workspace smaller than mla_decode_hidden_workspace_size()");
@@ -433,7 +448,7 @@ mla_status mla_decode_layer(const mla_dims* dims, const mla_paged_cache* cache, 
     return generic_hidden(L, cache, batch, seq_lens, d_model, d_q, h, w_dkv, w_kr, w_dq, w_uq, w_qr,
                           w_uk, w_uv, w_o, u, workspace, workspace_bytes, timing_events, stream);
   int wg = 0;
-  if (resolve_wg(n_workgroups, &wg) != 0) return fail(MLA_ERR_HIP, "cannot query the device");
+  if (resolve_decode_wg(n_workgroups, batch, cache->max_pages, &wg) != 0) return fail(MLA_ERR_HIP, "cannot query the device");
   const size_t need = mla::v2_hidden_workspace(L, batch, wg, d_model, d_q);
   if (!workspace || workspace_bytes < need)
     return fail(MLA_ERR_WORKSPACE, "workspace smaller than mla_decode_hidden_workspace_size()");
@@ -486,7 +501,7 @@ mla_status mla_decode_hidden_merged(const mla_dims* dims, const mla_paged_cache*
   if (n_workgroups < 0 || n_workgroups > 65536)
     return fail(MLA_ERR_INVALID_ARG, "n_workgroups must be in [0, 65536]");
   int wg = 0;
-  if (resolve_wg(n_workgroups, &wg) != 0) return fail(MLA_ERR_HIP, "cannot query the device");
+  if (resolve_decode_wg(n_workgroups, batch, cache->max_pages, &wg) != 0) return fail(MLA_ERR_HIP, "cannot query the device");
   const size_t need = mla::v2_hidden_workspace(L, batch, wg, d_model, d_q);
   if (!workspace || workspace_bytes < need)
     return fail(MLA_ERR_WORKSPACE, "workspace smaller than mla_decode_hidden_workspace_size()");
@@ -541,7 +556,7 @@ mla_status mla_decode_layer_merged(const mla_dims* dims, const mla_paged_cache* 
   if (n_workgroups < 0 || n_workgroups > 65536)
     return fail(MLA_ERR_INVALID_ARG, "n_workgroups must be in [0, 65536]");
   int wg = 0;
-  if (resolve_wg(n_workgroups, &wg) != 0) return fail(MLA_ERR_HIP, "cannot query the device");
+  if (resolve_decode_wg(n_workgroups, batch, cache->max_pages, &wg) != 0) return fail(MLA_ERR_HIP, "cannot query the device");
   const size_t need = mla::v2_hidden_workspace(L, batch, wg, d_model, d_q);
   if (!workspace || workspace_bytes < need)
     return fail(MLA_ERR_WORKSPACE, "workspace smaller than mla_decode_hidden_workspace_size()");
